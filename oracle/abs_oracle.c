@@ -1,0 +1,334 @@
+/*
+ * CPU oracle for the AB-Sparse decode path.  TEST INFRASTRUCTURE ONLY: the
+ * parity tests, the smoke check and the benchmark's CPU-baseline leg call
+ * it; the library and its kernels never do, and it shares no code with them.
+ *
+ * Source: "AB-Sparse: Sparse Attention with Adaptive Block Size for Accurate
+ * and Efficient Long-Context Inference" (arXiv 2605.12110), as shown on its
+ * Pith review page.  Figure 1 names the four stages this file follows, in
+ * order: a block representation (the centroid), dot-product estimation of an
+ * importance score per block, top-K selection, and sparse attention over the
+ * chosen blocks.  Figure 8's mapping residue fixes that 16-token physical
+ * pages are grouped into per-head logical blocks (stride = pages per block)
+ * and that heads with different strides select different numbers of blocks
+ * for the same number of pages; Figure 8's caption fixes INT4 asymmetric
+ * per-channel quantization of the centroids; Figure 5's text fixes that the
+ * block size of a head is static.  Exact attention over the kept tokens is
+ * the textbook softmax (FlashAttention, the page's reference list).
+ *
+ * Readings where the page is silent (each is stated at its function):
+ * mean-key centroid over the valid tokens of a block; one (scale, lo) pair
+ * per (sequence, KV head, channel) over all blocks of that head; float zero
+ * point, fp32 scale and quotient, round-half-even; query of a GQA group =
+ * sum of its heads' queries; K = min(N, max(1, budget / block_size));
+ * ties to the lower block index; selections reported in ascending order;
+ * softmax scale passed in, no mask.
+ *
+ * Arithmetic: fp64 everywhere, except the quantizer, whose fp32 steps are
+ * the ones that decide an integer code and are done in fp32 on purpose.
+ * Plain loops; OpenMP only splits independent (sequence, head) pairs.
+ *
+ * Layouts (shared by definition with the library, not by code):
+ *   cache  [num_pages][Hkv][16][D]   element = fp32, or bf16 bit pattern
+ *   page_table [B][max_pages] int32  token t of sequence b is at
+ *                                    page_table[b][t/16], slot t%16
+ *   q      [B][Hq][D]                query head i reads KV head i / (Hq/Hkv)
+ *   blocks of (b, h) are numbered j = 0..N-1, N = ceil(L_b / bs_h), and
+ *   stored b-major, then h, then j ("CSR" order).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define PAGE 16
+
+/* ---- element access ---------------------------------------------------- */
+
+static double elem(const void *base, int is_bf16, size_t i)
+{
+    if (is_bf16) {
+        uint32_t u = (uint32_t)((const uint16_t *)base)[i] << 16;
+        float f;
+        memcpy(&f, &u, sizeof f);
+        return (double)f;
+    }
+    return (double)((const float *)base)[i];
+}
+
+/* channel d of token t of sequence b, KV head h, read through the page table */
+static double cache_at(const void *cache, int is_bf16, const int32_t *page_table,
+                       int max_pages, int Hkv, int D, int b, int h, int64_t t, int d)
+{
+    int64_t page = page_table[(int64_t)b * max_pages + t / PAGE];
+    size_t i = ((((size_t)page * Hkv + h) * PAGE + (size_t)(t % PAGE)) * D) + d;
+    return elem(cache, is_bf16, i);
+}
+
+static int64_t n_blocks(int64_t L, int bs) { return (L + bs - 1) / bs; }
+
+int64_t oracle_total_blocks(int B, int Hkv, const int32_t *seq_lens, const int32_t *block_size)
+{
+    int64_t n = 0;
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < Hkv; ++h)
+            n += n_blocks(seq_lens[b], block_size[h]);
+    return n;
+}
+
+/* first block row of (b, h) in CSR order */
+static int64_t first_block(int b, int h, int Hkv, const int32_t *seq_lens, const int32_t *block_size)
+{
+    int64_t n = 0;
+    for (int bb = 0; bb < b; ++bb)
+        for (int hh = 0; hh < Hkv; ++hh)
+            n += n_blocks(seq_lens[bb], block_size[hh]);
+    for (int hh = 0; hh < h; ++hh)
+        n += n_blocks(seq_lens[b], block_size[hh]);
+    return n;
+}
+
+/* K for (b, h): the token budget buys floor(budget / bs) blocks, at least
+ * one, never more than exist (equal pages per head, Figure 8 residue). */
+static int64_t k_for(int64_t N, int bs, int budget)
+{
+    int64_t k = budget / bs;
+    if (k < 1) k = 1;
+    if (k > N) k = N;
+    return k;
+}
+
+int64_t oracle_k(int64_t L, int bs, int budget) { return k_for(n_blocks(L, bs), bs, budget); }
+
+/* ---- stage 1: block representation -------------------------------------- */
+
+/* Centroid of block j = arithmetic mean of the keys of its valid tokens
+ * [j*bs, min((j+1)*bs, L)), summed in fp64 and rounded once to fp32.
+ * block_size may be any value >= 1 here (1 gives centroid = key). */
+void oracle_centroids(int B, int Hkv, int D, int max_pages, int is_bf16,
+                      const void *k_cache, const int32_t *page_table,
+                      const int32_t *seq_lens, const int32_t *block_size,
+                      float *centroids /* [total_blocks][D] */)
+{
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        for (int h = 0; h < Hkv; ++h) {
+            int64_t L = seq_lens[b];
+            int bs = block_size[h];
+            int64_t N = n_blocks(L, bs);
+            int64_t row0 = first_block(b, h, Hkv, seq_lens, block_size);
+            double *acc = (double *)malloc(sizeof(double) * D);
+            for (int64_t j = 0; j < N; ++j) {
+                int64_t t0 = j * bs;
+                int64_t t1 = t0 + bs < L ? t0 + bs : L;
+                for (int d = 0; d < D; ++d) acc[d] = 0.0;
+                for (int64_t t = t0; t < t1; ++t)
+                    for (int d = 0; d < D; ++d)
+                        acc[d] += cache_at(k_cache, is_bf16, page_table, max_pages, Hkv, D, b, h, t, d);
+                for (int d = 0; d < D; ++d)
+                    centroids[(row0 + j) * D + d] = (float)(acc[d] / (double)(t1 - t0));
+            }
+            free(acc);
+        }
+    }
+}
+
+/* ---- stage 1b: INT4 asymmetric per-channel quantization ----------------- */
+
+/* Per (b, h, d): lo = min_j c_j[d], hi = max_j c_j[d] over the head's blocks;
+ * scale = (hi - lo) / 15 and code = clamp(rint((c - lo) / scale), 0, 15),
+ * each of those fp32 operations rounded to fp32 (the integer code is decided
+ * in fp32); a constant channel (scale 0) gets code 0 and dequantizes to lo.
+ * codes are one byte per channel here (values 0..15), [total_blocks][D]. */
+void oracle_quantize(int B, int Hkv, int D, const int32_t *seq_lens, const int32_t *block_size,
+                     const float *centroids, uint8_t *codes, float *scale, float *lo)
+{
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        for (int h = 0; h < Hkv; ++h) {
+            int64_t N = n_blocks(seq_lens[b], block_size[h]);
+            int64_t row0 = first_block(b, h, Hkv, seq_lens, block_size);
+            for (int d = 0; d < D; ++d) {
+                float mn = centroids[row0 * D + d], mx = mn;
+                for (int64_t j = 1; j < N; ++j) {
+                    float c = centroids[(row0 + j) * D + d];
+                    if (c < mn) mn = c;
+                    if (c > mx) mx = c;
+                }
+                volatile float range = mx - mn;          /* fp32 subtraction */
+                volatile float s = range / 15.0f;        /* fp32 division */
+                scale[((size_t)b * Hkv + h) * D + d] = s;
+                lo[((size_t)b * Hkv + h) * D + d] = mn;
+                for (int64_t j = 0; j < N; ++j) {
+                    uint8_t code = 0;
+                    if (s > 0.0f) {
+                        volatile float diff = centroids[(row0 + j) * D + d] - mn;
+                        volatile float quot = diff / s;
+                        float r = rintf(quot);
+                        if (r < 0.0f) r = 0.0f;
+                        if (r > 15.0f) r = 15.0f;
+                        code = (uint8_t)r;
+                    }
+                    codes[(row0 + j) * D + d] = code;
+                }
+            }
+        }
+    }
+}
+
+/* ---- stage 2: dot-product estimation ------------------------------------ */
+
+/* Importance score of block j of (b, h): the group query qbar = sum of the
+ * G query heads that share KV head h, dotted with the dequantized centroid
+ * code*scale + lo, all in fp64.  No softmax scale: it does not change the
+ * order.  scores: [total_blocks] in CSR order. */
+void oracle_scores(int B, int Hq, int Hkv, int D, int is_bf16, const void *q,
+                   const int32_t *seq_lens, const int32_t *block_size,
+                   const uint8_t *codes, const float *scale, const float *lo, double *scores)
+{
+    int G = Hq / Hkv;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        for (int h = 0; h < Hkv; ++h) {
+            int64_t N = n_blocks(seq_lens[b], block_size[h]);
+            int64_t row0 = first_block(b, h, Hkv, seq_lens, block_size);
+            double *qbar = (double *)calloc((size_t)D, sizeof(double));
+            for (int g = 0; g < G; ++g)
+                for (int d = 0; d < D; ++d)
+                    qbar[d] += elem(q, is_bf16, ((size_t)b * Hq + (size_t)h * G + g) * D + d);
+            const float *sc = scale + ((size_t)b * Hkv + h) * D;
+            const float *zp = lo + ((size_t)b * Hkv + h) * D;
+            for (int64_t j = 0; j < N; ++j) {
+                double s = 0.0;
+                for (int d = 0; d < D; ++d) {
+                    double chat = (double)codes[(row0 + j) * D + d] * (double)sc[d] + (double)zp[d];
+                    s += qbar[d] * chat;
+                }
+                scores[row0 + j] = s;
+            }
+            free(qbar);
+        }
+    }
+}
+
+/* ---- stage 3: top-K selection ------------------------------------------- */
+
+typedef struct { double s; int64_t j; } ranked;
+
+/* higher score first; equal scores: lower block index first */
+static int by_rank(const void *a, const void *b)
+{
+    const ranked *x = (const ranked *)a, *y = (const ranked *)b;
+    if (x->s > y->s) return -1;
+    if (x->s < y->s) return 1;
+    return (x->j > y->j) - (x->j < y->j);
+}
+
+static int by_index(const void *a, const void *b)
+{
+    int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+    return (x > y) - (x < y);
+}
+
+/* Keep the K best blocks of each (b, h), ranked by (score desc, index asc);
+ * write them in ascending block order to sel[b][h][0..K-1] (row stride
+ * sel_cap) and K to count[b][h].  Unused sel slots are left untouched. */
+void oracle_select(int B, int Hkv, const int32_t *seq_lens, const int32_t *block_size,
+                   int budget, const double *scores, int32_t *sel, int sel_cap, int32_t *count)
+{
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        for (int h = 0; h < Hkv; ++h) {
+            int64_t N = n_blocks(seq_lens[b], block_size[h]);
+            int64_t K = k_for(N, block_size[h], budget);
+            int64_t row0 = first_block(b, h, Hkv, seq_lens, block_size);
+            ranked *r = (ranked *)malloc(sizeof(ranked) * (size_t)N);
+            for (int64_t j = 0; j < N; ++j) { r[j].s = scores[row0 + j]; r[j].j = j; }
+            qsort(r, (size_t)N, sizeof(ranked), by_rank);
+            int32_t *out = sel + ((size_t)b * Hkv + h) * sel_cap;
+            int64_t k = K < sel_cap ? K : sel_cap;
+            for (int64_t i = 0; i < k; ++i) out[i] = (int32_t)r[i].j;
+            qsort(out, (size_t)k, sizeof(int32_t), by_index);
+            count[(size_t)b * Hkv + h] = (int32_t)k;
+            free(r);
+        }
+    }
+}
+
+/* ---- stage 4: sparse attention ------------------------------------------ */
+
+/* For each query head i of KV head h: the kept tokens T are the union of the
+ * selected blocks' token ranges (clipped to L_b).  z_t = sm_scale * q_i.k_t,
+ * out_i = sum_t softmax(z)_t v_t, lse_i = ln sum_t exp(z_t); fp64 with the
+ * maximum subtracted.  out: [B][Hq][D], lse: [B][Hq]. */
+void oracle_attend(int B, int Hq, int Hkv, int D, int max_pages, int is_bf16,
+                   const void *q, const void *k_cache, const void *v_cache,
+                   const int32_t *page_table, const int32_t *seq_lens, const int32_t *block_size,
+                   const int32_t *sel, int sel_cap, const int32_t *count, double sm_scale,
+                   double *out, double *lse)
+{
+    int G = Hq / Hkv;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        for (int h = 0; h < Hkv; ++h) {
+            int64_t L = seq_lens[b];
+            int bs = block_size[h];
+            const int32_t *blk = sel + ((size_t)b * Hkv + h) * sel_cap;
+            int64_t K = count[(size_t)b * Hkv + h];
+            int64_t ntok = 0;
+            int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)(K * bs + 1));
+            for (int64_t i = 0; i < K; ++i)
+                for (int64_t t = (int64_t)blk[i] * bs; t < (int64_t)(blk[i] + 1) * bs && t < L; ++t)
+                    tok[ntok++] = t;
+            double *z = (double *)malloc(sizeof(double) * (size_t)(ntok + 1));
+            for (int g = 0; g < G; ++g) {
+                int i = h * G + g;
+                size_t qrow = ((size_t)b * Hq + i) * D;
+                double m = -INFINITY;
+                for (int64_t n = 0; n < ntok; ++n) {
+                    double s = 0.0;
+                    for (int d = 0; d < D; ++d)
+                        s += elem(q, is_bf16, qrow + d) *
+                             cache_at(k_cache, is_bf16, page_table, max_pages, Hkv, D, b, h, tok[n], d);
+                    z[n] = sm_scale * s;
+                    if (z[n] > m) m = z[n];
+                }
+                double denom = 0.0;
+                for (int64_t n = 0; n < ntok; ++n) {
+                    z[n] = exp(z[n] - m);                 /* unnormalized weight */
+                    denom += z[n];
+                }
+                for (int d = 0; d < D; ++d) {
+                    double acc = 0.0;
+                    for (int64_t n = 0; n < ntok; ++n)
+                        acc += z[n] * cache_at(v_cache, is_bf16, page_table, max_pages, Hkv, D, b, h, tok[n], d);
+                    out[qrow + d] = ntok > 0 ? acc / denom : 0.0;
+                }
+                lse[(size_t)b * Hq + i] = ntok > 0 ? m + log(denom) : -INFINITY;
+            }
+            free(z);
+            free(tok);
+        }
+    }
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

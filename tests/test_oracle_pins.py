@@ -1,0 +1,265 @@
+"""Pins of the CPU oracle against what the AB-Sparse page and plain mathematics
+fix, independent of the oracle's own code (no GPU).
+
+Each test names the part it pins: Figure 1's four stages (centroid,
+dot-product estimation, top-K, sparse attention), Figure 8's INT4 asymmetric
+per-channel centroids, and the page-to-block mapping figure after Figure 8.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_abs_amd import workload as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+TINY = W.PRESETS[0]
+
+
+def small(dtype="f32", **kw):
+    base = dict(batch=2, num_q_heads=4, num_kv_heads=2, head_dim=64, context=300, dtype=dtype,
+                token_budget=64, needles_per_head=4, fixed_block_sizes=(16, 64))
+    base.update(kw)
+    return TINY.scaled(**base)
+
+
+# ---------------------------------------------------------------- centroid
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_centroid_block_size_one_is_the_key(oracle_mod, dtype):
+    """Special case: a one-token block's centroid is that token's key exactly."""
+    x = W.make_layer(small(dtype), seq_lens=[37, 20])
+    ones = np.ones(2, dtype=np.int32)
+    c = oracle_mod.centroids(x.k_cache, x.page_table, x.seq_lens, ones, dtype)
+    for b, h, r0, n in oracle_mod.block_rows(x.seq_lens, ones):
+        keys = W.contiguous_kv(x, "k", b)[h]
+        assert n == x.seq_lens[b]
+        np.testing.assert_array_equal(c[r0:r0 + n], keys)
+
+
+@pytest.mark.parametrize("bs", [(16, 64), (32, 16), (64, 32)])
+def test_centroid_matches_exact_mean_on_ragged_blocks(oracle_mod, bs):
+    """Brute force: the mean of a block's valid tokens, summed exactly (fsum),
+    rounded once to fp32; partial last blocks average only their valid tokens."""
+    x = W.make_layer(small("bf16", fixed_block_sizes=bs), seq_lens=[131, 77])
+    c = oracle_mod.centroids(x.k_cache, x.page_table, x.seq_lens, x.block_size, "bf16")
+    for b, h, r0, n in oracle_mod.block_rows(x.seq_lens, x.block_size):
+        keys = W.contiguous_kv(x, "k", b)[h].astype(np.float64)
+        L, s = int(x.seq_lens[b]), int(x.block_size[h])
+        for j in range(n):
+            blk = keys[j * s:min((j + 1) * s, L)]
+            want = np.float32([math.fsum(blk[:, d]) / len(blk) for d in range(blk.shape[1])])
+            np.testing.assert_array_equal(c[r0 + j], want)
+        assert np.abs(c[r0:r0 + n]).max() < W.PAD_SENTINEL / 4   # no padding slot leaked in
+
+
+def test_centroid_constant_and_scaled_keys(oracle_mod):
+    """Constant keys give that constant; doubling every key doubles every centroid."""
+    x = W.make_layer(small("f32"), seq_lens=[150, 64])
+    c = oracle_mod.centroids(x.k_cache, x.page_table, x.seq_lens, x.block_size, "f32")
+    c2 = oracle_mod.centroids(x.k_cache * np.float32(2), x.page_table, x.seq_lens, x.block_size, "f32")
+    np.testing.assert_array_equal(c2, 2 * c)
+    kc = np.full_like(x.k_cache, 0.375)
+    cc = oracle_mod.centroids(kc, x.page_table, x.seq_lens, x.block_size, "f32")
+    assert (cc == np.float32(0.375)).all()
+
+
+def test_page_table_permutation_invariance(oracle_mod):
+    """Shuffled and identity page tables hold the same logical cache, so every
+    stage's output must be bit-identical."""
+    w = small("bf16", batch=3, fixed_block_sizes=(32, 16))
+    a = W.make_layer(w, seq_lens=[300, 129, 64], shuffle_pages=True)
+    b = W.make_layer(w, seq_lens=[300, 129, 64], shuffle_pages=False)
+    assert not np.array_equal(a.page_table, b.page_table)
+    ra, rb = oracle_mod.run(a), oracle_mod.run(b)
+    for f in ("cents", "scores", "sel", "count", "out", "lse"):
+        np.testing.assert_array_equal(getattr(ra, f), getattr(rb, f))
+
+
+# ---------------------------------------------------------------- quantization
+
+def _dequant(qz, rows, D):
+    out = np.empty(qz.codes.shape, dtype=np.float64)
+    for b, h, r0, n in rows:
+        out[r0:r0 + n] = qz.codes[r0:r0 + n] * qz.scale[b, h].astype(np.float64) + qz.lo[b, h]
+    return out
+
+
+def test_int4_error_bound_and_end_codes(oracle_mod):
+    """|c_hat - c| <= scale/2 (plus fp32 rounding of the quotient); the channel
+    minimum gets code 0, the maximum code 15; codes stay in [0, 15]."""
+    x = W.make_layer(small("bf16", fixed_block_sizes=(16, 32)), seq_lens=[300, 211])
+    c = oracle_mod.centroids(x.k_cache, x.page_table, x.seq_lens, x.block_size, "bf16")
+    qz = oracle_mod.quantize(c, x.seq_lens, x.block_size)
+    rows = oracle_mod.block_rows(x.seq_lens, x.block_size)
+    chat = _dequant(qz, rows, c.shape[1])
+    assert qz.codes.max() <= 15
+    for b, h, r0, n in rows:
+        cb = c[r0:r0 + n].astype(np.float64)
+        sc = qz.scale[b, h].astype(np.float64)
+        err = np.abs(chat[r0:r0 + n] - cb)
+        assert (err <= sc / 2 * (1 + 1e-5) + 1e-7).all()
+        np.testing.assert_array_equal(qz.lo[b, h], c[r0:r0 + n].min(axis=0))
+        np.testing.assert_allclose(sc * 15, cb.max(axis=0) - cb.min(axis=0), rtol=1e-6)
+        cols = np.arange(c.shape[1])
+        assert (qz.codes[r0 + cb.argmin(axis=0), cols] == 0).all()
+        assert (qz.codes[r0 + cb.argmax(axis=0), cols] == 15).all()
+
+
+def test_int4_code_is_the_nearest_level(oracle_mod):
+    """Brute force over the 16 levels lo + k*scale: the code is the nearest one
+    (exact midpoints excluded)."""
+    rng = np.random.default_rng(5)
+    c = (rng.standard_normal((200, 16)) * rng.uniform(0.1, 20, 16)).astype(np.float32)
+    qz = oracle_mod.quantize(c, [200 * 16], [16])
+    lv = qz.lo[0, 0][None, :, None] + np.arange(16)[None, None, :] * qz.scale[0, 0].astype(np.float64)[None, :, None]
+    dist = np.abs(lv - c.astype(np.float64)[:, :, None])
+    best = dist.argmin(axis=2)
+    srt = np.sort(dist, axis=2)
+    clear = (srt[:, :, 1] - srt[:, :, 0]) > 1e-5 * qz.scale[0, 0]
+    assert clear.mean() > 0.99
+    np.testing.assert_array_equal(qz.codes[clear], best[clear])
+
+
+def test_int4_constant_channel_is_exact(oracle_mod):
+    """A channel equal in every block: scale 0, code 0, dequantizes to the value."""
+    rng = np.random.default_rng(1)
+    c = rng.standard_normal((40, 8)).astype(np.float32)
+    c[:, 3] = np.float32(-2.71875)
+    qz = oracle_mod.quantize(c, [40 * 16], [16])
+    assert qz.scale[0, 0, 3] == 0 and (qz.codes[:, 3] == 0).all() and qz.lo[0, 0, 3] == c[0, 3]
+    assert (qz.scale[0, 0, np.arange(8) != 3] > 0).all()
+
+
+# ---------------------------------------------------------------- estimation
+
+def test_scores_are_group_query_dot_dequantized_centroid(oracle_mod):
+    """Closed form: S_j = (sum of the group's queries) . (code*scale + lo),
+    recomputed with numpy from independent pieces; equals the sum of per-head dots."""
+    w = small("bf16", num_q_heads=8, num_kv_heads=2, fixed_block_sizes=(32, 16))
+    x = W.make_layer(w, seq_lens=[300, 99])
+    c = oracle_mod.centroids(x.k_cache, x.page_table, x.seq_lens, x.block_size, "bf16")
+    qz = oracle_mod.quantize(c, x.seq_lens, x.block_size)
+    s = oracle_mod.scores(x.q, qz, x.seq_lens, x.block_size, "bf16")
+    rows = oracle_mod.block_rows(x.seq_lens, x.block_size)
+    chat = _dequant(qz, rows, c.shape[1])
+    qf = W.to_f32(x.q, "bf16").astype(np.float64)
+    G = w.group
+    for b, h, r0, n in rows:
+        per_head = chat[r0:r0 + n] @ qf[b, h * G:(h + 1) * G].T       # [n][G]
+        np.testing.assert_allclose(s[r0:r0 + n], per_head.sum(axis=1), rtol=1e-12, atol=1e-9)
+    s2 = oracle_mod.scores(W.f32_to_bf16_bits(2 * qf.astype(np.float32)), qz, x.seq_lens, x.block_size, "bf16")
+    np.testing.assert_array_equal(s2, 2 * s)
+
+
+# ---------------------------------------------------------------- top-K
+
+def _brute_topk(s, k):
+    order = sorted(range(len(s)), key=lambda j: (-s[j], j))
+    return sorted(order[:k])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_matches_full_sort(oracle_mod, seed):
+    """Brute force: a full sort of (-S, j) on N <= 256, with many exact ties."""
+    rng = np.random.default_rng(seed)
+    bs = [16, 32, 64]
+    lens = [int(rng.integers(1, 256 * 16)), int(rng.integers(1, 1000))]
+    n_tot = oracle_mod.total_blocks(lens, bs)
+    s = np.round(rng.standard_normal(n_tot) * 4) / 4          # coarse grid -> ties
+    budget = int(rng.integers(1, 600))
+    cap = oracle_mod.sel_capacity(lens, bs, budget)
+    sel, cnt = oracle_mod.select(s, lens, bs, budget, cap)
+    for b, h, r0, n in oracle_mod.block_rows(lens, bs):
+        k = min(n, max(1, budget // bs[h]))
+        assert cnt[b, h] == k
+        got = sel[b, h, :k].tolist()
+        assert got == _brute_topk(s[r0:r0 + n].tolist(), k)
+        chosen = np.zeros(n, bool)
+        chosen[got] = True
+        if k < n:
+            assert s[r0:r0 + n][chosen].min() >= s[r0:r0 + n][~chosen].max()
+
+
+def test_topk_budget_rule_and_all_selected(oracle_mod):
+    """K = min(N, max(1, budget/bs)); a budget >= the context selects every block."""
+    assert oracle_mod.k_of(131072, 16, 4096) == 256
+    assert oracle_mod.k_of(131072, 64, 4096) == 64
+    assert oracle_mod.k_of(100, 64, 10) == 1
+    assert oracle_mod.k_of(100, 16, 4096) == 7
+    s = np.arange(10, dtype=np.float64)
+    sel, cnt = oracle_mod.select(s, [150], [16], 4096, 10)
+    assert cnt[0, 0] == 10 and sel[0, 0].tolist() == list(range(10))
+
+
+# ---------------------------------------------------------------- attention
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_all_blocks_selected_equals_dense_attention(oracle_mod, dtype):
+    """With a budget covering the whole context the sparse path is dense
+    attention; checked against torch's scaled_dot_product_attention in fp64
+    on the CPU (GQA: query head i reads KV head i // G)."""
+    w = small(dtype, num_q_heads=8, num_kv_heads=2, fixed_block_sizes=(64, 16))
+    x = W.make_layer(w, seq_lens=[300, 77])
+    sm = 0.125
+    r = oracle_mod.run(x, sm_scale=sm, budget=10 ** 6)
+    qf = torch.from_numpy(W.to_f32(x.q, dtype).astype(np.float64))
+    for b in range(w.batch):
+        k = torch.from_numpy(W.contiguous_kv(x, "k", b).astype(np.float64)).repeat_interleave(w.group, 0)
+        v = torch.from_numpy(W.contiguous_kv(x, "v", b).astype(np.float64)).repeat_interleave(w.group, 0)
+        qb = qf[b][:, None, :]                                           # [Hq][1][D]
+        ref = torch.nn.functional.scaled_dot_product_attention(qb, k, v, scale=sm)[:, 0]
+        np.testing.assert_allclose(r.out[b], ref.numpy(), rtol=1e-10, atol=1e-12)
+        lse = torch.logsumexp(sm * (qb @ k.transpose(1, 2))[:, 0], dim=-1)
+        np.testing.assert_allclose(r.lse[b], lse.numpy(), rtol=1e-12)
+
+
+def test_single_token_attention_returns_its_value(oracle_mod):
+    """One cached token: the softmax weight is 1, so out = v and lse = z."""
+    x = W.make_layer(small("f32"), seq_lens=[1, 1])
+    r = oracle_mod.run(x, sm_scale=0.5)
+    qf = W.to_f32(x.q, "f32").astype(np.float64)
+    for b in range(2):
+        k0 = W.contiguous_kv(x, "k", b)[:, 0].astype(np.float64)
+        v0 = W.contiguous_kv(x, "v", b)[:, 0].astype(np.float64)
+        for i in range(4):
+            np.testing.assert_array_equal(r.out[b, i], v0[i // 2])
+            np.testing.assert_allclose(r.lse[b, i], 0.5 * qf[b, i] @ k0[i // 2], rtol=1e-14)
+
+
+def test_page_mapping_worked_example(oracle_mod):
+    """The mapping figure after Figure 8: head A (stride 4) keeps block 1, head
+    B (stride 2) keeps blocks 1 and 3, and both read four pages.  Keys are
+    built so that exactly those blocks win; every value carries its logical
+    page number as a one-hot channel, so the output shows which pages were read."""
+    g = json.load(open(os.path.join(GOLDEN, "fig8_page_mapping.json")))
+    P = g["page_size"]
+    heads = g["heads"]
+    D, npages = 64, 8
+    L = npages * P
+    w = small("f32", batch=1, num_q_heads=2, num_kv_heads=2, fixed_block_sizes=None)
+    x = W.make_layer(w, seq_lens=[L], block_sizes=[hd["stride"] * P for hd in heads], needles=False)
+    x.q[:] = 0
+    x.q[0, :, 0] = 1.0
+    keys = np.zeros((2, L, D), np.float32)
+    vals = np.zeros((2, L, D), np.float32)
+    for h, hd in enumerate(heads):
+        st = hd["stride"] * P
+        for j in hd["topk"]:
+            keys[h, j * st:(j + 1) * st, 0] = 3.0
+        vals[h, np.arange(L), np.arange(L) // P] = 1.0
+    for lp in range(npages):
+        x.k_cache[x.page_table[0, lp]] = keys[:, lp * P:(lp + 1) * P]
+        x.v_cache[x.page_table[0, lp]] = vals[:, lp * P:(lp + 1) * P]
+    budget = g["equal_page_count"] * P
+    r = oracle_mod.run(x, sm_scale=1.0, budget=budget)
+    for h, hd in enumerate(heads):
+        k = int(r.count[0, h])
+        assert r.sel[0, h, :k].tolist() == hd["topk"]
+        read = np.nonzero(r.out[0, h] > 1e-12)[0].tolist()
+        assert read == g["expected_logical_pages"][hd["name"]]
+        assert len(read) == g["equal_page_count"]
+        np.testing.assert_allclose(r.out[0, h, read], 1.0 / len(read), rtol=1e-12)
