@@ -1,0 +1,277 @@
+"""Python binding of libabs.so, the AB-Sparse decode library (include/abs.h).
+
+Argument marshalling only: the functions below have the C names, take the
+same descriptors (as ctypes structures) and raw device pointers, and call
+straight into the library.  Every step of the decode path runs in the HIP
+kernels behind those calls; there is no fallback.  If libabs.so is missing
+or does not load, every call raises.
+
+`PagedKV` is a convenience holder that keeps torch tensors alive and fills
+the descriptors from them (PyTorch supplies device memory and streams only).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libabs.so")
+
+ABS_OK, ABS_ERR_INVALID_ARG, ABS_ERR_UNSUPPORTED, ABS_ERR_WORKSPACE, ABS_ERR_HIP = range(5)
+ABS_F32, ABS_BF16 = 0, 1
+ABS_OP_BUILD, ABS_OP_SELECT, ABS_OP_DECODE = 0, 1, 2
+
+EXPORTS = ("abs_status_str", "abs_last_error", "abs_total_blocks", "abs_centroid_offsets",
+           "abs_select_capacity", "abs_workspace_bytes", "abs_build_centroids", "abs_score_select",
+           "abs_sparse_decode")
+
+
+class abs_paged_kv(C.Structure):
+    _fields_ = [("num_seqs", C.c_int32), ("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("page_size", C.c_int32), ("max_pages_per_seq", C.c_int32),
+                ("num_pages", C.c_int64), ("kv_dtype", C.c_int32), ("reserved0", C.c_int32),
+                ("k_cache", C.c_void_p), ("v_cache", C.c_void_p), ("page_table", C.c_void_p),
+                ("seq_lens", C.c_void_p), ("seq_lens_host", C.c_void_p)]
+
+
+class abs_block_map(C.Structure):
+    _fields_ = [("block_size_host", C.c_void_p), ("block_size", C.c_void_p), ("centroid_off", C.c_void_p)]
+
+
+class abs_centroids(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("scale", C.c_void_p), ("lo", C.c_void_p)]
+
+
+class AbsError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status} ({detail})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libabs.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m block_sparse_attention_abs_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        P, KV, MAP, CEN = C.c_void_p, C.POINTER(abs_paged_kv), C.POINTER(abs_block_map), C.POINTER(abs_centroids)
+        i32, st = C.c_int32, C.c_int
+        L.abs_status_str.restype = C.c_char_p
+        L.abs_status_str.argtypes = [st]
+        L.abs_last_error.restype = C.c_char_p
+        L.abs_last_error.argtypes = []
+        L.abs_total_blocks.restype = st
+        L.abs_total_blocks.argtypes = [KV, MAP, C.POINTER(C.c_int64)]
+        L.abs_centroid_offsets.restype = st
+        L.abs_centroid_offsets.argtypes = [KV, MAP, P]
+        L.abs_select_capacity.restype = st
+        L.abs_select_capacity.argtypes = [KV, MAP, i32, C.POINTER(C.c_int32)]
+        L.abs_workspace_bytes.restype = st
+        L.abs_workspace_bytes.argtypes = [KV, MAP, i32, st, C.POINTER(C.c_size_t)]
+        L.abs_build_centroids.restype = st
+        L.abs_build_centroids.argtypes = [KV, MAP, CEN, P, C.c_size_t, P]
+        L.abs_score_select.restype = st
+        L.abs_score_select.argtypes = [KV, MAP, CEN, P, i32, P, i32, P, P, C.c_size_t, P]
+        L.abs_sparse_decode.restype = st
+        L.abs_sparse_decode.argtypes = [KV, MAP, P, P, i32, P, i32, C.c_float, P, P, P, C.c_size_t, P]
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != ABS_OK:
+        L = lib()
+        raise AbsError(status, where, f"{L.abs_status_str(status).decode()}: {L.abs_last_error().decode()}")
+
+
+# ---- the C calls, same names ------------------------------------------------
+
+def abs_status_str(status: int) -> str:
+    return lib().abs_status_str(status).decode()
+
+
+def abs_last_error() -> str:
+    return lib().abs_last_error().decode()
+
+
+def abs_total_blocks(kv: abs_paged_kv, bmap: abs_block_map) -> int:
+    n = C.c_int64()
+    _check(lib().abs_total_blocks(C.byref(kv), C.byref(bmap), C.byref(n)), "abs_total_blocks")
+    return n.value
+
+
+def abs_centroid_offsets(kv: abs_paged_kv, bmap: abs_block_map) -> np.ndarray:
+    off = np.zeros(kv.num_seqs * kv.num_kv_heads + 1, dtype=np.int64)
+    _check(lib().abs_centroid_offsets(C.byref(kv), C.byref(bmap), off.ctypes.data), "abs_centroid_offsets")
+    return off
+
+
+def abs_select_capacity(kv: abs_paged_kv, bmap: abs_block_map, token_budget: int) -> int:
+    cap = C.c_int32()
+    _check(lib().abs_select_capacity(C.byref(kv), C.byref(bmap), token_budget, C.byref(cap)),
+           "abs_select_capacity")
+    return cap.value
+
+
+def abs_workspace_bytes(kv: abs_paged_kv, bmap: abs_block_map, token_budget: int, op: int) -> int:
+    n = C.c_size_t()
+    _check(lib().abs_workspace_bytes(C.byref(kv), C.byref(bmap), token_budget, op, C.byref(n)),
+           "abs_workspace_bytes")
+    return n.value
+
+
+def abs_build_centroids(kv, bmap, cents, ws_ptr: int, ws_bytes: int, stream: int) -> None:
+    _check(lib().abs_build_centroids(C.byref(kv), C.byref(bmap), C.byref(cents), ws_ptr, ws_bytes, stream),
+           "abs_build_centroids")
+
+
+def abs_score_select(kv, bmap, cents, q_ptr: int, token_budget: int, sel_ptr: int, sel_cap: int,
+                     count_ptr: int, ws_ptr: int, ws_bytes: int, stream: int) -> None:
+    _check(lib().abs_score_select(C.byref(kv), C.byref(bmap), C.byref(cents), q_ptr, token_budget, sel_ptr,
+                                  sel_cap, count_ptr, ws_ptr, ws_bytes, stream), "abs_score_select")
+
+
+def abs_sparse_decode(kv, bmap, q_ptr: int, sel_ptr: int, sel_cap: int, count_ptr: int, token_budget: int,
+                      sm_scale: float, out_ptr: int, lse_ptr: Optional[int], ws_ptr: int, ws_bytes: int,
+                      stream: int) -> None:
+    _check(lib().abs_sparse_decode(C.byref(kv), C.byref(bmap), q_ptr, sel_ptr, sel_cap, count_ptr, token_budget,
+                                   sm_scale, out_ptr, lse_ptr, ws_ptr, ws_bytes, stream), "abs_sparse_decode")
+
+
+# ---- torch-side holder ------------------------------------------------------
+
+def _ptr(t) -> int:
+    return int(t.data_ptr()) if t is not None else 0
+
+
+def torch_dtype(kv_dtype: str):
+    import torch
+    return torch.bfloat16 if kv_dtype == "bf16" else torch.float32
+
+
+def upload(a: np.ndarray, device, kv_dtype: Optional[str] = None):
+    """Host array -> device tensor (bf16 bit patterns become torch.bfloat16)."""
+    import torch
+    if kv_dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+@dataclass
+class PagedKV:
+    """One layer's paged cache + block map on the device, with its descriptors."""
+    k_cache: object
+    v_cache: object
+    page_table: object
+    seq_lens: object
+    seq_lens_host: np.ndarray
+    block_size: object
+    block_size_host: np.ndarray
+    centroid_off: object
+    num_q_heads: int
+    kv_dtype: str
+    kv: abs_paged_kv = field(init=False)
+    bmap: abs_block_map = field(init=False)
+
+    def __post_init__(self):
+        self.seq_lens_host = np.ascontiguousarray(self.seq_lens_host, dtype=np.int32)
+        self.block_size_host = np.ascontiguousarray(self.block_size_host, dtype=np.int32)
+        P, Hkv, page, D = self.k_cache.shape
+        self.kv = abs_paged_kv(
+            num_seqs=len(self.seq_lens_host), num_q_heads=self.num_q_heads, num_kv_heads=Hkv, head_dim=D,
+            page_size=page, max_pages_per_seq=self.page_table.shape[1], num_pages=P,
+            kv_dtype=ABS_BF16 if self.kv_dtype == "bf16" else ABS_F32, reserved0=0,
+            k_cache=_ptr(self.k_cache), v_cache=_ptr(self.v_cache), page_table=_ptr(self.page_table),
+            seq_lens=_ptr(self.seq_lens), seq_lens_host=self.seq_lens_host.ctypes.data)
+        self.bmap = abs_block_map(block_size_host=self.block_size_host.ctypes.data,
+                                  block_size=_ptr(self.block_size), centroid_off=_ptr(self.centroid_off))
+
+    @classmethod
+    def from_host(cls, q_heads: int, k_cache: np.ndarray, v_cache: np.ndarray, page_table: np.ndarray,
+                  seq_lens: np.ndarray, block_size: np.ndarray, kv_dtype: str, device="cuda") -> "PagedKV":
+        import torch
+        sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        bs = np.ascontiguousarray(block_size, dtype=np.int32)
+        self = cls(upload(k_cache, device, kv_dtype), upload(v_cache, device, kv_dtype),
+                   upload(np.ascontiguousarray(page_table, dtype=np.int32), device),
+                   upload(sl, device), sl, upload(bs, device), bs,
+                   torch.zeros(len(sl) * len(bs) + 1, dtype=torch.int64, device=device), q_heads, kv_dtype)
+        off = abs_centroid_offsets(self.kv, self.bmap)
+        self.centroid_off.copy_(torch.from_numpy(off))
+        return self
+
+    @property
+    def head_dim(self) -> int:
+        return int(self.kv.head_dim)
+
+    def total_blocks(self) -> int:
+        return abs_total_blocks(self.kv, self.bmap)
+
+    def select_capacity(self, budget: int) -> int:
+        return abs_select_capacity(self.kv, self.bmap, budget)
+
+    def workspace_bytes(self, budget: int, op: int) -> int:
+        return abs_workspace_bytes(self.kv, self.bmap, budget, op)
+
+
+@dataclass
+class Centroids:
+    codes: object      # uint8 [total_blocks][D/2]
+    scale: object      # f32 [B][Hkv][D]
+    lo: object         # f32 [B][Hkv][D]
+    desc: abs_centroids = field(init=False)
+
+    def __post_init__(self):
+        self.desc = abs_centroids(codes=_ptr(self.codes), scale=_ptr(self.scale), lo=_ptr(self.lo))
+
+    @classmethod
+    def empty(cls, kv: PagedKV) -> "Centroids":
+        import torch
+        dev = kv.k_cache.device
+        B, Hkv, D = kv.kv.num_seqs, kv.kv.num_kv_heads, kv.kv.head_dim
+        return cls(torch.empty(kv.total_blocks(), D // 2, dtype=torch.uint8, device=dev),
+                   torch.empty(B, Hkv, D, dtype=torch.float32, device=dev),
+                   torch.empty(B, Hkv, D, dtype=torch.float32, device=dev))
+
+
+def current_stream() -> int:
+    import torch
+    return int(torch.cuda.current_stream().cuda_stream)
+
+
+def workspace(nbytes: int, device="cuda"):
+    import torch
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def build_centroids(kv: PagedKV, cents: Centroids, ws=None, stream: Optional[int] = None) -> Centroids:
+    need = kv.workspace_bytes(1, ABS_OP_BUILD)
+    ws = workspace(need, kv.k_cache.device) if ws is None else ws
+    abs_build_centroids(kv.kv, kv.bmap, cents.desc, _ptr(ws), ws.numel(),
+                        current_stream() if stream is None else stream)
+    return cents
+
+
+def score_select(kv: PagedKV, cents: Centroids, q, budget: int, sel, count, ws=None,
+                 stream: Optional[int] = None) -> None:
+    need = kv.workspace_bytes(budget, ABS_OP_SELECT)
+    ws = workspace(need, kv.k_cache.device) if ws is None else ws
+    abs_score_select(kv.kv, kv.bmap, cents.desc, _ptr(q), budget, _ptr(sel), int(sel.shape[-1]), _ptr(count),
+                     _ptr(ws), ws.numel(), current_stream() if stream is None else stream)
+
+
+def sparse_decode(kv: PagedKV, q, sel, count, budget: int, sm_scale: float, out, lse=None, ws=None,
+                  stream: Optional[int] = None) -> None:
+    need = kv.workspace_bytes(budget, ABS_OP_DECODE)
+    ws = workspace(need, kv.k_cache.device) if ws is None else ws
+    abs_sparse_decode(kv.kv, kv.bmap, _ptr(q), _ptr(sel), int(sel.shape[-1]), _ptr(count), budget, sm_scale,
+                      _ptr(out), _ptr(lse) if lse is not None else None, _ptr(ws), ws.numel(),
+                      current_stream() if stream is None else stream)

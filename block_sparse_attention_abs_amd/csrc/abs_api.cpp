@@ -1,0 +1,335 @@
+// C ABI of the AB-Sparse decode library (declared in include/abs.h).
+//
+// This layer owns everything the host knows before a launch: it validates
+// the descriptors, derives the block geometry (N_{b,h} = ceil(L_b / bs_h),
+// K_{b,h} = min(N, max(1, floor(budget / bs_h))), the CSR centroid offsets,
+// the page count each head reads), carves the caller's workspace, sizes the
+// grids, and enqueues the kernels on the caller's stream.  It never
+// allocates, frees or synchronizes, and nothing is read back from the device.
+#include "abs.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+abs_status fail(abs_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+abs_status ok() {
+    g_err[0] = '\0';
+    return ABS_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Everything derived on the host from the descriptors (and budget).
+struct Plan {
+    absk::Geom g{};
+    absk::DType dt{};
+    int64_t total_blocks = 0;
+    int max_n = 0;            // largest N_{b,h}
+    int sel_cap = 0;          // largest K_{b,h}
+    int max_pages_read = 0;   // largest K_{b,h} * (bs_h / 16)
+};
+
+abs_status check_geometry(const abs_paged_kv* kv, const abs_block_map* map, Plan* p) {
+    if (kv == nullptr || map == nullptr) return fail(ABS_ERR_INVALID_ARG, "null descriptor");
+    if (kv->num_seqs < 1 || kv->num_q_heads < 1 || kv->num_kv_heads < 1)
+        return fail(ABS_ERR_INVALID_ARG, "num_seqs, num_q_heads, num_kv_heads must be >= 1");
+    if (kv->num_q_heads % kv->num_kv_heads != 0)
+        return fail(ABS_ERR_INVALID_ARG, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                    kv->num_q_heads, kv->num_kv_heads);
+    const int G = kv->num_q_heads / kv->num_kv_heads;
+    if (G > 8) return fail(ABS_ERR_UNSUPPORTED, "query group size %d > 8", G);
+    if (kv->head_dim != 64 && kv->head_dim != 128)
+        return fail(ABS_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", kv->head_dim);
+    if (kv->page_size != 16) return fail(ABS_ERR_UNSUPPORTED, "page_size %d (supported: 16)", kv->page_size);
+    if (kv->kv_dtype != ABS_F32 && kv->kv_dtype != ABS_BF16)
+        return fail(ABS_ERR_UNSUPPORTED, "kv_dtype %d", kv->kv_dtype);
+    if (kv->reserved0 != 0) return fail(ABS_ERR_INVALID_ARG, "reserved0 must be 0");
+    if (kv->max_pages_per_seq < 1 || kv->num_pages < 1)
+        return fail(ABS_ERR_INVALID_ARG, "max_pages_per_seq and num_pages must be >= 1");
+    if (kv->seq_lens_host == nullptr) return fail(ABS_ERR_INVALID_ARG, "seq_lens_host is null");
+    if (map->block_size_host == nullptr) return fail(ABS_ERR_INVALID_ARG, "block_size_host is null");
+    const int64_t max_len = (int64_t)kv->max_pages_per_seq * 16;
+    for (int b = 0; b < kv->num_seqs; ++b) {
+        const int L = kv->seq_lens_host[b];
+        if (L < 1 || L > max_len)
+            return fail(ABS_ERR_INVALID_ARG, "seq_lens[%d] = %d outside [1, %lld]", b, L, (long long)max_len);
+    }
+    for (int h = 0; h < kv->num_kv_heads; ++h) {
+        const int bs = map->block_size_host[h];
+        if (bs < 1) return fail(ABS_ERR_INVALID_ARG, "block_size[%d] = %d", h, bs);
+        if (bs != 16 && bs != 32 && bs != 64)
+            return fail(ABS_ERR_UNSUPPORTED, "block_size[%d] = %d (supported: 16, 32, 64)", h, bs);
+    }
+    p->dt = kv->kv_dtype == ABS_BF16 ? absk::DType::BF16 : absk::DType::F32;
+    absk::Geom& g = p->g;
+    g.B = kv->num_seqs;
+    g.Hq = kv->num_q_heads;
+    g.Hkv = kv->num_kv_heads;
+    g.D = kv->head_dim;
+    g.G = G;
+    g.max_pages = kv->max_pages_per_seq;
+    g.num_pages = kv->num_pages;
+    g.k = kv->k_cache;
+    g.v = kv->v_cache;
+    g.page_table = kv->page_table;
+    g.seq_lens = kv->seq_lens;
+    g.block_size = map->block_size;
+    g.off = map->centroid_off;
+    p->total_blocks = 0;
+    p->max_n = 0;
+    for (int b = 0; b < g.B; ++b)
+        for (int h = 0; h < g.Hkv; ++h) {
+            const int64_t n = ceil_div64(kv->seq_lens_host[b], map->block_size_host[h]);
+            p->total_blocks += n;
+            p->max_n = std::max<int>(p->max_n, (int)n);
+        }
+    return ok();
+}
+
+abs_status plan_budget(const abs_paged_kv* kv, const abs_block_map* map, int32_t budget, Plan* p) {
+    if (budget < 1) return fail(ABS_ERR_INVALID_ARG, "token_budget %d < 1", budget);
+    p->sel_cap = 0;
+    p->max_pages_read = 0;
+    for (int b = 0; b < kv->num_seqs; ++b)
+        for (int h = 0; h < kv->num_kv_heads; ++h) {
+            const int bs = map->block_size_host[h];
+            const int64_t n = ceil_div64(kv->seq_lens_host[b], bs);
+            const int64_t k = std::min<int64_t>(n, std::max<int64_t>(1, budget / bs));
+            p->sel_cap = std::max<int>(p->sel_cap, (int)k);
+            p->max_pages_read = std::max<int>(p->max_pages_read, (int)(k * (bs / 16)));
+        }
+    return ok();
+}
+
+abs_status require_device(const Plan& p, bool need_v) {
+    const absk::Geom& g = p.g;
+    if (g.k == nullptr || (need_v && g.v == nullptr)) return fail(ABS_ERR_INVALID_ARG, "null cache pointer");
+    if (g.page_table == nullptr || g.seq_lens == nullptr)
+        return fail(ABS_ERR_INVALID_ARG, "null page_table or seq_lens");
+    if (g.block_size == nullptr || g.off == nullptr)
+        return fail(ABS_ERR_INVALID_ARG, "null block_size or centroid_off");
+    return ok();
+}
+
+// ---- workspace layouts ----------------------------------------------------
+
+struct BuildLayout {
+    int tiles = 0;
+    size_t staging = 0, pmin = 0, pmax = 0, bytes = 0;
+};
+
+BuildLayout build_layout(const Plan& p) {
+    BuildLayout l;
+    l.tiles = (int)ceil_div64(p.max_n, absk::kBuildTile);
+    const size_t part = align_up((size_t)p.g.B * p.g.Hkv * l.tiles * p.g.D * sizeof(float));
+    l.staging = 0;
+    l.pmin = align_up((size_t)p.total_blocks * p.g.D * sizeof(float));
+    l.pmax = l.pmin + part;
+    l.bytes = l.pmax + part;
+    return l;
+}
+
+size_t select_bytes(const Plan& p) { return align_up((size_t)p.total_blocks * sizeof(float)); }
+
+struct DecodeLayout {
+    int ppw = 8, splits = 1;
+    size_t ml = 0, o = 0, bytes = 0;
+};
+
+// Pages per workgroup: the largest of 8/4/2/1 that still gives >= 4
+// workgroups per compute unit (256 CUs), so that small batches fill the chip.
+DecodeLayout decode_layout(const Plan& p) {
+    DecodeLayout l;
+    const int64_t heads = (int64_t)p.g.B * p.g.Hkv;
+    const int maxp = std::max(p.max_pages_read, 1);
+    l.ppw = 1;
+    for (int ppw : {8, 4, 2}) {
+        if (heads * ceil_div64(maxp, ppw) >= 1024) {
+            l.ppw = ppw;
+            break;
+        }
+    }
+    l.splits = (int)ceil_div64(maxp, l.ppw);
+    const size_t rows = (size_t)p.g.B * p.g.Hq * l.splits;
+    l.ml = 0;
+    l.o = align_up(rows * 2 * sizeof(float));
+    l.bytes = l.o + align_up(rows * p.g.D * sizeof(float));
+    return l;
+}
+
+char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+abs_status hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(ABS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* abs_status_str(abs_status s) {
+    switch (s) {
+        case ABS_OK: return "ok";
+        case ABS_ERR_INVALID_ARG: return "invalid argument";
+        case ABS_ERR_UNSUPPORTED: return "unsupported configuration";
+        case ABS_ERR_WORKSPACE: return "workspace too small";
+        case ABS_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* abs_last_error(void) { return g_err; }
+
+abs_status abs_total_blocks(const abs_paged_kv* kv, const abs_block_map* map, int64_t* total) {
+    if (total == nullptr) return fail(ABS_ERR_INVALID_ARG, "null output");
+    Plan p;
+    if (abs_status st = check_geometry(kv, map, &p)) return st;
+    *total = p.total_blocks;
+    return ok();
+}
+
+abs_status abs_centroid_offsets(const abs_paged_kv* kv, const abs_block_map* map, int64_t* off_host) {
+    if (off_host == nullptr) return fail(ABS_ERR_INVALID_ARG, "null output");
+    Plan p;
+    if (abs_status st = check_geometry(kv, map, &p)) return st;
+    int64_t run = 0;
+    for (int b = 0; b < kv->num_seqs; ++b)
+        for (int h = 0; h < kv->num_kv_heads; ++h) {
+            off_host[(int64_t)b * kv->num_kv_heads + h] = run;
+            run += ceil_div64(kv->seq_lens_host[b], map->block_size_host[h]);
+        }
+    off_host[(int64_t)kv->num_seqs * kv->num_kv_heads] = run;
+    return ok();
+}
+
+abs_status abs_select_capacity(const abs_paged_kv* kv, const abs_block_map* map, int32_t token_budget,
+                               int32_t* sel_cap) {
+    if (sel_cap == nullptr) return fail(ABS_ERR_INVALID_ARG, "null output");
+    Plan p;
+    if (abs_status st = check_geometry(kv, map, &p)) return st;
+    if (abs_status st = plan_budget(kv, map, token_budget, &p)) return st;
+    *sel_cap = p.sel_cap;
+    return ok();
+}
+
+abs_status abs_workspace_bytes(const abs_paged_kv* kv, const abs_block_map* map, int32_t token_budget, abs_op op,
+                               size_t* bytes) {
+    if (bytes == nullptr) return fail(ABS_ERR_INVALID_ARG, "null output");
+    Plan p;
+    if (abs_status st = check_geometry(kv, map, &p)) return st;
+    switch (op) {
+        case ABS_OP_BUILD: *bytes = build_layout(p).bytes; return ok();
+        case ABS_OP_SELECT: *bytes = select_bytes(p); return ok();
+        case ABS_OP_DECODE:
+            if (abs_status st = plan_budget(kv, map, token_budget, &p)) return st;
+            *bytes = decode_layout(p).bytes;
+            return ok();
+    }
+    return fail(ABS_ERR_INVALID_ARG, "unknown op %d", (int)op);
+}
+
+abs_status abs_build_centroids(const abs_paged_kv* kv, const abs_block_map* map, const abs_centroids* out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    Plan p;
+    if (abs_status st = check_geometry(kv, map, &p)) return st;
+    if (abs_status st = require_device(p, false)) return st;
+    if (out == nullptr || out->codes == nullptr || out->scale == nullptr || out->lo == nullptr)
+        return fail(ABS_ERR_INVALID_ARG, "null centroid output");
+    const BuildLayout l = build_layout(p);
+    if (workspace == nullptr || workspace_bytes < l.bytes)
+        return fail(ABS_ERR_WORKSPACE, "build needs %zu workspace bytes, got %zu", l.bytes, workspace_bytes);
+    absk::BuildArgs a;
+    a.codes = out->codes;
+    a.scale = out->scale;
+    a.lo = out->lo;
+    a.staging = reinterpret_cast<float*>(ws_at(workspace, l.staging));
+    a.pmin = reinterpret_cast<float*>(ws_at(workspace, l.pmin));
+    a.pmax = reinterpret_cast<float*>(ws_at(workspace, l.pmax));
+    a.tiles = l.tiles;
+    return hip_status(absk::launch_build(p.g, p.dt, a, static_cast<hipStream_t>(stream)), "build_centroids");
+}
+
+abs_status abs_score_select(const abs_paged_kv* kv, const abs_block_map* map, const abs_centroids* cents,
+                            const void* q, int32_t token_budget, int32_t* sel, int32_t sel_cap,
+                            int32_t* sel_count, void* workspace, size_t workspace_bytes, void* stream) {
+    Plan p;
+    if (abs_status st = check_geometry(kv, map, &p)) return st;
+    if (abs_status st = require_device(p, false)) return st;
+    if (abs_status st = plan_budget(kv, map, token_budget, &p)) return st;
+    if (cents == nullptr || cents->codes == nullptr || cents->scale == nullptr || cents->lo == nullptr)
+        return fail(ABS_ERR_INVALID_ARG, "null centroid store");
+    if (q == nullptr || sel == nullptr || sel_count == nullptr)
+        return fail(ABS_ERR_INVALID_ARG, "null q, sel or sel_count");
+    if (sel_cap < p.sel_cap) return fail(ABS_ERR_INVALID_ARG, "sel_cap %d < required %d", sel_cap, p.sel_cap);
+    if (p.max_n > absk::kTopkThreads * absk::kTopkMaxPerThread)
+        return fail(ABS_ERR_UNSUPPORTED, "%d blocks in one head (max %d)", p.max_n,
+                    absk::kTopkThreads * absk::kTopkMaxPerThread);
+    const size_t need = select_bytes(p);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(ABS_ERR_WORKSPACE, "select needs %zu workspace bytes, got %zu", need, workspace_bytes);
+    absk::SelectArgs a;
+    a.codes = cents->codes;
+    a.scale = cents->scale;
+    a.lo = cents->lo;
+    a.q = q;
+    a.scores = reinterpret_cast<float*>(workspace);
+    a.sel = sel;
+    a.count = sel_count;
+    a.sel_cap = sel_cap;
+    a.budget = token_budget;
+    a.max_n = p.max_n;
+    return hip_status(absk::launch_select(p.g, p.dt, a, static_cast<hipStream_t>(stream)), "score_select");
+}
+
+abs_status abs_sparse_decode(const abs_paged_kv* kv, const abs_block_map* map, const void* q, const int32_t* sel,
+                             int32_t sel_cap, const int32_t* sel_count, int32_t token_budget, float sm_scale,
+                             void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+    Plan p;
+    if (abs_status st = check_geometry(kv, map, &p)) return st;
+    if (abs_status st = require_device(p, true)) return st;
+    if (abs_status st = plan_budget(kv, map, token_budget, &p)) return st;
+    if (q == nullptr || sel == nullptr || sel_count == nullptr || out == nullptr)
+        return fail(ABS_ERR_INVALID_ARG, "null q, sel, sel_count or out");
+    if (sel_cap < p.sel_cap) return fail(ABS_ERR_INVALID_ARG, "sel_cap %d < required %d", sel_cap, p.sel_cap);
+    if (!std::isfinite(sm_scale)) return fail(ABS_ERR_INVALID_ARG, "sm_scale is not finite");
+    const DecodeLayout l = decode_layout(p);
+    if (workspace == nullptr || workspace_bytes < l.bytes)
+        return fail(ABS_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", l.bytes, workspace_bytes);
+    absk::DecodeArgs a;
+    a.q = q;
+    a.sel = sel;
+    a.count = sel_count;
+    a.sel_cap = sel_cap;
+    a.sm_scale = sm_scale;
+    a.out = out;
+    a.lse = lse;
+    a.part_ml = reinterpret_cast<float*>(ws_at(workspace, l.ml));
+    a.part_o = reinterpret_cast<float*>(ws_at(workspace, l.o));
+    a.pages_per_wg = l.ppw;
+    a.splits = l.splits;
+    return hip_status(absk::launch_decode(p.g, p.dt, a, static_cast<hipStream_t>(stream)), "sparse_decode");
+}
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+// Device-side helpers shared by the gfx950 kernels of the AB-Sparse library:
+// element conversion, wide loads, and reductions across the 16 lanes of a
+// DPP row (a row of 16 lanes holds one cache row: 16 lanes x head_dim/16
+// channels).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.hpp"
+
+namespace absk {
+
+constexpr int kPage = 16;       // tokens per physical page
+constexpr int kRowLanes = 16;   // lanes that share one cache row
+
+// ---- element conversion ---------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// A run of NW 32-bit words loaded with the widest aligned loads available.
+template <int NW>
+struct Words {
+    uint32_t w[NW];
+};
+
+template <int NW>
+__device__ __forceinline__ Words<NW> load_words(const void* p) {
+    Words<NW> r;
+    if constexpr (NW % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < NW / 4; ++i) {
+            uint4 v = reinterpret_cast<const uint4*>(p)[i];
+            r.w[4 * i + 0] = v.x;
+            r.w[4 * i + 1] = v.y;
+            r.w[4 * i + 2] = v.z;
+            r.w[4 * i + 3] = v.w;
+        }
+    } else if constexpr (NW == 2) {
+        uint2 v = *reinterpret_cast<const uint2*>(p);
+        r.w[0] = v.x;
+        r.w[1] = v.y;
+    } else {
+        static_assert(NW == 1, "unsupported width");
+        r.w[0] = *reinterpret_cast<const uint32_t*>(p);
+    }
+    return r;
+}
+
+template <int NW>
+__device__ __forceinline__ Words<NW> zero_words() {
+    Words<NW> r;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) r.w[i] = 0u;
+    return r;
+}
+
+// Storage traits: element e of a Words run as fp32.
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<float> {
+    static constexpr int kBytes = 4;
+    template <int NW>
+    __device__ static __forceinline__ float get(const Words<NW>& w, int e) { return __uint_as_float(w.w[e]); }
+    __device__ static __forceinline__ float load1(const float* p) { return *p; }
+    __device__ static __forceinline__ void store1(float* p, float v) { *p = v; }
+};
+
+template <>
+struct Elem<uint16_t> {  // bf16 bit patterns
+    static constexpr int kBytes = 2;
+    template <int NW>
+    __device__ static __forceinline__ float get(const Words<NW>& w, int e) {
+        return (e & 1) ? bf16_hi(w.w[e >> 1]) : bf16_lo(w.w[e >> 1]);
+    }
+    __device__ static __forceinline__ float load1(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
+    __device__ static __forceinline__ void store1(uint16_t* p, float v) { *p = (uint16_t)f32_to_bf16(v); }
+};
+
+// ---- cross-lane reductions --------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the 16 lanes of each DPP row; every lane of the row gets the sum.
+// quad_perm(1,0,3,2), quad_perm(2,3,0,1), row_half_mirror, row_mirror.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp<0xB1>(v);
+    v += dpp<0x4E>(v);
+    v += dpp<0x141>(v);
+    v += dpp<0x140>(v);
+    return v;
+}
+
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    v = fmaxf(v, dpp<0x140>(v));
+    return v;
+}
+
+// Combine the four rows of a wavefront (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float rows4_sum(float v) {
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+__device__ __forceinline__ float rows4_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+__device__ __forceinline__ float rows4_min(float v) {
+    v = fminf(v, __shfl_xor(v, 16));
+    v = fminf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+__host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace absk

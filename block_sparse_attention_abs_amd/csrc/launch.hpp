@@ -1,0 +1,79 @@
+// Internal interface between the C-ABI layer (abs_api.cpp) and the kernel
+// launchers (*.hip).  Everything here has already been validated by the
+// caller; launchers only size grids and enqueue kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace absk {
+
+// Geometry of one layer's paged cache and block map, passed by value to kernels.
+struct Geom {
+    int B, Hq, Hkv, D, G, max_pages;
+    int64_t num_pages;
+    const void* k;
+    const void* v;
+    const int32_t* page_table;
+    const int32_t* seq_lens;
+    const int32_t* block_size;
+    const int64_t* off;
+};
+
+enum class DType { F32 = 0, BF16 = 1 };
+
+// Centroid build: blocks per workgroup tile, and the tile count the host
+// derives from the largest N_{b,h}.
+constexpr int kBuildTile = 64;
+
+struct BuildArgs {
+    uint8_t* codes;
+    float* scale;
+    float* lo;
+    float* staging;   // [total_blocks][D] fp32 centroids
+    float* pmin;      // [B*Hkv][tiles][D]
+    float* pmax;      // [B*Hkv][tiles][D]
+    int tiles;        // ceil(max N / kBuildTile)
+};
+
+hipError_t launch_build(const Geom& g, DType dt, const BuildArgs& a, hipStream_t s);
+
+// Score + select.
+constexpr int kScoreTile = 64;          // blocks per score workgroup (D = 128)
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkMaxPerThread = 64;   // N_{b,h} <= 65536
+
+struct SelectArgs {
+    const uint8_t* codes;
+    const float* scale;
+    const float* lo;
+    const void* q;
+    float* scores;    // [total_blocks]
+    int32_t* sel;
+    int32_t* count;
+    int sel_cap;
+    int budget;
+    int max_n;        // largest N_{b,h}
+};
+
+hipError_t launch_select(const Geom& g, DType dt, const SelectArgs& a, hipStream_t s);
+
+// Split-K sparse decode + merge.
+struct DecodeArgs {
+    const void* q;
+    const int32_t* sel;
+    const int32_t* count;
+    int sel_cap;
+    float sm_scale;
+    void* out;
+    float* lse;       // may be null
+    float* part_ml;   // [B*Hq][splits][2]
+    float* part_o;    // [B*Hq][splits][D]
+    int pages_per_wg;
+    int splits;
+};
+
+hipError_t launch_decode(const Geom& g, DType dt, const DecodeArgs& a, hipStream_t s);
+
+}  // namespace absk

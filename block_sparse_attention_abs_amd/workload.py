@@ -8,10 +8,10 @@ random data (outlier channels, planted needle keys, the bf16 cast).
 
 Shapes follow the 8B-class models the AB-Sparse page evaluates on (32 query
 heads, 8 KV heads, head dim 128), the page's observation that centroid
-channels carry outliers (the channel-distribution residue next to Figure 6 of
-the AB-Sparse page), and the page's 16-token physical pages grouped into
-16/32/64-token logical blocks (Figure 8's mapping residue and Figure 4's
-block-size heatmap).  Every random stream is a PCG64 generator seeded with
+channels carry outliers (the channel-distribution figure printed after
+Figure 6 of the AB-Sparse page), and the page's 16-token physical pages
+grouped into 16/32/64-token logical blocks (the mapping figure after Figure 8
+and the per-head block-size heatmap after Figure 3).  Every random stream is a PCG64 generator seeded with
 ``SeedSequence([cfg_id, layer, b, kv_head, stream])`` so that a single
 (sequence, head) can be regenerated on its own.
 
@@ -21,6 +21,8 @@ patterns in ``np.uint16`` (numpy has no bfloat16), rounded to nearest-even.
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 from typing import Optional, Sequence
 
@@ -192,20 +194,29 @@ def make_layer(w: Workload, layer: int = 0, *, seq_lens: Optional[Sequence[int]]
     nmax = min(w.needles_per_head, int(lens.max())) if needles else 0
     needle_pos = np.full((B, Hkv, nmax), -1, dtype=np.int64)
     wn = w if needles else dataclasses.replace(w, needles_per_head=0)
-    for b in range(B):
+
+    def fill(b, h):   # every (b, h) writes disjoint cache slices
         L, P = int(lens[b]), int(npages[b])
         phys = page_table[b, :P]
-        for h in range(Hkv):
-            qbar = qf[b, h * G:(h + 1) * G].sum(axis=0)
-            k, pos = _head_keys(wn, layer, b, h, L, D, qbar)
-            needle_pos[b, h, :len(pos)] = pos
-            v = _rng(w, layer, b, h, S_V).standard_normal((L, D), dtype=np.float32)
-            kp = np.full((P * PAGE_SIZE, D), PAD_SENTINEL, dtype=np.float32)
-            vp = np.full((P * PAGE_SIZE, D), PAD_SENTINEL, dtype=np.float32)
-            kp[:L] = k
-            vp[:L] = v
-            k_cache[phys, h] = to_storage(kp, w.dtype).reshape(P, PAGE_SIZE, D)
-            v_cache[phys, h] = to_storage(vp, w.dtype).reshape(P, PAGE_SIZE, D)
+        qbar = qf[b, h * G:(h + 1) * G].sum(axis=0)
+        k, pos = _head_keys(wn, layer, b, h, L, D, qbar)
+        needle_pos[b, h, :len(pos)] = pos
+        v = _rng(w, layer, b, h, S_V).standard_normal((L, D), dtype=np.float32)
+        kp = np.full((P * PAGE_SIZE, D), PAD_SENTINEL, dtype=np.float32)
+        vp = np.full((P * PAGE_SIZE, D), PAD_SENTINEL, dtype=np.float32)
+        kp[:L] = k
+        vp[:L] = v
+        k_cache[phys, h] = to_storage(kp, w.dtype).reshape(P, PAGE_SIZE, D)
+        v_cache[phys, h] = to_storage(vp, w.dtype).reshape(P, PAGE_SIZE, D)
+
+    pairs = [(b, h) for b in range(B) for h in range(Hkv)]
+    if B * Hkv * int(lens.max()) * D < (1 << 22):
+        for bh in pairs:
+            fill(*bh)
+    else:
+        workers = max(1, min(8, os.cpu_count() or 1))
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(lambda bh: fill(*bh), pairs))
     return LayerInputs(w, layer, q, k_cache, v_cache, page_table, lens, bsz, needle_pos, w.dtype)
 
 

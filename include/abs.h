@@ -1,0 +1,196 @@
+/*
+ * abs.h -- C ABI of the AB-Sparse decode library for AMD Instinct MI355X (gfx950).
+ *
+ * AB-Sparse ("AB-Sparse: Sparse Attention with Adaptive Block Size for
+ * Accurate and Efficient Long-Context Inference", arXiv 2605.12110, Pith
+ * review page) is block-sparse decode attention in which every KV head has
+ * its own block size.  Figure 1 of the page fixes the pipeline: one
+ * representative vector (centroid) per block, a dot-product estimate of each
+ * block's importance against the query, top-K selection, and exact attention
+ * over the selected blocks only.  Figure 8 and the mapping figure after it
+ * fix the storage: centroids quantized to INT4 (asymmetric, per channel) and
+ * 16-token physical pages grouped into per-head logical blocks of
+ * stride = pages per block, each head reading the same number of pages.
+ * Figure 5's text fixes that block sizes are static per head (changing one
+ * means rebuilding its centroids).
+ *
+ * Conventions for every call:
+ *   - All pointers marked "device" are HIP device memory; "host" pointers are
+ *     read on the host during the call only.  The caller owns every buffer;
+ *     the library never allocates, frees or synchronizes.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     default stream).  Outputs are valid once that stream reaches the point
+ *     after the call.
+ *   - Host-side arguments are validated before anything is enqueued; on any
+ *     status other than ABS_OK nothing is enqueued and no output is written,
+ *     except ABS_ERR_HIP, which reports a failed launch (outputs undefined).
+ *   - Device contents are trusted: page ids, selections and counts must obey
+ *     the layouts below.  Kernels clamp or skip out-of-range ids rather than
+ *     fault, but results are then undefined.
+ *   - Calls are thread-safe; calls that share a workspace or output buffer
+ *     must be ordered by the caller (same stream, or events).
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef ABS_H
+#define ABS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum abs_status {
+    ABS_OK = 0,
+    ABS_ERR_INVALID_ARG = 1,  /* null pointer, bad dimension, too-small capacity */
+    ABS_ERR_UNSUPPORTED = 2,  /* valid but not built: head_dim, page size, block size, group size, N */
+    ABS_ERR_WORKSPACE = 3,    /* workspace smaller than abs_workspace_bytes() */
+    ABS_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} abs_status;
+
+typedef enum abs_dtype {
+    ABS_F32 = 0,   /* IEEE binary32 */
+    ABS_BF16 = 1   /* bfloat16 (upper half of binary32) */
+} abs_dtype;
+
+typedef enum abs_op {
+    ABS_OP_BUILD = 0,    /* abs_build_centroids */
+    ABS_OP_SELECT = 1,   /* abs_score_select */
+    ABS_OP_DECODE = 2    /* abs_sparse_decode */
+} abs_op;
+
+/*
+ * Paged KV cache of one layer (the paged layout of the mapping figure after
+ * Figure 8; PagedAttention in the page's references).
+ *   k_cache, v_cache: device, [num_pages][num_kv_heads][page_size][head_dim]
+ *       in kv_dtype: each (page, KV head) is one contiguous page_size x
+ *       head_dim tile.
+ *   page_table: device, int32 [num_seqs][max_pages_per_seq]; token t of
+ *       sequence b lives in physical page page_table[b][t / 16], slot t % 16.
+ *       Entries past a sequence's ceil(L_b / 16) pages are never read.
+ *   seq_lens: device, int32 [num_seqs], L_b = cached tokens of sequence b,
+ *       the current decode token included.  seq_lens_host: the same values on
+ *       the host (launch sizes are computed from it; it must equal seq_lens).
+ * Supported: page_size 16, head_dim 64 or 128, num_q_heads / num_kv_heads in
+ * 1..8, 1 <= L_b <= max_pages_per_seq * 16.
+ */
+typedef struct abs_paged_kv {
+    int32_t num_seqs;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t page_size;
+    int32_t max_pages_per_seq;
+    int64_t num_pages;
+    int32_t kv_dtype;            /* abs_dtype */
+    int32_t reserved0;           /* must be 0 */
+    const void *k_cache;
+    const void *v_cache;
+    const int32_t *page_table;
+    const int32_t *seq_lens;
+    const int32_t *seq_lens_host;
+} abs_paged_kv;
+
+/*
+ * Block-size map of one layer (the per-head block-size heatmap printed after
+ * Figure 3; static per Figure 5's text).
+ *   block_size_host / block_size: host / device int32 [num_kv_heads], each in
+ *       {16, 32, 64}; bs_h / 16 is the head's page stride.
+ *   centroid_off: device int64 [num_seqs * num_kv_heads + 1]; the first
+ *       centroid row of (b, h) is centroid_off[b * num_kv_heads + h], with
+ *       N_{b,h} = ceil(L_b / bs_h) rows.  Fill it with abs_centroid_offsets().
+ */
+typedef struct abs_block_map {
+    const int32_t *block_size_host;
+    const int32_t *block_size;
+    const int64_t *centroid_off;
+} abs_block_map;
+
+/*
+ * INT4 centroid store (Figure 8: asymmetric, per channel).
+ *   codes: device uint8 [total_blocks][head_dim / 2]; channel 2i in the low
+ *       nibble of byte i, channel 2i+1 in the high nibble.
+ *   scale, lo: device f32 [num_seqs][num_kv_heads][head_dim]; the
+ *       dequantized centroid is code * scale + lo.
+ */
+typedef struct abs_centroids {
+    uint8_t *codes;
+    float *scale;
+    float *lo;
+} abs_centroids;
+
+/* Static text for a status code. */
+const char *abs_status_str(abs_status s);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char *abs_last_error(void);
+
+/* Sum over (b, h) of N_{b,h} = ceil(L_b / bs_h), the number of centroid rows. */
+abs_status abs_total_blocks(const abs_paged_kv *kv, const abs_block_map *map, int64_t *total);
+
+/* Host: fill off_host[num_seqs * num_kv_heads + 1] with the running sum of
+ * N_{b,h}, b-major then h (only map->block_size_host is read). */
+abs_status abs_centroid_offsets(const abs_paged_kv *kv, const abs_block_map *map, int64_t *off_host);
+
+/* Largest K_{b,h} = min(N_{b,h}, max(1, floor(token_budget / bs_h))) over all
+ * (b, h): the smallest row length (sel_cap) a selection buffer may have. */
+abs_status abs_select_capacity(const abs_paged_kv *kv, const abs_block_map *map,
+                               int32_t token_budget, int32_t *sel_cap);
+
+/* Workspace bytes that `op` needs for these descriptors and budget (the
+ * budget is ignored for ABS_OP_BUILD). */
+abs_status abs_workspace_bytes(const abs_paged_kv *kv, const abs_block_map *map,
+                               int32_t token_budget, abs_op op, size_t *bytes);
+
+/*
+ * Centroid build + INT4 quantization, for every (b, h) of the layer.
+ * Centroid of block j of (b, h) = mean of the keys of its valid tokens
+ * [j*bs_h, min((j+1)*bs_h, L_b)) (Figure 1's block representation; mean key).
+ * Per (b, h, channel d): lo = min_j c_j[d], scale = (max_j c_j[d] - lo) / 15
+ * (fp32), code = clamp(rint((c - lo) / scale), 0, 15) in fp32, 0 if scale == 0.
+ * Writes out->codes (all total_blocks rows), out->scale, out->lo.
+ */
+abs_status abs_build_centroids(const abs_paged_kv *kv, const abs_block_map *map,
+                               const abs_centroids *out, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/*
+ * Dot-product estimation + top-K (Figure 1; the "Estimation" and "Top-K"
+ * stages of the per-stage latency figure after Figure 13).  For each (b, h): qbar = sum of the query heads
+ * h*G .. h*G+G-1 (G = num_q_heads / num_kv_heads), score_j = qbar . (code_j *
+ * scale + lo); keep the K_{b,h} best blocks ranked by (score desc, index asc).
+ *   q: device [num_seqs][num_q_heads][head_dim] in kv_dtype.
+ *   sel: device int32 [num_seqs][num_kv_heads][sel_cap]; row (b, h) gets its
+ *       K_{b,h} block indices in ascending order; slots past K are not written.
+ *   sel_count: device int32 [num_seqs][num_kv_heads], receives K_{b,h}.
+ *   sel_cap >= abs_select_capacity(); N_{b,h} <= 65536 is supported.
+ */
+abs_status abs_score_select(const abs_paged_kv *kv, const abs_block_map *map,
+                            const abs_centroids *cents, const void *q, int32_t token_budget,
+                            int32_t *sel, int32_t sel_cap, int32_t *sel_count,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Exact attention over the selected blocks only (Figure 1's sparse attention;
+ * the "Attention" stage of the figure after Figure 13), split over pages with an fp32 online
+ * softmax and a log-sum-exp merge (FlashAttention, in the page's references).
+ * For query head i of KV head h = i / G: the kept tokens are the union of
+ * [j*bs_h, min((j+1)*bs_h, L_b)) over the first sel_count[b][h] entries j of
+ * sel row (b, h); z_t = sm_scale * q_i . k_t;
+ * out_i = sum_t softmax(z)_t v_t; lse_i = ln sum_t exp(z_t).
+ *   token_budget: the budget the selection was made with (sizes the launch;
+ *       sel_count[b][h] must not exceed K_{b,h} for it).
+ *   out: device [num_seqs][num_q_heads][head_dim] in kv_dtype.
+ *   lse: device f32 [num_seqs][num_q_heads], natural log; may be NULL.
+ */
+abs_status abs_sparse_decode(const abs_paged_kv *kv, const abs_block_map *map, const void *q,
+                             const int32_t *sel, int32_t sel_cap, const int32_t *sel_count,
+                             int32_t token_budget, float sm_scale, void *out, float *lse,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ABS_H */

@@ -1,0 +1,172 @@
+"""The C ABI without a GPU: libabs.so loads, exports every call include/abs.h
+declares, the Python structures match the C layouts, the host-side geometry
+helpers agree with the oracle's block counts, and invalid descriptors are
+rejected with the documented status before anything is enqueued."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from block_sparse_attention_abs_amd import abs as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "abs.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(A.LIB_PATH), reason="libabs.so not built")
+
+
+def header_functions():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(abs_\w+)\s*\(", txt, re.M)))
+
+
+def test_exports_every_declared_call():
+    names = header_functions()
+    assert len(names) == 9
+    assert sorted(A.EXPORTS) == names
+    L = A.lib()
+    for n in names:
+        assert getattr(L, n) is not None
+    out = subprocess.run(["nm", "-D", "--defined-only", A.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = set(re.findall(r" T (abs_\w+)", out.stdout))
+    assert set(names) <= exported
+
+
+def test_struct_layout_matches_c(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text("""
+#include <stdio.h>
+#include <stddef.h>
+#include "abs.h"
+#define F(s, f) printf(#s "." #f " %zu\\n", offsetof(s, f))
+int main(void) {
+  printf("abs_paged_kv %zu\\nabs_block_map %zu\\nabs_centroids %zu\\n",
+         sizeof(abs_paged_kv), sizeof(abs_block_map), sizeof(abs_centroids));
+  F(abs_paged_kv, num_pages); F(abs_paged_kv, kv_dtype); F(abs_paged_kv, k_cache);
+  F(abs_paged_kv, seq_lens_host); F(abs_block_map, centroid_off); F(abs_centroids, lo);
+  return 0;
+}""")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True).stdout.splitlines())
+    assert int(got["abs_paged_kv"]) == C.sizeof(A.abs_paged_kv)
+    assert int(got["abs_block_map"]) == C.sizeof(A.abs_block_map)
+    assert int(got["abs_centroids"]) == C.sizeof(A.abs_centroids)
+    for key, (st, f) in {"abs_paged_kv.num_pages": (A.abs_paged_kv, "num_pages"),
+                         "abs_paged_kv.kv_dtype": (A.abs_paged_kv, "kv_dtype"),
+                         "abs_paged_kv.k_cache": (A.abs_paged_kv, "k_cache"),
+                         "abs_paged_kv.seq_lens_host": (A.abs_paged_kv, "seq_lens_host"),
+                         "abs_block_map.centroid_off": (A.abs_block_map, "centroid_off"),
+                         "abs_centroids.lo": (A.abs_centroids, "lo")}.items():
+        assert int(got[key]) == getattr(st, f).offset
+
+
+FAKE = 1 << 40  # stands in for a device address; never dereferenced on these paths
+
+
+class Host:
+    """Descriptors with host metadata and placeholder device pointers."""
+
+    def __init__(self, seq_lens=(300, 77), block_size=(16, 64), Hq=4, D=64, dtype=A.ABS_BF16, max_pages=32):
+        self.sl = np.asarray(seq_lens, dtype=np.int32)
+        self.bs = np.asarray(block_size, dtype=np.int32)
+        self.kv = A.abs_paged_kv(num_seqs=len(self.sl), num_q_heads=Hq, num_kv_heads=len(self.bs), head_dim=D,
+                                 page_size=16, max_pages_per_seq=max_pages, num_pages=64, kv_dtype=dtype,
+                                 reserved0=0, k_cache=FAKE, v_cache=FAKE, page_table=FAKE, seq_lens=FAKE,
+                                 seq_lens_host=self.sl.ctypes.data)
+        self.bmap = A.abs_block_map(block_size_host=self.bs.ctypes.data, block_size=FAKE, centroid_off=FAKE)
+        self.cents = A.abs_centroids(codes=FAKE, scale=FAKE, lo=FAKE)
+
+
+def test_geometry_helpers_agree_with_oracle(oracle_mod):
+    h = Host(seq_lens=(300, 77, 1), block_size=(16, 64, 32), Hq=6)
+    assert A.abs_total_blocks(h.kv, h.bmap) == oracle_mod.total_blocks(h.sl, h.bs)
+    off = A.abs_centroid_offsets(h.kv, h.bmap)
+    rows = oracle_mod.block_rows(h.sl, h.bs)
+    assert off[:-1].tolist() == [r[2] for r in rows] and off[-1] == oracle_mod.total_blocks(h.sl, h.bs)
+    for budget in (1, 17, 64, 100, 4096):
+        assert A.abs_select_capacity(h.kv, h.bmap, budget) == oracle_mod.sel_capacity(h.sl, h.bs, budget)
+    for op in (A.ABS_OP_BUILD, A.ABS_OP_SELECT, A.ABS_OP_DECODE):
+        assert A.abs_workspace_bytes(h.kv, h.bmap, 64, op) > 0
+
+
+def status_of(fn):
+    try:
+        fn()
+    except A.AbsError as e:
+        assert A.abs_last_error()
+        return e.status
+    return A.ABS_OK
+
+
+@pytest.mark.parametrize("field,value,want", [
+    ("num_seqs", 0, A.ABS_ERR_INVALID_ARG),
+    ("num_q_heads", 3, A.ABS_ERR_INVALID_ARG),
+    ("num_q_heads", 36, A.ABS_ERR_UNSUPPORTED),
+    ("head_dim", 96, A.ABS_ERR_UNSUPPORTED),
+    ("page_size", 32, A.ABS_ERR_UNSUPPORTED),
+    ("kv_dtype", 7, A.ABS_ERR_UNSUPPORTED),
+    ("reserved0", 1, A.ABS_ERR_INVALID_ARG),
+    ("max_pages_per_seq", 0, A.ABS_ERR_INVALID_ARG),
+    ("max_pages_per_seq", 4, A.ABS_ERR_INVALID_ARG),      # 300 tokens do not fit in 4 pages
+    ("seq_lens_host", None, A.ABS_ERR_INVALID_ARG),
+])
+def test_descriptor_validation(field, value, want):
+    h = Host()
+    setattr(h.kv, field, value)
+    assert status_of(lambda: A.abs_total_blocks(h.kv, h.bmap)) == want
+    assert status_of(lambda: A.abs_build_centroids(h.kv, h.bmap, h.cents, FAKE, 1 << 30, 0)) == want
+
+
+@pytest.mark.parametrize("sizes,lens,want", [
+    ((16, 48), (300, 77), A.ABS_ERR_UNSUPPORTED),
+    ((16, 0), (300, 77), A.ABS_ERR_INVALID_ARG),
+    ((16, 1), (300, 77), A.ABS_ERR_UNSUPPORTED),           # block size 1 exists in the oracle only
+    ((16, 64), (0, 77), A.ABS_ERR_INVALID_ARG),
+])
+def test_block_map_and_length_validation(sizes, lens, want):
+    h = Host(seq_lens=lens, block_size=sizes)
+    assert status_of(lambda: A.abs_total_blocks(h.kv, h.bmap)) == want
+
+
+def test_call_level_validation():
+    h = Host()
+    need_b = A.abs_workspace_bytes(h.kv, h.bmap, 64, A.ABS_OP_BUILD)
+    need_s = A.abs_workspace_bytes(h.kv, h.bmap, 64, A.ABS_OP_SELECT)
+    need_d = A.abs_workspace_bytes(h.kv, h.bmap, 64, A.ABS_OP_DECODE)
+    cap = A.abs_select_capacity(h.kv, h.bmap, 64)
+    W = A.ABS_ERR_WORKSPACE
+    assert status_of(lambda: A.abs_build_centroids(h.kv, h.bmap, h.cents, FAKE, need_b - 1, 0)) == W
+    assert status_of(lambda: A.abs_score_select(h.kv, h.bmap, h.cents, FAKE, 64, FAKE, cap, FAKE, FAKE,
+                                                need_s - 1, 0)) == W
+    assert status_of(lambda: A.abs_sparse_decode(h.kv, h.bmap, FAKE, FAKE, cap, FAKE, 64, 0.125, FAKE, None,
+                                                 FAKE, need_d - 1, 0)) == W
+    I = A.ABS_ERR_INVALID_ARG
+    assert status_of(lambda: A.abs_score_select(h.kv, h.bmap, h.cents, FAKE, 64, FAKE, cap - 1, FAKE, FAKE,
+                                                need_s, 0)) == I
+    assert status_of(lambda: A.abs_score_select(h.kv, h.bmap, h.cents, FAKE, 0, FAKE, cap, FAKE, FAKE,
+                                                need_s, 0)) == I
+    assert status_of(lambda: A.abs_score_select(h.kv, h.bmap, h.cents, None, 64, FAKE, cap, FAKE, FAKE,
+                                                need_s, 0)) == I
+    assert status_of(lambda: A.abs_sparse_decode(h.kv, h.bmap, FAKE, FAKE, cap, FAKE, 64, float("nan"), FAKE,
+                                                 None, FAKE, need_d, 0)) == I
+    h.kv.v_cache = None
+    assert status_of(lambda: A.abs_sparse_decode(h.kv, h.bmap, FAKE, FAKE, cap, FAKE, 64, 0.125, FAKE, None,
+                                                 FAKE, need_d, 0)) == I
+
+
+def test_too_many_blocks_per_head_is_unsupported():
+    h = Host(seq_lens=(65537 * 16,), block_size=(16,), Hq=1, max_pages=65537)
+    cap = A.abs_select_capacity(h.kv, h.bmap, 64)
+    need = A.abs_workspace_bytes(h.kv, h.bmap, 64, A.ABS_OP_SELECT)
+    assert status_of(lambda: A.abs_score_select(h.kv, h.bmap, h.cents, FAKE, 64, FAKE, cap, FAKE, FAKE, need,
+                                                0)) == A.ABS_ERR_UNSUPPORTED
+
+
+def test_status_strings():
+    assert A.abs_status_str(A.ABS_OK) == "ok"
+    assert A.abs_status_str(A.ABS_ERR_WORKSPACE) == "workspace too small"
+    assert A.abs_status_str(99) == "unknown status"

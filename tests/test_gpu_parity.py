@@ -1,0 +1,183 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on the GPU.
+
+Stage-isolated checks feed each stage's oracle the GPU's own upstream
+results (GPU codes into the oracle's scoring, GPU selection into the
+oracle's attention), so each kernel is judged on the same inputs; the
+end-to-end check runs the oracle from the raw inputs.  Rules and tolerances
+are in gpu_pipeline.py.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_abs_amd import workload as W
+from gpu_pipeline import GpuLayer, check_attention, check_selection, default_scale, oracle_quant_from_gpu
+
+pytestmark = pytest.mark.gpu
+
+P = W.PRESETS
+
+
+def _case(name):
+    if name == "tiny":
+        return W.make_layer(P[0])
+    if name == "tiny-ragged":
+        return W.make_layer(P[0].scaled(batch=3), seq_lens=[2048, 1001, 17])
+    if name == "llama-4k-ragged":
+        return W.make_layer(P[1].scaled(batch=2, context=4096, token_budget=512), seq_lens=[4096, 3001])
+    if name == "llama-16k-b2":
+        return W.make_layer(P[2].scaled(batch=2, context=16384))
+    if name == "mha-d128-f32":
+        return W.make_layer(P[1].scaled(num_q_heads=8, num_kv_heads=8, dtype="f32", context=1500, token_budget=256))
+    if name == "gqa8-d64-bf16":
+        return W.make_layer(P[1].scaled(num_q_heads=16, num_kv_heads=2, head_dim=64, context=3000,
+                                        token_budget=512, batch=2), seq_lens=[3000, 2222])
+    raise KeyError(name)
+
+
+CASES = ["tiny", "tiny-ragged", "llama-4k-ragged", "llama-16k-b2", "mha-d128-f32", "gqa8-d64-bf16"]
+
+
+@pytest.fixture(scope="module")
+def runs(oracle_mod):
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            x = _case(name)
+            print(f"[gpu parity] case {name}: B={x.q.shape[0]} Hq={x.q.shape[1]} Hkv={x.k_cache.shape[1]} "
+                  f"D={x.q.shape[2]} lens={x.seq_lens.tolist()} bs={x.block_size.tolist()} {x.dtype}", flush=True)
+            g = GpuLayer(x)
+            sm = default_scale(x.q.shape[2])
+            res = g.run(x.workload.token_budget, sm)
+            cache[name] = (x, g, res, sm)
+        return cache[name]
+
+    return get
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_build_is_bit_exact(runs, oracle_mod, case):
+    x, _, r, _ = runs(case)
+    c = oracle_mod.centroids(x.k_cache, x.page_table, x.seq_lens, x.block_size, x.dtype)
+    qz = oracle_mod.quantize(c, x.seq_lens, x.block_size)
+    np.testing.assert_array_equal(r.scale, qz.scale)
+    np.testing.assert_array_equal(r.lo, qz.lo)
+    np.testing.assert_array_equal(r.codes, qz.codes)
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_select_stage(runs, oracle_mod, case):
+    x, _, r, _ = runs(case)
+    qz = oracle_quant_from_gpu(oracle_mod, r)
+    s = oracle_mod.scores(x.q, qz, x.seq_lens, x.block_size, x.dtype)
+    check_selection(oracle_mod, x, qz, s, r.sel, r.count, x.workload.token_budget)
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_decode_stage(runs, oracle_mod, case):
+    x, _, r, sm = runs(case)
+    out, lse = oracle_mod.attend(x.q, x.k_cache, x.v_cache, x.page_table, x.seq_lens, x.block_size, r.sel, r.count,
+                                 sm, x.dtype)
+    check_attention(r.out, r.lse, out, lse, x.dtype)
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_end_to_end(runs, oracle_mod, case):
+    x, _, r, sm = runs(case)
+    ref = oracle_mod.run(x, sm_scale=sm)
+    check_selection(oracle_mod, x, ref.quant, ref.scores, r.sel, r.count, x.workload.token_budget)
+    if np.array_equal(ref.count, r.count) and all(
+            np.array_equal(ref.sel[b, h, :k], r.sel[b, h, :k]) for (b, h), k in np.ndenumerate(ref.count)):
+        check_attention(r.out, r.lse, ref.out, ref.lse, x.dtype)
+
+
+def _run_and_compare(oracle_mod, x, budget, sm=None):
+    sm = default_scale(x.q.shape[2]) if sm is None else sm
+    r = GpuLayer(x).run(budget, sm)
+    ref = oracle_mod.run(x, sm_scale=sm, budget=budget)
+    np.testing.assert_array_equal(r.codes, ref.quant.codes)
+    check_selection(oracle_mod, x, ref.quant, ref.scores, r.sel, r.count, budget)
+    out, lse = oracle_mod.attend(x.q, x.k_cache, x.v_cache, x.page_table, x.seq_lens, x.block_size, r.sel, r.count,
+                                 sm, x.dtype)
+    check_attention(r.out, r.lse, out, lse, x.dtype)
+    return r, ref
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_budget_covering_context_is_dense_attention(oracle_mod, dtype):
+    x = W.make_layer(P[1].scaled(batch=2, context=1000, dtype=dtype), seq_lens=[1000, 333])
+    r, ref = _run_and_compare(oracle_mod, x, budget=1 << 20)
+    n = [[(int(L) + int(bs) - 1) // int(bs) for bs in x.block_size] for L in x.seq_lens]
+    assert r.count.tolist() == n
+    check_attention(r.out, r.lse, ref.out, ref.lse, dtype)
+
+
+def test_tiny_lengths_partial_pages_and_blocks(oracle_mod):
+    lens = [1, 15, 16, 17, 33, 63, 64, 65, 100]
+    x = W.make_layer(P[1].scaled(batch=len(lens), context=100, needles_per_head=2), seq_lens=lens)
+    _run_and_compare(oracle_mod, x, budget=64)
+
+
+def test_budget_below_block_size_keeps_one_block(oracle_mod):
+    x = W.make_layer(P[1].scaled(batch=2, context=2048, needles_per_head=4))
+    r, _ = _run_and_compare(oracle_mod, x, budget=8)
+    assert (r.count == 1).all()
+
+
+def test_equal_scores_take_lowest_indices(oracle_mod):
+    x = W.make_layer(P[1].scaled(batch=2, context=1000, dtype="f32"), seq_lens=[1000, 640], needles=False)
+    x.k_cache[:] = np.float32(0.5)
+    r, ref = _run_and_compare(oracle_mod, x, budget=128)
+    assert (r.codes == 0).all() and (r.scale == 0).all()
+    for (b, h), k in np.ndenumerate(r.count):
+        assert r.sel[b, h, :k].tolist() == list(range(k))
+
+
+def test_page_table_invariance_and_determinism():
+    w = P[1].scaled(batch=3, context=3000, needles_per_head=4)
+    a = W.make_layer(w, seq_lens=[3000, 1234, 77], shuffle_pages=True, extra_pages=5)
+    b = W.make_layer(w, seq_lens=[3000, 1234, 77], shuffle_pages=False, extra_pages=5)
+    sm = default_scale(128)
+    ga = GpuLayer(a)
+    ra = ga.run(2048, sm)
+    ra2 = ga.run(2048, sm)
+    rb = GpuLayer(b).run(2048, sm)
+    for f in ("codes", "scale", "lo", "sel", "count", "out", "lse"):
+        np.testing.assert_array_equal(getattr(ra, f), getattr(ra2, f))
+        np.testing.assert_array_equal(getattr(ra, f), getattr(rb, f))
+
+
+def test_largest_head_65536_blocks(oracle_mod):
+    """The largest supported block count per head (1M tokens at block size 16)."""
+    w = P[1].scaled(num_q_heads=4, num_kv_heads=1, context=(1 << 20), fixed_block_sizes=(16,), token_budget=4096)
+    x = W.make_layer(w)
+    _run_and_compare(oracle_mod, x, budget=4096)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_full_size_sampled(oracle_mod, cfg):
+    """Full-size workload in the benchmark's launch configuration; the oracle
+    recomputes the first and last sequence on their own."""
+    w = P[cfg]
+    x = W.make_layer(w)
+    sm = default_scale(w.head_dim)
+    print(f"[gpu parity] full size cfg {cfg}: {w.name} bs={x.block_size.tolist()}", flush=True)
+    g = GpuLayer(x)
+    r = g.run(w.token_budget, sm)
+    off = g.kv.centroid_off.cpu().numpy()
+    for b in sorted({0, w.batch - 1}):
+        xb = dataclasses.replace(x, q=x.q[b:b + 1], page_table=x.page_table[b:b + 1], seq_lens=x.seq_lens[b:b + 1])
+        ref = oracle_mod.run(xb, sm_scale=sm)
+        r0, r1 = off[b * w.num_kv_heads], off[(b + 1) * w.num_kv_heads]
+        np.testing.assert_array_equal(r.codes[r0:r1], ref.quant.codes)
+        np.testing.assert_array_equal(r.scale[b], ref.quant.scale[0])
+        np.testing.assert_array_equal(r.lo[b], ref.quant.lo[0])
+        check_selection(oracle_mod, xb, ref.quant, ref.scores, r.sel[b:b + 1], r.count[b:b + 1], w.token_budget)
+        out, lse = oracle_mod.attend(xb.q, x.k_cache, x.v_cache, xb.page_table, xb.seq_lens, x.block_size,
+                                     r.sel[b:b + 1], r.count[b:b + 1], sm, x.dtype)
+        check_attention(r.out[b:b + 1], r.lse[b:b + 1], out, lse, x.dtype)
+    del g
+    torch.cuda.empty_cache()
