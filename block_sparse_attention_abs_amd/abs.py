@@ -248,8 +248,9 @@ def current_stream() -> int:
 
 
 def workspace(nbytes: int, device="cuda"):
+    """Zero-filled device workspace (the decode workspace must start zeroed)."""
     import torch
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
 def build_centroids(kv: PagedKV, cents: Centroids, ws=None, stream: Optional[int] = None) -> Centroids:

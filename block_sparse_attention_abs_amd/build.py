@@ -27,21 +27,22 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, defines=(), objdir: str = OBJ) -> str:
+    """Compile every source and link `out`; `defines` are extra -D tuning macros."""
+    os.makedirs(objdir, exist_ok=True)
     procs = []
     for src in SOURCES:
-        obj = os.path.join(OBJ, src + ".o")
-        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        obj = os.path.join(objdir, src + ".o")
+        cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
         procs.append((src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
                                                  text=True)))
     objs, errors = [], []
     for src, obj, p in procs:
-        out, _ = p.communicate()
+        log, _ = p.communicate()
         if verbose or p.returncode != 0:
-            txt = "\n".join(l for l in out.splitlines() if "packed-fp32-ops" not in l and l.strip())
+            txt = "\n".join(l for l in log.splitlines() if "packed-fp32-ops" not in l and l.strip())
             if txt:
                 print(f"--- {src}\n{txt}", file=sys.stderr)
         if p.returncode != 0:
@@ -49,10 +50,10 @@ def build(verbose: bool = False) -> str:
         objs.append(obj)
     if errors:
         raise RuntimeError(f"hipcc failed for {errors}")
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

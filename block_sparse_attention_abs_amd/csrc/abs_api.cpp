@@ -150,26 +150,36 @@ BuildLayout build_layout(const Plan& p) {
     return l;
 }
 
-size_t select_bytes(const Plan& p) { return align_up((size_t)p.total_blocks * sizeof(float)); }
+int score_stride(const Plan& p) { return (p.max_n + 3) / 4 * 4; }
+
+size_t select_bytes(const Plan& p) {
+    return align_up((size_t)p.g.B * p.g.Hkv * score_stride(p) * sizeof(float));
+}
 
 struct DecodeLayout {
-    int ppw = 8, splits = 1;
+    int ppw = 8, chunk = 8, splits = 1;
     size_t ml = 0, o = 0, bytes = 0;
 };
 
-// Pages per workgroup: the largest of 8/4/2/1 that still gives >= 4
-// workgroups per compute unit (256 CUs), so that small batches fill the chip.
+// Build-time tuning of the decode launch (see decode_layout).
+#ifndef ABS_DECODE_TARGET_WGS
+#define ABS_DECODE_TARGET_WGS 1024
+#endif
+#ifndef ABS_DECODE_MAX_CHUNK
+#define ABS_DECODE_MAX_CHUNK 8
+#endif
+
+// Pages per workgroup: enough workgroups to fill the chip (about
+// ABS_DECODE_TARGET_WGS) but at most kMaxPagesPerWg pages each; pages are
+// held in registers `chunk` at a time.
 DecodeLayout decode_layout(const Plan& p) {
     DecodeLayout l;
     const int64_t heads = (int64_t)p.g.B * p.g.Hkv;
-    const int maxp = std::max(p.max_pages_read, 1);
-    l.ppw = 1;
-    for (int ppw : {8, 4, 2}) {
-        if (heads * ceil_div64(maxp, ppw) >= 1024) {
-            l.ppw = ppw;
-            break;
-        }
-    }
+    const int64_t maxp = std::max(p.max_pages_read, 1);
+    const int64_t ideal = std::max<int64_t>(1, ceil_div64(heads * maxp, ABS_DECODE_TARGET_WGS));
+    const int64_t cmax = ABS_DECODE_MAX_CHUNK;
+    l.chunk = (int)std::min<int64_t>(cmax, ideal >= 8 ? 8 : ideal >= 4 ? 4 : ideal >= 2 ? 2 : 1);
+    l.ppw = (int)std::min<int64_t>(absk::kMaxPagesPerWg, ceil_div64(ideal, l.chunk) * l.chunk);
     l.splits = (int)ceil_div64(maxp, l.ppw);
     const size_t rows = (size_t)p.g.B * p.g.Hq * l.splits;
     l.ml = 0;
@@ -283,9 +293,8 @@ abs_status abs_score_select(const abs_paged_kv* kv, const abs_block_map* map, co
     if (q == nullptr || sel == nullptr || sel_count == nullptr)
         return fail(ABS_ERR_INVALID_ARG, "null q, sel or sel_count");
     if (sel_cap < p.sel_cap) return fail(ABS_ERR_INVALID_ARG, "sel_cap %d < required %d", sel_cap, p.sel_cap);
-    if (p.max_n > absk::kTopkThreads * absk::kTopkMaxPerThread)
-        return fail(ABS_ERR_UNSUPPORTED, "%d blocks in one head (max %d)", p.max_n,
-                    absk::kTopkThreads * absk::kTopkMaxPerThread);
+    if (p.max_n > absk::kMaxBlocksPerHead)
+        return fail(ABS_ERR_UNSUPPORTED, "%d blocks in one head (max %d)", p.max_n, absk::kMaxBlocksPerHead);
     const size_t need = select_bytes(p);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(ABS_ERR_WORKSPACE, "select needs %zu workspace bytes, got %zu", need, workspace_bytes);
@@ -295,6 +304,7 @@ abs_status abs_score_select(const abs_paged_kv* kv, const abs_block_map* map, co
     a.lo = cents->lo;
     a.q = q;
     a.scores = reinterpret_cast<float*>(workspace);
+    a.stride = score_stride(p);
     a.sel = sel;
     a.count = sel_count;
     a.sel_cap = sel_cap;
@@ -328,6 +338,7 @@ abs_status abs_sparse_decode(const abs_paged_kv* kv, const abs_block_map* map, c
     a.part_ml = reinterpret_cast<float*>(ws_at(workspace, l.ml));
     a.part_o = reinterpret_cast<float*>(ws_at(workspace, l.o));
     a.pages_per_wg = l.ppw;
+    a.chunk = l.chunk;
     a.splits = l.splits;
     return hip_status(absk::launch_decode(p.g, p.dt, a, static_cast<hipStream_t>(stream)), "sparse_decode");
 }

@@ -12,8 +12,11 @@
 //         q.k is reduced over the 16 lanes of a DPP row; logits are kept in
 //         log2 units (q pre-scaled by sm_scale*log2 e).  The workgroup writes
 //         (m, l, o[D]) per query head to fp32 partials.
-// merge:  one workgroup per (b, query head): M = max m_s, l = sum 2^(m_s-M) l_s,
+// merge:  a second launch, one workgroup per (b, query head), merges the
+//         partials: M = max m_s, l = sum 2^(m_s-M) l_s,
 //         out = sum 2^(m_s-M) o_s / l, lse = (M + log2 l) * ln 2.
+//         (Merging inside the split launch would need an agent-scope release
+//         per workgroup, which on this GPU writes back the XCD's whole L2.)
 #include "device.hpp"
 
 namespace absk {
@@ -22,169 +25,246 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <typename T, int D, int GT, int PPW>
-__global__ __launch_bounds__(256) void k_decode_split(Geom g, const T* __restrict__ q,
-                                                      const int32_t* __restrict__ sel, int sel_cap,
-                                                      const int32_t* __restrict__ count, float qscale,
-                                                      float* __restrict__ part_ml, float* __restrict__ part_o,
-                                                      int splits) {
+// Waves per SIMD the split kernel is compiled for: 4 (all of a typical
+// grid resident at once) unless the group or the row width needs more registers.
+template <typename T, int D, int GT>
+struct DecodeOccupancy {
+    static constexpr int value = (GT >= 8 || D * (int)sizeof(T) > 256) ? 2 : 4;
+};
+
+template <typename T, int D, int GT, int CH>
+__global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT>::value)) void k_sparse_decode(Geom g, const T* __restrict__ q,
+                                                          const int32_t* __restrict__ sel, int sel_cap,
+                                                          const int32_t* __restrict__ count, float qscale,
+                                                          float* __restrict__ part_ml, float* __restrict__ part_o,
+                                                          int splits, int ppw) {
     constexpr int VEC = D / kRowLanes;
     constexpr int NW = VEC * Elem<T>::kBytes / 4;
+    constexpr float NEG = -__builtin_inff();
     const int split = blockIdx.x;
     const int bh = blockIdx.y;
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
+    const int row = threadIdx.x / kRowLanes;
+    const int lane = threadIdx.x & (kRowLanes - 1);
+    const int wave = threadIdx.x / 64;
+    const int wl = threadIdx.x & 63;
+
+    // The group's queries (raw storage words): independent of everything else, so issued first.
+    Words<NW> qw[GT];
+#pragma unroll
+    for (int gg = 0; gg < GT; ++gg) {
+        const int head = h * g.G + min(gg, g.G - 1);
+        qw[gg] = load_words<NW>(q + ((int64_t)b * g.Hq + head) * D + lane * VEC);
+    }
+
     const int L = g.seq_lens[b];
     const int bs = g.block_size[h];
     const int spb = bs / kPage;                        // pages per block (stride)
     const int npages = ceil_div(L, kPage);
     const int N = ceil_div(L, bs);
     const int K = min(max(count[bh], 0), sel_cap);
-    const int total = K * spb;
-    const int p0 = split * PPW;
-    const int row = threadIdx.x / kRowLanes;
-    const int lane = threadIdx.x & (kRowLanes - 1);
-    const int wave = threadIdx.x / 64;
-    const T* kc = reinterpret_cast<const T*>(g.k);
-    const T* vc = reinterpret_cast<const T*>(g.v);
+    const int total = min(K * spb, splits * ppw);      // selected pages of (b, h)
+    const int p0 = split * ppw;                        // ppw <= 64
 
-    // physical page and first token of each of this workgroup's pages (uniform)
-    int64_t phys[PPW];
-    int tok0[PPW];
-#pragma unroll
-    for (int i = 0; i < PPW; ++i) {
-        const int gp = p0 + i;
-        phys[i] = -1;
-        tok0[i] = 0;
-        if (gp < total) {
+    // Resolve this workgroup's pages lane-parallel: lane i of every wavefront
+    // follows selection entry -> logical page -> physical page for page p0 + i
+    // (the selection row is read speculatively up to sel_cap, so the page-table
+    // read does not wait for the count); readlane then broadcasts them.
+    int ph = -1, lp = 0;
+    {
+        const int gp = p0 + wl;
+        if (wl < ppw && gp < sel_cap * spb) {
             const int blk = min(max(sel[(int64_t)bh * sel_cap + gp / spb], 0), N - 1);
-            const int lp = blk * spb + gp % spb;
+            lp = blk * spb + gp % spb;
             if (lp < npages) {
                 const int pg = g.page_table[(int64_t)b * g.max_pages + lp];
-                if (pg >= 0 && pg < g.num_pages) {
-                    phys[i] = pg;
-                    tok0[i] = lp * kPage;
-                }
+                if (pg >= 0 && pg < g.num_pages) ph = pg;
             }
         }
+        if (gp >= total) ph = -1;
     }
 
-    Words<NW> kw[PPW], vw[PPW];
-#pragma unroll
-    for (int i = 0; i < PPW; ++i) {
-        if (phys[i] >= 0) {
-            const int64_t off = ((phys[i] * g.Hkv + h) * kPage + row) * D + lane * VEC;
-            kw[i] = load_words<NW>(kc + off);
-            vw[i] = load_words<NW>(vc + off);
-        } else {
-            kw[i] = zero_words<NW>();
-            vw[i] = zero_words<NW>();
-        }
-    }
-
-    float qv[GT][VEC];
-#pragma unroll
-    for (int gg = 0; gg < GT; ++gg) {
-        const bool on = gg < g.G;
-        const T* qp = q + ((int64_t)b * g.Hq + h * g.G + (on ? gg : 0)) * D + lane * VEC;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) qv[gg][e] = on ? Elem<T>::load1(qp + e) * qscale : 0.0f;
-    }
-
-    float sc[PPW][GT];
-    float m[GT];
-#pragma unroll
-    for (int gg = 0; gg < GT; ++gg) m[gg] = -__builtin_inff();
-#pragma unroll
-    for (int i = 0; i < PPW; ++i) {
-        const bool valid = phys[i] >= 0 && tok0[i] + row < L;
-#pragma unroll
-        for (int gg = 0; gg < GT; ++gg) {
-            float acc = 0.0f;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) acc += qv[gg][e] * Elem<T>::template get<NW>(kw[i], e);
-            acc = row16_sum(acc);
-            sc[i][gg] = valid ? acc : -__builtin_inff();
-            m[gg] = fmaxf(m[gg], sc[i][gg]);
-        }
-    }
-
-    __shared__ float s_m[4][GT];
-    __shared__ float s_l[4][GT];
+    __shared__ float s_red[4][GT];
     __shared__ float s_o[4][GT][D];
-#pragma unroll
-    for (int gg = 0; gg < GT; ++gg) {
-        m[gg] = rows4_max(m[gg]);
-        if ((threadIdx.x & 63) == 0) s_m[wave][gg] = m[gg];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int gg = 0; gg < GT; ++gg) m[gg] = fmaxf(fmaxf(s_m[0][gg], s_m[1][gg]), fmaxf(s_m[2][gg], s_m[3][gg]));
 
-    float l[GT], o[GT][VEC];
+    // Per-row running softmax state (each row of 16 lanes sees one token per page).
+    float m[GT], l[GT], o[GT][VEC];
 #pragma unroll
     for (int gg = 0; gg < GT; ++gg) {
+        m[gg] = NEG;
         l[gg] = 0.0f;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) o[gg][e] = 0.0f;
     }
+    // Selected pages are contiguous from the start of the list, so a
+    // workgroup whose first page is empty has nothing to do.
+    const bool active = __builtin_amdgcn_readfirstlane(ph) >= 0;
+    if (active) {
+        const T* kc = reinterpret_cast<const T*>(g.k);
+        const T* vc = reinterpret_cast<const T*>(g.v);
+        const uint32_t lane_off = (uint32_t)((row * D + lane * VEC) * sizeof(T));
+        for (int c0 = 0; c0 < ppw; c0 += CH) {
+            if (__builtin_amdgcn_readlane(ph, c0) < 0) break;      // rest of the list is empty
+            int phys[CH], tok0[CH];
 #pragma unroll
-    for (int i = 0; i < PPW; ++i) {
+            for (int i = 0; i < CH; ++i) {
+                phys[i] = __builtin_amdgcn_readlane(ph, c0 + i);
+                tok0[i] = __builtin_amdgcn_readlane(lp, c0 + i) * kPage;
+            }
+            // every K and V load of the chunk is in flight before any math
+            Words<NW> kw[CH], vw[CH];
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {   // branch-free: empty slots re-read page 0 and are masked below
+                const int64_t base = ((int64_t)(phys[i] >= 0 ? phys[i] : 0) * g.Hkv + h) * (kPage * D);
+                kw[i] = load_words_at<NW>(kc + base, lane_off);
+            }
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                const int64_t base = ((int64_t)(phys[i] >= 0 ? phys[i] : 0) * g.Hkv + h) * (kPage * D);
+                vw[i] = load_words_at<NW>(vc + base, lane_off);
+            }
+            float sc[CH][GT], cm[GT];
+#pragma unroll
+            for (int gg = 0; gg < GT; ++gg) cm[gg] = m[gg];
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                const bool valid = phys[i] >= 0 && tok0[i] + row < L;
+#pragma unroll
+                for (int gg = 0; gg < GT; ++gg) {
+                    const float z = row16_sum(dot_words<T, NW>(qw[gg], kw[i])) * qscale;
+                    sc[i][gg] = valid ? z : NEG;
+                    cm[gg] = fmaxf(cm[gg], sc[i][gg]);
+                }
+            }
+#pragma unroll
+            for (int gg = 0; gg < GT; ++gg) {
+                const float alpha = cm[gg] == NEG ? 1.0f : exp2f(m[gg] - cm[gg]);
+                m[gg] = cm[gg];
+                l[gg] *= alpha;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) o[gg][e] *= alpha;
+            }
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                float p[GT];
+#pragma unroll
+                for (int gg = 0; gg < GT; ++gg) {
+                    p[gg] = sc[i][gg] == NEG ? 0.0f : exp2f(sc[i][gg] - m[gg]);
+                    l[gg] += p[gg];
+                }
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const float v = Elem<T>::template get<NW>(vw[i], e);
+#pragma unroll
+                    for (int gg = 0; gg < GT; ++gg) o[gg][e] = fmaf(p[gg], v, o[gg][e]);
+                }
+            }
+        }
+
+        // rows -> workgroup: common max, rescale, sum (shuffles within a
+        // wavefront, LDS across the four wavefronts)
+        float M[GT];
+#pragma unroll
+        for (int gg = 0; gg < GT; ++gg) M[gg] = rows4_max(m[gg]);
+#pragma unroll
+        for (int gg = 0; gg < GT; ++gg)
+            if (wl == 0) s_red[wave][gg] = M[gg];
+        __syncthreads();
 #pragma unroll
         for (int gg = 0; gg < GT; ++gg) {
-            const float p = sc[i][gg] == -__builtin_inff() ? 0.0f : exp2f(sc[i][gg] - m[gg]);
-            l[gg] += p;
+            M[gg] = fmaxf(fmaxf(s_red[0][gg], s_red[1][gg]), fmaxf(s_red[2][gg], s_red[3][gg]));
+            const float f = m[gg] == NEG ? 0.0f : exp2f(m[gg] - M[gg]);
+            l[gg] = rows4_sum(l[gg] * f);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) o[gg][e] += p * Elem<T>::template get<NW>(vw[i], e);
+            for (int e = 0; e < VEC; ++e) o[gg][e] = rows4_sum(o[gg][e] * f);
         }
-    }
+        __syncthreads();
+        if (wl < kRowLanes) {
 #pragma unroll
-    for (int gg = 0; gg < GT; ++gg) {
-        l[gg] = rows4_sum(l[gg]);
+            for (int gg = 0; gg < GT; ++gg) {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) o[gg][e] = rows4_sum(o[gg][e]);
-    }
-    if ((threadIdx.x & 63) < kRowLanes) {
-#pragma unroll
-        for (int gg = 0; gg < GT; ++gg) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) s_o[wave][gg][lane * VEC + e] = o[gg][e];
-            if (lane == 0) s_l[wave][gg] = l[gg];
+                for (int e = 0; e < VEC; ++e) s_o[wave][gg][lane * VEC + e] = o[gg][e];
+                if (lane == 0) s_red[wave][gg] = l[gg];
+            }
         }
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < GT * D; idx += blockDim.x) {
-        const int gg = idx / D, d = idx - gg * D;
-        if (gg >= g.G) continue;
-        const int64_t prow = ((int64_t)b * g.Hq + h * g.G + gg) * splits + split;
-        part_o[prow * D + d] = s_o[0][gg][d] + s_o[1][gg][d] + s_o[2][gg][d] + s_o[3][gg][d];
-        if (d == 0) {
-            part_ml[prow * 2 + 0] = m[gg];
-            part_ml[prow * 2 + 1] = s_l[0][gg] + s_l[1][gg] + s_l[2][gg] + s_l[3][gg];
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < GT * D; idx += blockDim.x) {
+            const int gg = idx / D, d = idx - gg * D;
+            if (gg >= g.G) continue;
+            const int64_t prow = ((int64_t)b * g.Hq + h * g.G + gg) * splits + split;
+            part_o[prow * D + d] = s_o[0][gg][d] + s_o[1][gg][d] + s_o[2][gg][d] + s_o[3][gg][d];
+            if (d == 0) {
+                part_ml[prow * 2 + 0] = M[gg];
+                part_ml[prow * 2 + 1] = s_red[0][gg] + s_red[1][gg] + s_red[2][gg] + s_red[3][gg];
+            }
         }
+    } else if (p0 < total) {
+        // in the merged range but every page of it is empty (the tail of a
+        // partial last block): an empty partial
+        for (int gg = threadIdx.x; gg < g.G; gg += blockDim.x)
+            part_ml[(((int64_t)b * g.Hq + h * g.G + gg) * splits + split) * 2] = NEG;
     }
 }
 
+// One workgroup per (b, query head): merge the partials of the splits that
+// held pages of (b, h).  Thread (group sg, channel d) folds splits sg,
+// sg + NG, ... with an online max/sum (its loads are independent, so they are
+// all in flight together); the NG groups are then combined through LDS.
 template <typename T, int D>
-__global__ __launch_bounds__(D) void k_decode_merge(Geom g, const float* __restrict__ part_ml,
-                                                    const float* __restrict__ part_o, int splits,
-                                                    T* __restrict__ out, float* __restrict__ lse) {
-    const int bi = blockIdx.x;                 // b * Hq + query head
-    const int d = threadIdx.x;
+__global__ __launch_bounds__(256) void k_decode_merge(Geom g, const int32_t* __restrict__ count, int sel_cap,
+                                                      int ppw, int splits, const float* __restrict__ part_ml,
+                                                      const float* __restrict__ part_o, T* __restrict__ out,
+                                                      float* __restrict__ lse) {
+    constexpr float NEG = -__builtin_inff();
+    constexpr int NG = 256 / D;
+    const int bi = blockIdx.x;                       // b * Hq + query head
+    const int b = bi / g.Hq, head = bi - b * g.Hq;
+    const int h = head / g.G;
+    const int bh = b * g.Hkv + h;
+    const int spb = g.block_size[h] / kPage;
+    const int K = min(max(count[bh], 0), sel_cap);
+    const int total = min(K * spb, splits * ppw);
+    const int nact = max(1, ceil_div(total, ppw));
+    const int d = threadIdx.x % D, sg = threadIdx.x / D;
     const float* ml = part_ml + (int64_t)bi * splits * 2;
-    float M = -__builtin_inff();
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[2 * s]);
-    float lsum = 0.0f, acc = 0.0f;
-    if (M != -__builtin_inff()) {
-        for (int s = 0; s < splits; ++s) {
-            const float ms = ml[2 * s];
-            if (ms == -__builtin_inff()) continue;
-            const float w = exp2f(ms - M);
-            lsum += w * ml[2 * s + 1];
-            acc += w * part_o[((int64_t)bi * splits + s) * D + d];
+    const float* po = part_o + (int64_t)bi * splits * D + d;
+
+    float m = NEG, ls = 0.0f, acc = 0.0f;
+#pragma unroll 8
+    for (int s = sg; s < nact; s += NG) {
+        const float ms = ml[2 * s];
+        const float lv = ml[2 * s + 1];
+        const float ov = po[(int64_t)s * D];
+        if (ms != NEG) {
+            const float mn = fmaxf(m, ms);
+            const float a = m == NEG ? 0.0f : exp2f(m - mn);
+            const float w = exp2f(ms - mn);
+            ls = ls * a + lv * w;
+            acc = acc * a + ov * w;
+            m = mn;
         }
     }
-    Elem<T>::store1(out + (int64_t)bi * D + d, lsum > 0.0f ? acc / lsum : 0.0f);
-    if (lse != nullptr && d == 0) lse[bi] = lsum > 0.0f ? (M + log2f(lsum)) * kLn2 : -__builtin_inff();
+    __shared__ float s_m[NG][D], s_l[NG][D], s_a[NG][D];
+    s_m[sg][d] = m;
+    s_l[sg][d] = ls;
+    s_a[sg][d] = acc;
+    __syncthreads();
+    if (sg != 0) return;
+    float M = s_m[0][d];
+#pragma unroll
+    for (int i = 1; i < NG; ++i) M = fmaxf(M, s_m[i][d]);
+    float lsum = 0.0f, o = 0.0f;
+    if (M != NEG) {
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+            if (s_m[i][d] == NEG) continue;
+            const float w = exp2f(s_m[i][d] - M);
+            lsum += s_l[i][d] * w;
+            o += s_a[i][d] * w;
+        }
+    }
+    Elem<T>::store1(out + (int64_t)bi * D + d, lsum > 0.0f ? o / lsum : 0.0f);
+    if (lse != nullptr && d == 0) lse[bi] = lsum > 0.0f ? (M + log2f(lsum)) * kLn2 : NEG;
 }
 
 template <typename T, int D, int GT>
@@ -192,18 +272,19 @@ hipError_t decode_gt(const Geom& g, const DecodeArgs& a, hipStream_t s) {
     const dim3 grid(a.splits, g.B * g.Hkv);
     const float qscale = a.sm_scale * kLog2e;
     const T* q = reinterpret_cast<const T*>(a.q);
-#define ABS_SPLIT(PPW_)                                                                                   \
-    hipLaunchKernelGGL((k_decode_split<T, D, GT, PPW_>), grid, dim3(256), 0, s, g, q, a.sel, a.sel_cap, \
-                       a.count, qscale, a.part_ml, a.part_o, a.splits)
-    switch (a.pages_per_wg) {
-        case 1: ABS_SPLIT(1); break;
-        case 2: ABS_SPLIT(2); break;
-        case 4: ABS_SPLIT(4); break;
-        default: ABS_SPLIT(8); break;
+    T* out = reinterpret_cast<T*>(a.out);
+#define ABS_DECODE(CH_)                                                                                      \
+    hipLaunchKernelGGL((k_sparse_decode<T, D, GT, CH_>), grid, dim3(256), 0, s, g, q, a.sel, a.sel_cap,  \
+                       a.count, qscale, a.part_ml, a.part_o, a.splits, a.pages_per_wg)
+    switch (a.chunk) {
+        case 1: ABS_DECODE(1); break;
+        case 2: ABS_DECODE(2); break;
+        case 4: ABS_DECODE(4); break;
+        default: ABS_DECODE(8); break;
     }
-#undef ABS_SPLIT
-    hipLaunchKernelGGL((k_decode_merge<T, D>), dim3(g.B * g.Hq), dim3(D), 0, s, g, a.part_ml, a.part_o, a.splits,
-                       reinterpret_cast<T*>(a.out), a.lse);
+#undef ABS_DECODE
+    hipLaunchKernelGGL((k_decode_merge<T, D>), dim3(g.B * g.Hq), dim3(256), 0, s, g, a.count, a.sel_cap,
+                       a.pages_per_wg, a.splits, a.part_ml, a.part_o, out, a.lse);
     return hipGetLastError();
 }
 

@@ -56,6 +56,13 @@ __device__ __forceinline__ Words<NW> load_words(const void* p) {
     return r;
 }
 
+// Load from a wavefront-uniform base plus a per-lane unsigned byte offset
+// (lets the compiler use scalar-base addressing: one VGPR per lane, not two).
+template <int NW>
+__device__ __forceinline__ Words<NW> load_words_at(const void* uniform_base, uint32_t byte_off) {
+    return load_words<NW>(static_cast<const char*>(uniform_base) + byte_off);
+}
+
 template <int NW>
 __device__ __forceinline__ Words<NW> zero_words() {
     Words<NW> r;
@@ -87,6 +94,50 @@ struct Elem<uint16_t> {  // bf16 bit patterns
     __device__ static __forceinline__ float load1(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
     __device__ static __forceinline__ void store1(uint16_t* p, float v) { *p = (uint16_t)f32_to_bf16(v); }
 };
+
+// Partial dot product of one lane's run of a query row and a key row (raw
+// storage words, fp32 result).  bf16: v_dot2c_f32_bf16 on packed pairs (exact
+// products, fp32 accumulation, no unpacking); fp32: plain fma.
+template <typename T, int NW>
+__device__ __forceinline__ float dot_words(const Words<NW>& a, const Words<NW>& b);
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <>
+__device__ __forceinline__ float dot_words<uint16_t, 2>(const Words<2>& a, const Words<2>& b) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w[i]),
+                                              __builtin_bit_cast(bf16x2_t, b.w[i]), acc, false);
+    return acc;
+}
+
+template <>
+__device__ __forceinline__ float dot_words<uint16_t, 4>(const Words<4>& a, const Words<4>& b) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w[i]),
+                                              __builtin_bit_cast(bf16x2_t, b.w[i]), acc, false);
+    return acc;
+}
+
+template <>
+__device__ __forceinline__ float dot_words<float, 4>(const Words<4>& a, const Words<4>& b) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = fmaf(__uint_as_float(a.w[i]), __uint_as_float(b.w[i]), acc);
+    return acc;
+}
+
+template <>
+__device__ __forceinline__ float dot_words<float, 8>(const Words<8>& a, const Words<8>& b) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = fmaf(__uint_as_float(a.w[i]), __uint_as_float(b.w[i]), acc);
+    return acc;
+}
 
 // ---- cross-lane reductions --------------------------------------------------
 

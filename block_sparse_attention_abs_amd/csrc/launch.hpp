@@ -40,16 +40,15 @@ struct BuildArgs {
 hipError_t launch_build(const Geom& g, DType dt, const BuildArgs& a, hipStream_t s);
 
 // Score + select.
-constexpr int kScoreTile = 64;          // blocks per score workgroup (D = 128)
-constexpr int kTopkThreads = 1024;
-constexpr int kTopkMaxPerThread = 64;   // N_{b,h} <= 65536
+constexpr int kMaxBlocksPerHead = 65536;   // top-K keeps N_{b,h} keys in registers: 1024 x 64
 
 struct SelectArgs {
     const uint8_t* codes;
     const float* scale;
     const float* lo;
     const void* q;
-    float* scores;    // [total_blocks]
+    float* scores;    // [B*Hkv][stride]
+    int stride;       // max N_{b,h} rounded up to a multiple of 4
     int32_t* sel;
     int32_t* count;
     int sel_cap;
@@ -70,9 +69,12 @@ struct DecodeArgs {
     float* lse;       // may be null
     float* part_ml;   // [B*Hq][splits][2]
     float* part_o;    // [B*Hq][splits][D]
-    int pages_per_wg;
+    int pages_per_wg; // <= kMaxPagesPerWg, a multiple of chunk
+    int chunk;        // pages held in registers at a time: 1, 2, 4 or 8
     int splits;
 };
+
+constexpr int kMaxPagesPerWg = 64;
 
 hipError_t launch_decode(const Geom& g, DType dt, const DecodeArgs& a, hipStream_t s);
 

@@ -8,15 +8,24 @@
 //         per-channel dequantization once per workgroup:
 //             w_d = qbar_d * scale_d,   c0 = sum_d qbar_d * lo_d,
 //             score_j = c0 + sum_d w_d * code_{j,d}
-//         (fp64 inside, stored as fp32).  head_dim/32 lanes share one block
-//         row of INT4 codes, 16 bytes each, so one load instruction reads a
-//         contiguous 1 KiB run.
-// top-K:  one 1024-thread workgroup per (b, h).  Thread t owns the block
-//         indices [t*KPT, (t+1)*KPT) as order-preserving 32-bit keys in
-//         registers.  An 8-bit radix select (4 passes over an LDS histogram)
-//         finds the K-th largest key tau and how many keys equal to tau to
-//         keep; two block-wide scans then write the kept indices in ascending
-//         order (keys > tau, plus the lowest-index keys == tau).
+//         (fp64 inside, stored as fp32 in a [b*Hkv+h][stride] scratch with
+//         16-byte aligned rows).  head_dim/32 lanes share one block row of
+//         INT4 codes, 16 bytes each, so one load instruction reads a
+//         contiguous 1 KiB run; the code loads are issued before the
+//         workgroup's query prologue.
+// top-K:  one workgroup per (b, h); thread t owns block indices
+//         [t*KPT, (t+1)*KPT) as order-preserving 32-bit keys in registers.
+//         1. min/max of the scores; a 2048-bin histogram of the scores'
+//            position in [min, max] (a monotone binning, spread over the
+//            bins, so LDS atomics rarely collide);
+//         2. the bin b* holding the K-th largest score, and how many scores
+//            lie in higher bins;
+//         3. the few candidates in b* are ranked exactly by (score desc,
+//            index asc), giving the threshold pair (tau_key, tau_index);
+//            if b* is crowded (heavy ties) an 8-bit radix select over the
+//            keys gives the same pair instead;
+//         4. keep key > tau_key, or key == tau_key and index <= tau_index;
+//            a block scan writes the kept indices in ascending order.
 #include "device.hpp"
 
 namespace absk {
@@ -25,7 +34,7 @@ namespace {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_score(Geom g, const uint8_t* __restrict__ codes,
                                                const float* __restrict__ scale, const float* __restrict__ lo,
-                                               const T* __restrict__ q, float* __restrict__ scores) {
+                                               const T* __restrict__ q, float* __restrict__ scores, int stride) {
     constexpr int LPB = D / 32;               // lanes per block row (16 B of codes each)
     constexpr int BPW = 256 / LPB;            // blocks per workgroup
     const int bh = blockIdx.y;
@@ -34,6 +43,11 @@ __global__ __launch_bounds__(256) void k_score(Geom g, const uint8_t* __restrict
     const int j0 = blockIdx.x * BPW;
     if (j0 >= N) return;
     const int64_t row0 = g.off[bh];
+    const int sub = threadIdx.x % LPB;
+    const int j = j0 + threadIdx.x / LPB;
+
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (j < N) v = *reinterpret_cast<const uint4*>(codes + (row0 + j) * (D / 2) + sub * 16);
 
     __shared__ double w[D];
     __shared__ double c0_part[D / 64 > 0 ? D / 64 : 1];
@@ -52,21 +66,16 @@ __global__ __launch_bounds__(256) void k_score(Geom g, const uint8_t* __restrict
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) c0 += c0_part[i];
 
-    const int sub = threadIdx.x % LPB;
-    const int j = j0 + threadIdx.x / LPB;
+    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+    const double* ws = w + sub * 32;
     double acc = 0.0;
-    if (j < N) {
-        const uint4 v = *reinterpret_cast<const uint4*>(codes + (row0 + j) * (D / 2) + sub * 16);
-        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
-        const double* ws = w + sub * 32;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int n = 0; n < 8; ++n) acc += ws[i * 8 + n] * (double)((wd[i] >> (4 * n)) & 15u);
-    }
+        for (int n = 0; n < 8; ++n) acc += ws[i * 8 + n] * (double)((wd[i] >> (4 * n)) & 15u);
 #pragma unroll
     for (int off = 1; off < LPB; off <<= 1) acc += __shfl_xor(acc, off);
-    if (j < N && sub == 0) scores[row0 + j] = (float)(c0 + acc);
+    if (j < N && sub == 0) scores[(int64_t)bh * stride + j] = (float)(c0 + acc);
 }
 
 // Order-preserving map of a float to uint32 (larger float -> larger key);
@@ -77,7 +86,12 @@ __device__ __forceinline__ uint32_t float_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum over the workgroup (blockDim.x == kTopkThreads).
+__device__ __forceinline__ float key_float(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Exclusive prefix sum over a workgroup of NT threads; `total` gets the sum.
+template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t x = v;
@@ -90,7 +104,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
     __syncthreads();
     uint32_t before = 0, all = 0;
 #pragma unroll
-    for (int i = 0; i < kTopkThreads / 64; ++i) {
+    for (int i = 0; i < NT / 64; ++i) {
         const uint32_t t = s_wave[i];
         before += i < wave ? t : 0u;
         all += t;
@@ -100,96 +114,217 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
     return before + x - v;
 }
 
-template <int KPT>
-__global__ __launch_bounds__(kTopkThreads) void k_topk(Geom g, const float* __restrict__ scores, int budget,
-                                                       int32_t* __restrict__ sel, int sel_cap,
-                                                       int32_t* __restrict__ count) {
+template <int NT>
+__device__ __forceinline__ float block_max(float v, float* s_wave) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    if ((threadIdx.x & 63) == 0) s_wave[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = s_wave[0];
+#pragma unroll
+    for (int i = 1; i < NT / 64; ++i) r = fmaxf(r, s_wave[i]);
+    __syncthreads();
+    return r;
+}
+
+constexpr int kBins = 2048;
+constexpr int kCandCap = 512;
+
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void k_topk(Geom g, const float* __restrict__ scores, int stride, int budget,
+                                             int32_t* __restrict__ sel, int sel_cap, int32_t* __restrict__ count) {
     const int bh = blockIdx.x;
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
     const int bs = g.block_size[h];
     const int N = ceil_div(g.seq_lens[b], bs);
     const int K = min(N, max(1, budget / bs));
-    const int64_t row0 = g.off[bh];
     int32_t* out = sel + (int64_t)bh * sel_cap;
     if (threadIdx.x == 0) count[bh] = K;
     if (K >= N) {
-        for (int j = threadIdx.x; j < N; j += blockDim.x) out[j] = j;
+        for (int j = threadIdx.x; j < N; j += NT) out[j] = j;
         return;
     }
 
     const int base = threadIdx.x * KPT;
+    const float* row = scores + (int64_t)bh * stride;
     uint32_t key[KPT];
+    if constexpr (KPT % 4 == 0) {
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) key[e] = base + e < N ? float_key(scores[row0 + base + e]) : 0u;
+        for (int e = 0; e < KPT; e += 4) {
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (base + e < N) v = *reinterpret_cast<const float4*>(row + base + e);   // rows are padded to 4
+            key[e] = float_key(v.x);
+            key[e + 1] = float_key(v.y);
+            key[e + 2] = float_key(v.z);
+            key[e + 3] = float_key(v.w);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) key[e] = float_key(base + e < N ? row[base + e] : 0.0f);
+    }
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+        if (base + e < N) {
+            mn = fminf(mn, key_float(key[e]));
+            mx = fmaxf(mx, key_float(key[e]));
+        }
+    }
 
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t s_digit, s_need;
-    __shared__ uint32_t s_wave[kTopkThreads / 64];
-    uint32_t prefix = 0, mask = 0, need = (uint32_t)K;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0u;
-        __syncthreads();
+    __shared__ uint32_t hist[kBins];
+    __shared__ uint32_t s_wave[NT / 64];
+    __shared__ float s_wf[NT / 64];
+    __shared__ uint32_t s_cand_key[kCandCap];
+    __shared__ int32_t s_cand_idx[kCandCap];
+    __shared__ uint32_t s_bin, s_above, s_ncand, s_tau_key;
+    __shared__ int32_t s_tau_idx;
+
+    for (int i = threadIdx.x; i < kBins; i += NT) hist[i] = 0u;
+    if (threadIdx.x == 0) s_ncand = 0u;
+    mx = block_max<NT>(mx, s_wf);
+    mn = -block_max<NT>(-mn, s_wf);
+    const float range = mx - mn;
+    const float inv = (float)kBins / range;
+    const bool binned = range > 0.0f && range <= 3.0e38f && inv > 0.0f && inv <= 3.0e38f;
+
+    uint32_t tau_key = 0u;
+    int32_t tau_idx = -1;
+    bool resolved = false;
+    // bin of a score: monotone non-decreasing in the score
+    auto bin_of = [&](uint32_t k) { return min(kBins - 1, (int)((key_float(k) - mn) * inv)); };
+    if (binned) {
 #pragma unroll
         for (int e = 0; e < KPT; ++e)
-            if (base + e < N && (key[e] & mask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 255u], 1u);
+            if (base + e < N) atomicAdd(&hist[bin_of(key[e])], 1u);
         __syncthreads();
-        if (threadIdx.x < 64) {
-            // lane l holds bins 255-4l .. 252-4l (descending digit order)
-            const int lane = threadIdx.x;
-            uint32_t c[4];
+        // thread t sums bins kBins-1-t*BPT ... downwards; scan from the top
+        constexpr int BPT = kBins / NT;
+        uint32_t c[BPT], mine = 0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) c[i] = hist[255 - 4 * lane - i];
-            const uint32_t mine = c[0] + c[1] + c[2] + c[3];
-            uint32_t incl = mine;
+        for (int i = 0; i < BPT; ++i) {
+            c[i] = hist[kBins - 1 - threadIdx.x * BPT - i];
+            mine += c[i];
+        }
+        uint32_t total;
+        const uint32_t excl = block_exclusive_scan<NT>(mine, s_wave, &total);
+        if (excl < (uint32_t)K && (uint32_t)K <= excl + mine) {     // exactly one thread
+            uint32_t above = excl;
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const uint32_t y = __shfl_up(incl, off);
-                if (lane >= off) incl += y;
+            for (int i = 0; i < BPT; ++i) {
+                if (above + c[i] >= (uint32_t)K) {
+                    s_bin = kBins - 1 - threadIdx.x * BPT - i;
+                    s_above = above;
+                    break;
+                }
+                above += c[i];
             }
-            const uint32_t excl = incl - mine;       // keys in bins above this lane's
-            if (excl < need && need <= incl) {        // exactly one lane
-                uint32_t above = excl;
+        }
+        __syncthreads();
+        const int bstar = (int)s_bin;
+        const uint32_t need = (uint32_t)K - s_above;                 // 1 <= need <= |bin b*|
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (above + c[i] >= need) {
-                        s_digit = 255u - 4u * lane - i;
-                        s_need = need - above;
-                        break;
-                    }
-                    above += c[i];
+        for (int e = 0; e < KPT; ++e) {
+            if (base + e < N && bin_of(key[e]) == bstar) {
+                const uint32_t slot = atomicAdd(&s_ncand, 1u);
+                if (slot < (uint32_t)kCandCap) {
+                    s_cand_key[slot] = key[e];
+                    s_cand_idx[slot] = base + e;
                 }
             }
         }
         __syncthreads();
-        prefix |= s_digit << shift;
-        mask |= 255u << shift;
-        need = s_need;
+        const uint32_t nc = s_ncand;
+        if (nc <= (uint32_t)kCandCap) {
+            for (uint32_t t = threadIdx.x; t < nc; t += NT) {
+                const uint32_t kt = s_cand_key[t];
+                const int32_t it = s_cand_idx[t];
+                uint32_t rank = 0;
+                for (uint32_t u = 0; u < nc; ++u) {
+                    const uint32_t ku = s_cand_key[u];
+                    rank += (ku > kt || (ku == kt && s_cand_idx[u] < it)) ? 1u : 0u;
+                }
+                if (rank == need - 1) {
+                    s_tau_key = kt;
+                    s_tau_idx = it;
+                }
+            }
+            __syncthreads();
+            tau_key = s_tau_key;
+            tau_idx = s_tau_idx;
+            resolved = true;
+        }
     }
-    const uint32_t tau = prefix;
+    if (!resolved) {
+        // crowded threshold bin or degenerate range: 8-bit radix select on the keys
+        uint32_t prefix = 0, mask = 0, need = (uint32_t)K;
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            __syncthreads();
+            for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < KPT; ++e)
+                if (base + e < N && (key[e] & mask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 255u], 1u);
+            __syncthreads();
+            if (threadIdx.x < 64) {
+                const int lane = threadIdx.x;   // lane l holds digits 255-4l .. 252-4l
+                uint32_t c[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) c[i] = hist[255 - 4 * lane - i];
+                const uint32_t mine = c[0] + c[1] + c[2] + c[3];
+                uint32_t incl = mine;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const uint32_t y = __shfl_up(incl, off);
+                    if (lane >= off) incl += y;
+                }
+                const uint32_t excl = incl - mine;
+                if (excl < need && need <= incl) {
+                    uint32_t above = excl;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if (above + c[i] >= need) {
+                            s_bin = 255u - 4u * lane - i;
+                            s_above = need - above;
+                            break;
+                        }
+                        above += c[i];
+                    }
+                }
+            }
+            __syncthreads();
+            prefix |= s_bin << shift;
+            mask |= 255u << shift;
+            need = s_above;
+        }
+        tau_key = prefix;
+        // the need-th lowest index among keys equal to tau
+        uint32_t n_eq = 0;
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) n_eq += (base + e < N && key[e] == tau_key) ? 1u : 0u;
+        uint32_t total;
+        uint32_t r = block_exclusive_scan<NT>(n_eq, s_wave, &total);
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            if (base + e < N && key[e] == tau_key) {
+                if (r == need - 1) s_tau_idx = base + e;
+                ++r;
+            }
+        }
+        __syncthreads();
+        tau_idx = s_tau_idx;
+    }
 
-    // keys > tau are kept; of the keys == tau, the `need` lowest indices.
-    uint32_t n_eq = 0;
+    // keep (key > tau_key) or (key == tau_key and index <= tau_idx): exactly K
+    uint32_t n_keep = 0;
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) n_eq += (base + e < N && key[e] == tau) ? 1u : 0u;
+    for (int e = 0; e < KPT; ++e)
+        n_keep += (base + e < N && (key[e] > tau_key || (key[e] == tau_key && base + e <= tau_idx))) ? 1u : 0u;
     uint32_t total;
-    const uint32_t eq_base = block_exclusive_scan(n_eq, s_wave, &total);
-    uint32_t r = eq_base, n_keep = 0;
+    uint32_t pos = block_exclusive_scan<NT>(n_keep, s_wave, &total);
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
-        if (base + e < N) {
-            if (key[e] > tau) ++n_keep;
-            else if (key[e] == tau && r++ < need) ++n_keep;
-        }
-    }
-    uint32_t pos = block_exclusive_scan(n_keep, s_wave, &total);
-    r = eq_base;
-#pragma unroll
-    for (int e = 0; e < KPT; ++e) {
-        if (base + e < N) {
-            bool keep = key[e] > tau;
-            if (key[e] == tau) keep = r++ < need;
-            if (keep && pos < (uint32_t)K) out[pos++] = base + e;
-        }
+        const bool keep = base + e < N && (key[e] > tau_key || (key[e] == tau_key && base + e <= tau_idx));
+        if (keep && pos < (uint32_t)K) out[pos++] = base + e;
     }
 }
 
@@ -198,19 +333,19 @@ hipError_t select_impl(const Geom& g, const SelectArgs& a, hipStream_t s) {
     constexpr int BPW = 256 / (D / 32);
     const dim3 sgrid(ceil_div(a.max_n, BPW), g.B * g.Hkv);
     hipLaunchKernelGGL((k_score<T, D>), sgrid, dim3(256), 0, s, g, a.codes, a.scale, a.lo,
-                       reinterpret_cast<const T*>(a.q), a.scores);
+                       reinterpret_cast<const T*>(a.q), a.scores, a.stride);
     const dim3 tgrid(g.B * g.Hkv);
-    const int kpt = ceil_div(a.max_n, kTopkThreads);
-#define ABS_TOPK(KPT_)                                                                                     \
-    hipLaunchKernelGGL((k_topk<KPT_>), tgrid, dim3(kTopkThreads), 0, s, g, a.scores, a.budget, a.sel, \
+#define ABS_TOPK(NT_, KPT_)                                                                                  \
+    hipLaunchKernelGGL((k_topk<NT_, KPT_>), tgrid, dim3(NT_), 0, s, g, a.scores, a.stride, a.budget, a.sel, \
                        a.sel_cap, a.count)
-    if (kpt <= 1) ABS_TOPK(1);
-    else if (kpt <= 2) ABS_TOPK(2);
-    else if (kpt <= 4) ABS_TOPK(4);
-    else if (kpt <= 8) ABS_TOPK(8);
-    else if (kpt <= 16) ABS_TOPK(16);
-    else if (kpt <= 32) ABS_TOPK(32);
-    else ABS_TOPK(64);
+    const int n = a.max_n;
+    if (n <= 512 * 1) ABS_TOPK(512, 1);
+    else if (n <= 512 * 2) ABS_TOPK(512, 2);
+    else if (n <= 512 * 4) ABS_TOPK(512, 4);
+    else if (n <= 512 * 8) ABS_TOPK(512, 8);
+    else if (n <= 512 * 16) ABS_TOPK(512, 16);
+    else if (n <= 512 * 32) ABS_TOPK(512, 32);
+    else ABS_TOPK(1024, 64);
 #undef ABS_TOPK
     return hipGetLastError();
 }

@@ -157,9 +157,10 @@ abs_status abs_build_centroids(const abs_paged_kv *kv, const abs_block_map *map,
 
 /*
  * Dot-product estimation + top-K (Figure 1; the "Estimation" and "Top-K"
- * stages of the per-stage latency figure after Figure 13).  For each (b, h): qbar = sum of the query heads
- * h*G .. h*G+G-1 (G = num_q_heads / num_kv_heads), score_j = qbar . (code_j *
- * scale + lo); keep the K_{b,h} best blocks ranked by (score desc, index asc).
+ * stages of the per-stage latency figure after Figure 13).  For each (b, h):
+ * qbar = sum of the query heads h*G .. h*G+G-1 (G = num_q_heads /
+ * num_kv_heads), score_j = qbar . (code_j * scale + lo); keep the K_{b,h}
+ * best blocks ranked by (score desc, index asc).
  *   q: device [num_seqs][num_q_heads][head_dim] in kv_dtype.
  *   sel: device int32 [num_seqs][num_kv_heads][sel_cap]; row (b, h) gets its
  *       K_{b,h} block indices in ascending order; slots past K are not written.
@@ -173,8 +174,9 @@ abs_status abs_score_select(const abs_paged_kv *kv, const abs_block_map *map,
 
 /*
  * Exact attention over the selected blocks only (Figure 1's sparse attention;
- * the "Attention" stage of the figure after Figure 13), split over pages with an fp32 online
- * softmax and a log-sum-exp merge (FlashAttention, in the page's references).
+ * the "Attention" stage of the figure after Figure 13), split over pages with
+ * an fp32 online softmax and a log-sum-exp merge (FlashAttention, in the
+ * page's references); two kernel launches (split, merge).
  * For query head i of KV head h = i / G: the kept tokens are the union of
  * [j*bs_h, min((j+1)*bs_h, L_b)) over the first sel_count[b][h] entries j of
  * sel row (b, h); z_t = sm_scale * q_i . k_t;
@@ -183,6 +185,8 @@ abs_status abs_score_select(const abs_paged_kv *kv, const abs_block_map *map,
  *       sel_count[b][h] must not exceed K_{b,h} for it).
  *   out: device [num_seqs][num_q_heads][head_dim] in kv_dtype.
  *   lse: device f32 [num_seqs][num_q_heads], natural log; may be NULL.
+ *   workspace: >= abs_workspace_bytes(ABS_OP_DECODE) bytes (fp32 partials;
+ *       no initialization needed).
  */
 abs_status abs_sparse_decode(const abs_paged_kv *kv, const abs_block_map *map, const void *q,
                              const int32_t *sel, int32_t sel_cap, const int32_t *sel_count,
