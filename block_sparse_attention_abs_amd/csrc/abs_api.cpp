@@ -158,6 +158,7 @@ size_t select_bytes(const Plan& p) {
 
 struct DecodeLayout {
     int ppw = 8, chunk = 8, splits = 1;
+    bool pipelined = false;
     size_t ml = 0, o = 0, bytes = 0;
 };
 
@@ -167,6 +168,9 @@ struct DecodeLayout {
 #endif
 #ifndef ABS_DECODE_MAX_CHUNK
 #define ABS_DECODE_MAX_CHUNK 8
+#endif
+#ifndef ABS_DECODE_PIPE_WGS
+#define ABS_DECODE_PIPE_WGS 256
 #endif
 
 // Pages per workgroup: enough workgroups to fill the chip (about
@@ -181,6 +185,16 @@ DecodeLayout decode_layout(const Plan& p) {
     l.chunk = (int)std::min<int64_t>(cmax, ideal >= 8 ? 8 : ideal >= 4 ? 4 : ideal >= 2 ? 2 : 1);
     l.ppw = (int)std::min<int64_t>(absk::kMaxPagesPerWg, ceil_div64(ideal, l.chunk) * l.chunk);
     l.splits = (int)ceil_div64(maxp, l.ppw);
+    // Enough pages for two chunks of 8 per workgroup at about
+    // ABS_DECODE_PIPE_WGS workgroups (two per compute unit): stream them
+    // double-buffered instead.
+    if (ABS_DECODE_PIPE_WGS > 0 && heads * maxp >= (int64_t)ABS_DECODE_PIPE_WGS * 16) {
+        const int64_t per = ceil_div64(heads * maxp, ABS_DECODE_PIPE_WGS);
+        l.chunk = 8;
+        l.pipelined = true;
+        l.ppw = (int)std::min<int64_t>(absk::kMaxPagesPerWg, std::max<int64_t>(16, ceil_div64(per, 16) * 16));
+        l.splits = (int)ceil_div64(maxp, l.ppw);
+    }
     const size_t rows = (size_t)p.g.B * p.g.Hq * l.splits;
     l.ml = 0;
     l.o = align_up(rows * 2 * sizeof(float));
@@ -339,6 +353,7 @@ abs_status abs_sparse_decode(const abs_paged_kv* kv, const abs_block_map* map, c
     a.part_o = reinterpret_cast<float*>(ws_at(workspace, l.o));
     a.pages_per_wg = l.ppw;
     a.chunk = l.chunk;
+    a.pipelined = l.pipelined;
     a.splits = l.splits;
     return hip_status(absk::launch_decode(p.g, p.dt, a, static_cast<hipStream_t>(stream)), "sparse_decode");
 }

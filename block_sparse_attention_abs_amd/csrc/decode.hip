@@ -12,11 +12,12 @@
 //         q.k is reduced over the 16 lanes of a DPP row; logits are kept in
 //         log2 units (q pre-scaled by sm_scale*log2 e).  The workgroup writes
 //         (m, l, o[D]) per query head to fp32 partials.
-// merge:  a second launch, one workgroup per (b, query head), merges the
-//         partials: M = max m_s, l = sum 2^(m_s-M) l_s,
-//         out = sum 2^(m_s-M) o_s / l, lse = (M + log2 l) * ln 2.
-//         (Merging inside the split launch would need an agent-scope release
-//         per workgroup, which on this GPU writes back the XCD's whole L2.)
+// merge:  a second launch, one workgroup per (b, query head): M = max m_s,
+//         l = sum 2^(m_s-M) l_s, out = sum 2^(m_s-M) o_s / l,
+//         lse = (M + log2 l) * ln 2.  (Merging in the split launch, in its
+//         last workgroup per (b, h), measured slower here: the partial stores
+//         must complete before the hand-off, and they queue behind the K/V
+//         reads; an agent-scope fence would write back the whole L2.)
 #include "device.hpp"
 
 namespace absk {
@@ -27,13 +28,14 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 // Waves per SIMD the split kernel is compiled for: 4 (all of a typical
 // grid resident at once) unless the group or the row width needs more registers.
-template <typename T, int D, int GT>
+// (PIPE: two chunks of K/V in registers at once.)
+template <typename T, int D, int GT, bool PIPE>
 struct DecodeOccupancy {
-    static constexpr int value = (GT >= 8 || D * (int)sizeof(T) > 256) ? 2 : 4;
+    static constexpr int value = (PIPE || GT >= 8 || D * (int)sizeof(T) > 256) ? 2 : 4;
 };
 
-template <typename T, int D, int GT, int CH>
-__global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT>::value)) void k_sparse_decode(Geom g, const T* __restrict__ q,
+template <typename T, int D, int GT, int CH, bool PIPE>
+__global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT, PIPE>::value)) void k_sparse_decode(Geom g, const T* __restrict__ q,
                                                           const int32_t* __restrict__ sel, int sel_cap,
                                                           const int32_t* __restrict__ count, float qscale,
                                                           float* __restrict__ part_ml, float* __restrict__ part_o,
@@ -103,32 +105,31 @@ __global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT>::value)) void k_spa
         const T* kc = reinterpret_cast<const T*>(g.k);
         const T* vc = reinterpret_cast<const T*>(g.v);
         const uint32_t lane_off = (uint32_t)((row * D + lane * VEC) * sizeof(T));
-        for (int c0 = 0; c0 < ppw; c0 += CH) {
-            if (__builtin_amdgcn_readlane(ph, c0) < 0) break;      // rest of the list is empty
-            int phys[CH], tok0[CH];
+        // issue every K and V load of the chunk of CH pages starting at c0
+        auto issue = [&](int c0, Words<NW>(&kw)[CH], Words<NW>(&vw)[CH]) {
 #pragma unroll
-            for (int i = 0; i < CH; ++i) {
-                phys[i] = __builtin_amdgcn_readlane(ph, c0 + i);
-                tok0[i] = __builtin_amdgcn_readlane(lp, c0 + i) * kPage;
-            }
-            // every K and V load of the chunk is in flight before any math
-            Words<NW> kw[CH], vw[CH];
-#pragma unroll
-            for (int i = 0; i < CH; ++i) {   // branch-free: empty slots re-read page 0 and are masked below
-                const int64_t base = ((int64_t)(phys[i] >= 0 ? phys[i] : 0) * g.Hkv + h) * (kPage * D);
+            for (int i = 0; i < CH; ++i) {   // branch-free: empty slots re-read page 0 and are masked later
+                const int pg = __builtin_amdgcn_readlane(ph, c0 + i);
+                const int64_t base = ((int64_t)(pg >= 0 ? pg : 0) * g.Hkv + h) * (kPage * D);
                 kw[i] = load_words_at<NW>(kc + base, lane_off);
             }
 #pragma unroll
             for (int i = 0; i < CH; ++i) {
-                const int64_t base = ((int64_t)(phys[i] >= 0 ? phys[i] : 0) * g.Hkv + h) * (kPage * D);
+                const int pg = __builtin_amdgcn_readlane(ph, c0 + i);
+                const int64_t base = ((int64_t)(pg >= 0 ? pg : 0) * g.Hkv + h) * (kPage * D);
                 vw[i] = load_words_at<NW>(vc + base, lane_off);
             }
+        };
+        // fold the chunk at c0 into this row's running (m, l, o)
+        auto consume = [&](int c0, const Words<NW>(&kw)[CH], const Words<NW>(&vw)[CH]) {
             float sc[CH][GT], cm[GT];
 #pragma unroll
             for (int gg = 0; gg < GT; ++gg) cm[gg] = m[gg];
 #pragma unroll
             for (int i = 0; i < CH; ++i) {
-                const bool valid = phys[i] >= 0 && tok0[i] + row < L;
+                const int pg = __builtin_amdgcn_readlane(ph, c0 + i);
+                const int t0 = __builtin_amdgcn_readlane(lp, c0 + i) * kPage;
+                const bool valid = pg >= 0 && t0 + row < L;
 #pragma unroll
                 for (int gg = 0; gg < GT; ++gg) {
                     const float z = row16_sum(dot_words<T, NW>(qw[gg], kw[i])) * qscale;
@@ -158,6 +159,28 @@ __global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT>::value)) void k_spa
 #pragma unroll
                     for (int gg = 0; gg < GT; ++gg) o[gg][e] = fmaf(p[gg], v, o[gg][e]);
                 }
+            }
+        };
+        auto has_chunk = [&](int c0) { return c0 < ppw && __builtin_amdgcn_readlane(ph, c0) >= 0; };
+        if constexpr (PIPE) {
+            // double-buffered: the next chunk's loads are in flight while this one is folded
+            Words<NW> ka[CH], va[CH], kb[CH], vb[CH];
+            issue(0, ka, va);
+            for (int c0 = 0;; c0 += 2 * CH) {
+                const bool nb = has_chunk(c0 + CH);
+                if (nb) issue(c0 + CH, kb, vb);
+                consume(c0, ka, va);
+                if (!nb) break;
+                const bool na = has_chunk(c0 + 2 * CH);
+                if (na) issue(c0 + 2 * CH, ka, va);
+                consume(c0 + CH, kb, vb);
+                if (!na) break;
+            }
+        } else {
+            for (int c0 = 0; has_chunk(c0); c0 += CH) {
+                Words<NW> kw[CH], vw[CH];
+                issue(c0, kw, vw);
+                consume(c0, kw, vw);
             }
         }
 
@@ -273,14 +296,18 @@ hipError_t decode_gt(const Geom& g, const DecodeArgs& a, hipStream_t s) {
     const float qscale = a.sm_scale * kLog2e;
     const T* q = reinterpret_cast<const T*>(a.q);
     T* out = reinterpret_cast<T*>(a.out);
-#define ABS_DECODE(CH_)                                                                                      \
-    hipLaunchKernelGGL((k_sparse_decode<T, D, GT, CH_>), grid, dim3(256), 0, s, g, q, a.sel, a.sel_cap,  \
-                       a.count, qscale, a.part_ml, a.part_o, a.splits, a.pages_per_wg)
-    switch (a.chunk) {
-        case 1: ABS_DECODE(1); break;
-        case 2: ABS_DECODE(2); break;
-        case 4: ABS_DECODE(4); break;
-        default: ABS_DECODE(8); break;
+#define ABS_DECODE(CH_, PIPE_)                                                                              \
+    hipLaunchKernelGGL((k_sparse_decode<T, D, GT, CH_, PIPE_>), grid, dim3(256), 0, s, g, q, a.sel,         \
+                       a.sel_cap, a.count, qscale, a.part_ml, a.part_o, a.splits, a.pages_per_wg)
+    if (a.pipelined) {
+        ABS_DECODE(8, true);
+    } else {
+        switch (a.chunk) {
+            case 1: ABS_DECODE(1, false); break;
+            case 2: ABS_DECODE(2, false); break;
+            case 4: ABS_DECODE(4, false); break;
+            default: ABS_DECODE(8, false); break;
+        }
     }
 #undef ABS_DECODE
     hipLaunchKernelGGL((k_decode_merge<T, D>), dim3(g.B * g.Hq), dim3(256), 0, s, g, a.count, a.sel_cap,

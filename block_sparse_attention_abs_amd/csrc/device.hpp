@@ -164,22 +164,71 @@ __device__ __forceinline__ float row16_max(float v) {
     return v;
 }
 
-// Combine the four rows of a wavefront (lanes l, l^16, l^32, l^48).
+// Combine the four 16-lane rows of a wavefront (lanes l, l^16, l^32, l^48)
+// with the gfx950 row swaps: v_permlane16_swap exchanges rows 0<->1 and
+// 2<->3 between its two operands and v_permlane32_swap the two halves, so
+// after a swap of (v, v) every lane holds {own value, partner's value}.
+__device__ __forceinline__ float swap16_other_plus(float v, bool is_max) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+    return is_max ? fmaxf(a, b) : a + b;
+}
+
+__device__ __forceinline__ float swap32_other_plus(float v, bool is_max) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+    return is_max ? fmaxf(a, b) : a + b;
+}
+
 __device__ __forceinline__ float rows4_sum(float v) {
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
+    return swap32_other_plus(swap16_other_plus(v, false), false);
 }
 
 __device__ __forceinline__ float rows4_max(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
+    return swap32_other_plus(swap16_other_plus(v, true), true);
 }
 
 __device__ __forceinline__ float rows4_min(float v) {
-    v = fminf(v, __shfl_xor(v, 16));
-    v = fminf(v, __shfl_xor(v, 32));
+    return -rows4_max(-v);
+}
+
+// Whole-wavefront max (every lane gets it): DPP within rows, row swaps across.
+__device__ __forceinline__ float wave_max(float v) { return rows4_max(row16_max(v)); }
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);   // out-of-row lanes read 0
+}
+
+// Inclusive prefix sum over the 64 lanes: row_shr 1/2/4/8 inside each
+// 16-lane row, then the totals of the rows below are added (readlane).
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+    x += dpp_u32<0x111>(x);   // row_shr:1
+    x += dpp_u32<0x112>(x);   // row_shr:2
+    x += dpp_u32<0x114>(x);   // row_shr:4
+    x += dpp_u32<0x118>(x);   // row_shr:8
+    const uint32_t t0 = __builtin_amdgcn_readlane(x, 15);
+    const uint32_t t1 = t0 + __builtin_amdgcn_readlane(x, 31);
+    const uint32_t t2 = t1 + __builtin_amdgcn_readlane(x, 47);
+    const int row = (threadIdx.x & 63) >> 4;
+    return x + (row == 1 ? t0 : row == 2 ? t1 : row == 3 ? t2 : 0u);
+}
+
+// Sum over aligned groups of N lanes (N = 2 or 4), fp64: both halves of the
+// double move with quad_perm DPP ([1,0,3,2], then [2,3,0,1] for N = 4).
+template <int N>
+__device__ __forceinline__ double lanes_sum_f64(double v) {
+    static_assert(N == 2 || N == 4, "pairs or quads");
+#pragma unroll
+    for (int step = 0; step < (N == 4 ? 2 : 1); ++step) {
+        const uint64_t u = __double_as_longlong(v);
+        const int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
+        const int lo2 = step == 0 ? __builtin_amdgcn_mov_dpp(lo, 0xB1, 0xF, 0xF, true)
+                                  : __builtin_amdgcn_mov_dpp(lo, 0x4E, 0xF, 0xF, true);
+        const int hi2 = step == 0 ? __builtin_amdgcn_mov_dpp(hi, 0xB1, 0xF, 0xF, true)
+                                  : __builtin_amdgcn_mov_dpp(hi, 0x4E, 0xF, 0xF, true);
+        v += __longlong_as_double((int64_t)(((uint64_t)(uint32_t)hi2 << 32) | (uint32_t)lo2));
+    }
     return v;
 }
 

@@ -71,6 +71,7 @@ struct DecodeArgs {
     float* part_o;    // [B*Hq][splits][D]
     int pages_per_wg; // <= kMaxPagesPerWg, a multiple of chunk
     int chunk;        // pages held in registers at a time: 1, 2, 4 or 8
+    bool pipelined;   // two chunks in flight (chunk 8, pages_per_wg a multiple of 16)
     int splits;
 };
 

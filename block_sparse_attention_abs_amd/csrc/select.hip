@@ -31,7 +31,7 @@
 namespace absk {
 namespace {
 
-template <typename T, int D>
+template <typename T, int D, int GT>
 __global__ __launch_bounds__(256) void k_score(Geom g, const uint8_t* __restrict__ codes,
                                                const float* __restrict__ scale, const float* __restrict__ lo,
                                                const T* __restrict__ q, float* __restrict__ scores, int stride) {
@@ -49,33 +49,34 @@ __global__ __launch_bounds__(256) void k_score(Geom g, const uint8_t* __restrict
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
     if (j < N) v = *reinterpret_cast<const uint4*>(codes + (row0 + j) * (D / 2) + sub * 16);
 
-    __shared__ double w[D];
-    __shared__ double c0_part[D / 64 > 0 ? D / 64 : 1];
+    // per channel: w_d = qbar_d * scale_d and z_d = qbar_d * lo_d (fp64, LDS)
+    __shared__ double w[D], z[D];
     if (threadIdx.x < D) {
         const int d = threadIdx.x;
+        float qv[GT];
+#pragma unroll
+        for (int gg = 0; gg < GT; ++gg)
+            qv[gg] = Elem<T>::load1(q + ((int64_t)b * g.Hq + h * g.G + min(gg, g.G - 1)) * D + d);
+        const float sc = scale[(int64_t)bh * D + d], zp = lo[(int64_t)bh * D + d];
         double qbar = 0.0;
-        for (int gg = 0; gg < g.G; ++gg)
-            qbar += (double)Elem<T>::load1(q + ((int64_t)b * g.Hq + h * g.G + gg) * D + d);
-        w[d] = qbar * (double)scale[(int64_t)bh * D + d];
-        double part = qbar * (double)lo[(int64_t)bh * D + d];
-        for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
-        if ((d & 63) == 0) c0_part[d / 64] = part;
+#pragma unroll
+        for (int gg = 0; gg < GT; ++gg) qbar += gg < g.G ? (double)qv[gg] : 0.0;
+        w[d] = qbar * (double)sc;
+        z[d] = qbar * (double)zp;
     }
     __syncthreads();
-    double c0 = 0.0;
-#pragma unroll
-    for (int i = 0; i < D / 64; ++i) c0 += c0_part[i];
 
+    // this lane's 32 channels: sum_d (w_d * code_d + z_d); the lanes of a block then add up
     const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
     const double* ws = w + sub * 32;
+    const double* zs = z + sub * 32;
     double acc = 0.0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int n = 0; n < 8; ++n) acc += ws[i * 8 + n] * (double)((wd[i] >> (4 * n)) & 15u);
-#pragma unroll
-    for (int off = 1; off < LPB; off <<= 1) acc += __shfl_xor(acc, off);
-    if (j < N && sub == 0) scores[(int64_t)bh * stride + j] = (float)(c0 + acc);
+        for (int n = 0; n < 8; ++n) acc += ws[i * 8 + n] * (double)((wd[i] >> (4 * n)) & 15u) + zs[i * 8 + n];
+    acc = lanes_sum_f64<LPB>(acc);
+    if (j < N && sub == 0) scores[(int64_t)bh * stride + j] = (float)acc;
 }
 
 // Order-preserving map of a float to uint32 (larger float -> larger key);
@@ -94,12 +95,7 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
+    const uint32_t x = wave_inclusive_scan(v);
     if (lane == 63) s_wave[wave] = x;
     __syncthreads();
     uint32_t before = 0, all = 0;
@@ -116,8 +112,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
 
 template <int NT>
 __device__ __forceinline__ float block_max(float v, float* s_wave) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    v = wave_max(v);
     if ((threadIdx.x & 63) == 0) s_wave[threadIdx.x >> 6] = v;
     __syncthreads();
     float r = s_wave[0];
@@ -271,12 +266,7 @@ __global__ __launch_bounds__(NT) void k_topk(Geom g, const float* __restrict__ s
 #pragma unroll
                 for (int i = 0; i < 4; ++i) c[i] = hist[255 - 4 * lane - i];
                 const uint32_t mine = c[0] + c[1] + c[2] + c[3];
-                uint32_t incl = mine;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const uint32_t y = __shfl_up(incl, off);
-                    if (lane >= off) incl += y;
-                }
+                const uint32_t incl = wave_inclusive_scan(mine);
                 const uint32_t excl = incl - mine;
                 if (excl < need && need <= incl) {
                     uint32_t above = excl;
@@ -332,8 +322,15 @@ template <typename T, int D>
 hipError_t select_impl(const Geom& g, const SelectArgs& a, hipStream_t s) {
     constexpr int BPW = 256 / (D / 32);
     const dim3 sgrid(ceil_div(a.max_n, BPW), g.B * g.Hkv);
-    hipLaunchKernelGGL((k_score<T, D>), sgrid, dim3(256), 0, s, g, a.codes, a.scale, a.lo,
-                       reinterpret_cast<const T*>(a.q), a.scores, a.stride);
+    const T* q = reinterpret_cast<const T*>(a.q);
+    if (g.G <= 1)
+        hipLaunchKernelGGL((k_score<T, D, 1>), sgrid, dim3(256), 0, s, g, a.codes, a.scale, a.lo, q, a.scores, a.stride);
+    else if (g.G <= 2)
+        hipLaunchKernelGGL((k_score<T, D, 2>), sgrid, dim3(256), 0, s, g, a.codes, a.scale, a.lo, q, a.scores, a.stride);
+    else if (g.G <= 4)
+        hipLaunchKernelGGL((k_score<T, D, 4>), sgrid, dim3(256), 0, s, g, a.codes, a.scale, a.lo, q, a.scores, a.stride);
+    else
+        hipLaunchKernelGGL((k_score<T, D, 8>), sgrid, dim3(256), 0, s, g, a.codes, a.scale, a.lo, q, a.scores, a.stride);
     const dim3 tgrid(g.B * g.Hkv);
 #define ABS_TOPK(NT_, KPT_)                                                                                  \
     hipLaunchKernelGGL((k_topk<NT_, KPT_>), tgrid, dim3(NT_), 0, s, g, a.scores, a.stride, a.budget, a.sel, \

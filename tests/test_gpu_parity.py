@@ -181,3 +181,27 @@ def test_full_size_sampled(oracle_mod, cfg):
         check_attention(r.out[b:b + 1], r.lse[b:b + 1], out, lse, x.dtype)
     del g
     torch.cuda.empty_cache()
+
+
+def test_decode_repeats_bit_identical():
+    """Split partials are handed to the merge launch through the workspace;
+    the merge order is fixed, so 200 back-to-back calls on one workspace
+    must agree bit for bit."""
+    from block_sparse_attention_abs_amd import abs as A
+    w = P[2].scaled(batch=4, context=16384)
+    x = W.make_layer(w)
+    g = GpuLayer(x)
+    g.build()
+    sel, cnt = g.select(w.token_budget)
+    sm = default_scale(w.head_dim)
+    B, Hq, D = x.q.shape
+    ws = A.workspace(g.kv.workspace_bytes(w.token_budget, A.ABS_OP_DECODE))
+    outs = []
+    for _ in range(200):
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+        A.sparse_decode(g.kv, g.q, sel, cnt, w.token_budget, sm, out, ws=ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    ref = outs[0].view(torch.int16)
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), ref)
