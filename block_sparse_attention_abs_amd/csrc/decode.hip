@@ -24,18 +24,46 @@ namespace absk {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// 2^x by the hardware's exp2 (v_exp_f32, about 1 ulp); -inf gives 0.  The
+// arguments here are <= 0 and results below 2^-126 only weigh tokens that
+// are negligible next to the row maximum (weight 1).
+__device__ __forceinline__ float exp2_approx(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr float kLn2 = 0.6931471805599453f;
 
 // Waves per SIMD the split kernel is compiled for: 4 (all of a typical
 // grid resident at once) unless the group or the row width needs more registers.
-// (PIPE: two chunks of K/V in registers at once.)
-template <typename T, int D, int GT, bool PIPE>
+// (PIPE: two chunks of K/V in registers at once; MF: the query in the A-operand
+// layout as well.)
+template <typename T, int D, int GT, bool PIPE, bool MF>
 struct DecodeOccupancy {
-    static constexpr int value = (PIPE || GT >= 8 || D * (int)sizeof(T) > 256) ? 2 : 4;
+    static constexpr int value = (PIPE || GT >= 8 || D * (int)sizeof(T) > 256) ? 2
+                                 : (MF && GT >= 4 && D * (int)sizeof(T) >= 256) ? 3
+                                                                                : 4;
 };
 
-template <typename T, int D, int GT, int CH, bool PIPE>
-__global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT, PIPE>::value)) void k_sparse_decode(Geom g, const T* __restrict__ q,
+// The double-buffered form fits the register file (no spills) only for
+// 2-byte elements and up to 4 query heads per group at D = 128.
+template <typename T, int D, int GT>
+constexpr bool kPipeFits = sizeof(T) == 2 && (D == 64 || GT <= 4);
+
+// Build-time switch: 0 keeps q.k on the vector ALUs for bf16 as well.
+#ifndef ABS_DECODE_MATRIX
+#define ABS_DECODE_MATRIX 1
+#endif
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// MF: q.k on the matrix cores (bf16 only, CH == 8).  Each wavefront owns two
+// pages of a chunk and loads their K in the B-operand layout of
+// v_mfma_f32_16x16x32_bf16 (lane l: token l%16, channels 8*(l/16)..+7 of the
+// step's 32, so a step reads 64 contiguous bytes of each key row).  The query
+// rows of the A operand are the group's heads repeated 4x, so lane l receives
+// S[head][token l%16] for all heads.  The scores go through LDS (one barrier
+// per chunk, double-buffered) to the row layout the V side uses.
+template <typename T, int D, int GT, int CH, bool PIPE, bool MF>
+__global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT, PIPE, MF>::value)) void k_sparse_decode(Geom g, const T* __restrict__ q,
                                                           const int32_t* __restrict__ sel, int sel_cap,
                                                           const int32_t* __restrict__ count, float qscale,
                                                           float* __restrict__ part_ml, float* __restrict__ part_o,
@@ -51,12 +79,29 @@ __global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT, PIPE>::value)) void
     const int wave = threadIdx.x / 64;
     const int wl = threadIdx.x & 63;
 
-    // The group's queries (raw storage words): independent of everything else, so issued first.
-    Words<NW> qw[GT];
+    constexpr int KSTEPS = D / 32;                       // MFMA k-steps per key row
+    constexpr int GP = (GT + 3) / 4;                     // MFMA passes (4 heads each)
+    constexpr int KW = MF ? 2 * KSTEPS : CH;             // K words held per chunk
+    static_assert(!MF || (CH == 8 && sizeof(T) == 2), "matrix-core path: bf16, 8-page chunks");
+
+    // The group's queries: independent of everything else, so issued first.
+    Words<NW> qw[MF ? 1 : GT];
+    Words<4> qa[MF ? GP : 1][MF ? KSTEPS : 1];
+    if constexpr (MF) {
+        const int m4 = (wl & 15) & 3;
 #pragma unroll
-    for (int gg = 0; gg < GT; ++gg) {
-        const int head = h * g.G + min(gg, g.G - 1);
-        qw[gg] = load_words<NW>(q + ((int64_t)b * g.Hq + head) * D + lane * VEC);
+        for (int pp = 0; pp < GP; ++pp) {
+            const int head = h * g.G + min(4 * pp + m4, g.G - 1);
+#pragma unroll
+            for (int st = 0; st < KSTEPS; ++st)
+                qa[pp][st] = load_words<4>(q + ((int64_t)b * g.Hq + head) * D + st * 32 + (wl >> 4) * 8);
+        }
+    } else {
+#pragma unroll
+        for (int gg = 0; gg < GT; ++gg) {
+            const int head = h * g.G + min(gg, g.G - 1);
+            qw[gg] = load_words<NW>(q + ((int64_t)b * g.Hq + head) * D + lane * VEC);
+        }
     }
 
     const int L = g.seq_lens[b];
@@ -87,7 +132,11 @@ __global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT, PIPE>::value)) void
     }
 
     __shared__ float s_red[4][GT];
-    __shared__ float s_o[4][GT][D];
+    constexpr int kRows = 256 / kRowLanes;
+    __shared__ __align__(16) float s_o[kRows][GT][D];   // epilogue: each row's rescaled output
+    __shared__ float s_l[kRows][GT];
+    __shared__ float s_sc[MF ? 2 : 1][MF ? CH : 1][MF ? 16 : 1][GT];   // MF: scores, double-buffered per chunk
+    int sbuf = 0;
 
     // Per-row running softmax state (each row of 16 lanes sees one token per page).
     float m[GT], l[GT], o[GT][VEC];
@@ -106,12 +155,25 @@ __global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT, PIPE>::value)) void
         const T* vc = reinterpret_cast<const T*>(g.v);
         const uint32_t lane_off = (uint32_t)((row * D + lane * VEC) * sizeof(T));
         // issue every K and V load of the chunk of CH pages starting at c0
-        auto issue = [&](int c0, Words<NW>(&kw)[CH], Words<NW>(&vw)[CH]) {
+        auto issue = [&](int c0, Words<MF ? 4 : NW>(&kw)[KW], Words<NW>(&vw)[CH]) {
+            if constexpr (MF) {
+                // this wavefront's two pages, B-operand layout
+                const uint32_t k_off = (uint32_t)(((wl & 15) * D + (wl >> 4) * 8) * sizeof(T));
 #pragma unroll
-            for (int i = 0; i < CH; ++i) {   // branch-free: empty slots re-read page 0 and are masked later
-                const int pg = __builtin_amdgcn_readlane(ph, c0 + i);
-                const int64_t base = ((int64_t)(pg >= 0 ? pg : 0) * g.Hkv + h) * (kPage * D);
-                kw[i] = load_words_at<NW>(kc + base, lane_off);
+                for (int j = 0; j < 2; ++j) {
+                    const int pg = __builtin_amdgcn_readlane(ph, c0 + wave + 4 * j);
+                    const int64_t base = ((int64_t)(pg >= 0 ? pg : 0) * g.Hkv + h) * (kPage * D);
+#pragma unroll
+                    for (int st = 0; st < KSTEPS; ++st)
+                        kw[j * KSTEPS + st] = load_words_at<4>(kc + base + st * 32, k_off);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < CH; ++i) {   // branch-free: empty slots re-read page 0 and are masked later
+                    const int pg = __builtin_amdgcn_readlane(ph, c0 + i);
+                    const int64_t base = ((int64_t)(pg >= 0 ? pg : 0) * g.Hkv + h) * (kPage * D);
+                    kw[i] = load_words_at<NW>(kc + base, lane_off);
+                }
             }
 #pragma unroll
             for (int i = 0; i < CH; ++i) {
@@ -121,25 +183,63 @@ __global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT, PIPE>::value)) void
             }
         };
         // fold the chunk at c0 into this row's running (m, l, o)
-        auto consume = [&](int c0, const Words<NW>(&kw)[CH], const Words<NW>(&vw)[CH]) {
+        auto consume = [&](int c0, const Words<MF ? 4 : NW>(&kw)[KW], const Words<NW>(&vw)[CH]) {
             float sc[CH][GT], cm[GT];
 #pragma unroll
             for (int gg = 0; gg < GT; ++gg) cm[gg] = m[gg];
+            if constexpr (MF) {
 #pragma unroll
-            for (int i = 0; i < CH; ++i) {
-                const int pg = __builtin_amdgcn_readlane(ph, c0 + i);
-                const int t0 = __builtin_amdgcn_readlane(lp, c0 + i) * kPage;
-                const bool valid = pg >= 0 && t0 + row < L;
+                for (int j = 0; j < 2; ++j) {
+                    const int pi = wave + 4 * j;
+                    const int pg = __builtin_amdgcn_readlane(ph, c0 + pi);
+                    const int t0 = __builtin_amdgcn_readlane(lp, c0 + pi) * kPage;
+                    const bool valid = pg >= 0 && t0 + (wl & 15) < L;
 #pragma unroll
-                for (int gg = 0; gg < GT; ++gg) {
-                    const float z = row16_sum(dot_words<T, NW>(qw[gg], kw[i])) * qscale;
-                    sc[i][gg] = valid ? z : NEG;
-                    cm[gg] = fmaxf(cm[gg], sc[i][gg]);
+                    for (int pp = 0; pp < GP; ++pp) {
+                        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                        for (int st = 0; st < KSTEPS; ++st)
+                            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8_t, qa[pp][st]), __builtin_bit_cast(bf16x8_t, kw[j * KSTEPS + st]),
+                                acc, 0, 0, 0);
+                        if (wl < 16) {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                if (4 * pp + i < GT) s_sc[sbuf][pi][wl][4 * pp + i] = valid ? acc[i] * qscale : NEG;
+                        }
+                    }
+                }
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < CH; ++i)
+#pragma unroll
+                    for (int gg = 0; gg < GT; ++gg) {
+                        sc[i][gg] = s_sc[sbuf][i][row][gg];
+                        cm[gg] = fmaxf(cm[gg], sc[i][gg]);
+                    }
+                sbuf ^= 1;
+            } else {
+#pragma unroll
+                for (int i = 0; i < CH; ++i) {
+                    const int pg = __builtin_amdgcn_readlane(ph, c0 + i);
+                    const int t0 = __builtin_amdgcn_readlane(lp, c0 + i) * kPage;
+                    const bool valid = pg >= 0 && t0 + row < L;
+#pragma unroll
+                    for (int gg = 0; gg < GT; ++gg) {
+                        const float z = row16_sum(dot_words<T, NW>(qw[gg], kw[i])) * qscale;
+                        sc[i][gg] = valid ? z : NEG;
+                        cm[gg] = fmaxf(cm[gg], sc[i][gg]);
+                    }
                 }
             }
+            // Exponents are taken against ms, the new running max, or 0 while a
+            // row has seen no valid token: exp2(-inf) = 0 then covers masked
+            // tokens and the empty state (l = o = 0) without further tests.
+            float ms[GT];
 #pragma unroll
             for (int gg = 0; gg < GT; ++gg) {
-                const float alpha = cm[gg] == NEG ? 1.0f : exp2f(m[gg] - cm[gg]);
+                ms[gg] = cm[gg] == NEG ? 0.0f : cm[gg];
+                const float alpha = exp2_approx(m[gg] - ms[gg]);
                 m[gg] = cm[gg];
                 l[gg] *= alpha;
 #pragma unroll
@@ -150,7 +250,7 @@ __global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT, PIPE>::value)) void
                 float p[GT];
 #pragma unroll
                 for (int gg = 0; gg < GT; ++gg) {
-                    p[gg] = sc[i][gg] == NEG ? 0.0f : exp2f(sc[i][gg] - m[gg]);
+                    p[gg] = exp2_approx(sc[i][gg] - ms[gg]);
                     l[gg] += p[gg];
                 }
 #pragma unroll
@@ -164,7 +264,8 @@ __global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT, PIPE>::value)) void
         auto has_chunk = [&](int c0) { return c0 < ppw && __builtin_amdgcn_readlane(ph, c0) >= 0; };
         if constexpr (PIPE) {
             // double-buffered: the next chunk's loads are in flight while this one is folded
-            Words<NW> ka[CH], va[CH], kb[CH], vb[CH];
+            Words<MF ? 4 : NW> ka[KW], kb[KW];
+            Words<NW> va[CH], vb[CH];
             issue(0, ka, va);
             for (int c0 = 0;; c0 += 2 * CH) {
                 const bool nb = has_chunk(c0 + CH);
@@ -178,14 +279,16 @@ __global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT, PIPE>::value)) void
             }
         } else {
             for (int c0 = 0; has_chunk(c0); c0 += CH) {
-                Words<NW> kw[CH], vw[CH];
+                Words<MF ? 4 : NW> kw[KW];
+                Words<NW> vw[CH];
                 issue(c0, kw, vw);
                 consume(c0, kw, vw);
             }
         }
 
-        // rows -> workgroup: common max, rescale, sum (shuffles within a
-        // wavefront, LDS across the four wavefronts)
+        // rows -> workgroup: the common max (shuffles within a wavefront, LDS
+        // across the four), then each row's rescaled state goes to LDS and
+        // every thread sums two channels over the 16 rows.
         float M[GT];
 #pragma unroll
         for (int gg = 0; gg < GT; ++gg) M[gg] = rows4_max(m[gg]);
@@ -196,29 +299,32 @@ __global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT, PIPE>::value)) void
 #pragma unroll
         for (int gg = 0; gg < GT; ++gg) {
             M[gg] = fmaxf(fmaxf(s_red[0][gg], s_red[1][gg]), fmaxf(s_red[2][gg], s_red[3][gg]));
-            const float f = m[gg] == NEG ? 0.0f : exp2f(m[gg] - M[gg]);
-            l[gg] = rows4_sum(l[gg] * f);
+            const float f = m[gg] == NEG ? 0.0f : exp2_approx(m[gg] - M[gg]);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) o[gg][e] = rows4_sum(o[gg][e] * f);
+            for (int e = 0; e < VEC; e += 4)
+                *reinterpret_cast<float4*>(&s_o[row][gg][lane * VEC + e]) =
+                    make_float4(o[gg][e] * f, o[gg][e + 1] * f, o[gg][e + 2] * f, o[gg][e + 3] * f);
+            if (lane == 0) s_l[row][gg] = l[gg] * f;
         }
         __syncthreads();
-        if (wl < kRowLanes) {
-#pragma unroll
-            for (int gg = 0; gg < GT; ++gg) {
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) s_o[wave][gg][lane * VEC + e] = o[gg][e];
-                if (lane == 0) s_red[wave][gg] = l[gg];
-            }
-        }
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < GT * D; idx += blockDim.x) {
+        for (int idx = 2 * (int)threadIdx.x; idx < GT * D; idx += 2 * (int)blockDim.x) {
             const int gg = idx / D, d = idx - gg * D;
             if (gg >= g.G) continue;
+            float2 acc = make_float2(0.0f, 0.0f);
+#pragma unroll
+            for (int r = 0; r < kRows; ++r) {
+                const float2 v = *reinterpret_cast<const float2*>(&s_o[r][gg][d]);
+                acc.x += v.x;
+                acc.y += v.y;
+            }
             const int64_t prow = ((int64_t)b * g.Hq + h * g.G + gg) * splits + split;
-            part_o[prow * D + d] = s_o[0][gg][d] + s_o[1][gg][d] + s_o[2][gg][d] + s_o[3][gg][d];
+            *reinterpret_cast<float2*>(part_o + prow * D + d) = acc;
             if (d == 0) {
-                part_ml[prow * 2 + 0] = M[gg];
-                part_ml[prow * 2 + 1] = s_red[0][gg] + s_red[1][gg] + s_red[2][gg] + s_red[3][gg];
+                float ls = 0.0f;
+#pragma unroll
+                for (int r = 0; r < kRows; ++r) ls += s_l[r][gg];
+                part_ml[prow * 2 + 0] = fmaxf(fmaxf(s_red[0][gg], s_red[1][gg]), fmaxf(s_red[2][gg], s_red[3][gg]));
+                part_ml[prow * 2 + 1] = ls;
             }
         }
     } else if (p0 < total) {
@@ -296,17 +402,22 @@ hipError_t decode_gt(const Geom& g, const DecodeArgs& a, hipStream_t s) {
     const float qscale = a.sm_scale * kLog2e;
     const T* q = reinterpret_cast<const T*>(a.q);
     T* out = reinterpret_cast<T*>(a.out);
-#define ABS_DECODE(CH_, PIPE_)                                                                              \
-    hipLaunchKernelGGL((k_sparse_decode<T, D, GT, CH_, PIPE_>), grid, dim3(256), 0, s, g, q, a.sel,         \
+#define ABS_DECODE(CH_, PIPE_, MF_)                                                                         \
+    hipLaunchKernelGGL((k_sparse_decode<T, D, GT, CH_, PIPE_, MF_>), grid, dim3(256), 0, s, g, q, a.sel,    \
                        a.sel_cap, a.count, qscale, a.part_ml, a.part_o, a.splits, a.pages_per_wg)
-    if (a.pipelined) {
-        ABS_DECODE(8, true);
+    constexpr bool kMatrix = ABS_DECODE_MATRIX && sizeof(T) == 2;   // bf16: q.k on the matrix cores
+    // (a pipelined plan on a variant that does not fit runs the plain 8-page loop)
+    // (fp32 rows of 8 query heads at D = 128 hold at most 4 pages at once)
+    constexpr bool kWide = sizeof(T) == 4 && D * GT >= 1024;
+    if (a.pipelined && kPipeFits<T, D, GT>) {
+        if constexpr (kPipeFits<T, D, GT>) ABS_DECODE(8, true, kMatrix);
+    } else if ((a.chunk == 8 || a.pipelined) && !kWide) {
+        if constexpr (!kWide) ABS_DECODE(8, false, kMatrix);
     } else {
         switch (a.chunk) {
-            case 1: ABS_DECODE(1, false); break;
-            case 2: ABS_DECODE(2, false); break;
-            case 4: ABS_DECODE(4, false); break;
-            default: ABS_DECODE(8, false); break;
+            case 1: ABS_DECODE(1, false, false); break;
+            case 2: ABS_DECODE(2, false, false); break;
+            default: ABS_DECODE(4, false, false); break;
         }
     }
 #undef ABS_DECODE
