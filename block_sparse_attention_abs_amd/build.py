@@ -23,17 +23,17 @@ FLAGS = [
     # IEEE fp32 division/sqrt: the INT4 quantizer's codes depend on it
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Wall", "-Wno-unused-command-line-argument",
-    "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+    "-I", os.path.join(ROOT, "include"),
 ]
 
 
-def build(verbose: bool = False, out: str = LIB, defines=(), objdir: str = OBJ) -> str:
-    """Compile every source and link `out`; `defines` are extra -D tuning macros."""
+def build(verbose: bool = False, out: str = LIB, defines=(), objdir: str = OBJ, csrc: str = CSRC) -> str:
+    """Compile every source under `csrc` and link `out`; `defines` are extra -D tuning macros."""
     os.makedirs(objdir, exist_ok=True)
     procs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src + ".o")
-        cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, "-I", csrc, *[f"-D{d}" for d in defines], "-c", os.path.join(csrc, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
         procs.append((src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,

@@ -159,7 +159,7 @@ size_t select_bytes(const Plan& p) {
 struct DecodeLayout {
     int ppw = 8, chunk = 8, splits = 1;
     bool pipelined = false;
-    size_t ml = 0, o = 0, bytes = 0;
+    size_t arrive = 0, ml = 0, o = 0, bytes = 0;
 };
 
 // Build-time tuning of the decode launch (see decode_layout).
@@ -171,6 +171,10 @@ struct DecodeLayout {
 #endif
 #ifndef ABS_DECODE_PIPE_WGS
 #define ABS_DECODE_PIPE_WGS 256
+#endif
+// 1: the last split workgroup of each (b, h) merges (one launch); 0: a merge launch.
+#ifndef ABS_DECODE_FUSED_MERGE
+#define ABS_DECODE_FUSED_MERGE 1
 #endif
 
 // Pages per workgroup: enough workgroups to fill the chip (about
@@ -196,8 +200,9 @@ DecodeLayout decode_layout(const Plan& p) {
         l.splits = (int)ceil_div64(maxp, l.ppw);
     }
     const size_t rows = (size_t)p.g.B * p.g.Hq * l.splits;
-    l.ml = 0;
-    l.o = align_up(rows * 2 * sizeof(float));
+    l.arrive = 0;
+    l.ml = align_up((size_t)p.g.B * p.g.Hkv * sizeof(int32_t));
+    l.o = l.ml + align_up(rows * 2 * sizeof(float));
     l.bytes = l.o + align_up(rows * p.g.D * sizeof(float));
     return l;
 }
@@ -351,6 +356,7 @@ abs_status abs_sparse_decode(const abs_paged_kv* kv, const abs_block_map* map, c
     a.lse = lse;
     a.part_ml = reinterpret_cast<float*>(ws_at(workspace, l.ml));
     a.part_o = reinterpret_cast<float*>(ws_at(workspace, l.o));
+    a.arrive = ABS_DECODE_FUSED_MERGE ? reinterpret_cast<int32_t*>(ws_at(workspace, l.arrive)) : nullptr;
     a.pages_per_wg = l.ppw;
     a.chunk = l.chunk;
     a.pipelined = l.pipelined;

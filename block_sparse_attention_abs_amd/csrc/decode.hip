@@ -8,16 +8,20 @@
 //         head's selected pages for all G query heads of the group (the K/V
 //         page is read once for the group).  Lane (row r, lane c) of the
 //         16x16 layout holds channels [c*D/16, (c+1)*D/16) of token r of each
-//         page; every K and V load of the workgroup is issued before any math.
-//         q.k is reduced over the 16 lanes of a DPP row; logits are kept in
-//         log2 units (q pre-scaled by sm_scale*log2 e).  The workgroup writes
-//         (m, l, o[D]) per query head to fp32 partials.
-// merge:  a second launch, one workgroup per (b, query head): M = max m_s,
-//         l = sum 2^(m_s-M) l_s, out = sum 2^(m_s-M) o_s / l,
-//         lse = (M + log2 l) * ln 2.  (Merging in the split launch, in its
-//         last workgroup per (b, h), measured slower here: the partial stores
-//         must complete before the hand-off, and they queue behind the K/V
-//         reads; an agent-scope fence would write back the whole L2.)
+//         page for the V side; pages are streamed in chunks of up to 8, two
+//         chunks in flight when the workgroup has enough pages.  For bf16,
+//         q.k runs on the matrix cores (each wavefront owns two pages of a
+//         chunk); otherwise it is reduced over the 16 lanes of a DPP row.
+//         Logits are kept in log2 units (q pre-scaled by sm_scale*log2 e).
+//         The workgroup's (m, l, o[D]) per query head is its partial.
+// merge:  M = max m_s, l = sum 2^(m_s-M) l_s, out = sum 2^(m_s-M) o_s / l,
+//         lse = (M + log2 l) * ln 2.  Done in the split launch by the last
+//         workgroup to finish each (b, h): partials are written with
+//         agent-scope stores, an agent-scope counter per (b, h) finds the
+//         last arrival, which reads the partials with agent-scope loads (no
+//         L2 writeback is needed, unlike an agent-scope fence).  A build
+//         switch keeps the older form, a second launch with one workgroup
+//         per (b, query head).
 #include "device.hpp"
 
 namespace absk {
@@ -52,6 +56,28 @@ constexpr bool kPipeFits = sizeof(T) == 2 && (D == 64 || GT <= 4);
 #define ABS_DECODE_MATRIX 1
 #endif
 
+// Agent-scope (device-coherent) 8-byte store and load: relaxed atomics, which
+// write through and read past the per-XCD L2.
+__device__ __forceinline__ void store2_agent(float* p, float a, float b) {
+    const uint64_t u = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load2_agent(const float* p) {
+    const uint64_t u = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
+}
+
+// Final output of query row bi, channels d and d+1, from the merged state
+// (sum o, max m in log2 units, sum l).
+template <typename T>
+__device__ __forceinline__ void write_output(T* out, float* lse, int64_t bi, int d, float2 acc, float m, float l, int D) {
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    Elem<T>::store1(out + bi * D + d, acc.x * inv);
+    Elem<T>::store1(out + bi * D + d + 1, acc.y * inv);
+    if (lse != nullptr && d == 0) lse[bi] = l > 0.0f ? (m + log2f(l)) * kLn2 : -__builtin_inff();
+}
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -67,7 +93,8 @@ __global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT, PIPE, MF>::value)) 
                                                           const int32_t* __restrict__ sel, int sel_cap,
                                                           const int32_t* __restrict__ count, float qscale,
                                                           float* __restrict__ part_ml, float* __restrict__ part_o,
-                                                          int splits, int ppw) {
+                                                          int splits, int ppw, int32_t* __restrict__ arrive,
+                                                          T* __restrict__ out, float* __restrict__ lse) {
     constexpr int VEC = D / kRowLanes;
     constexpr int NW = VEC * Elem<T>::kBytes / 4;
     constexpr float NEG = -__builtin_inff();
@@ -307,31 +334,99 @@ __global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT, PIPE, MF>::value)) 
             if (lane == 0) s_l[row][gg] = l[gg] * f;
         }
         __syncthreads();
+    }
+
+    // This workgroup's share of (b, h), per (query head, channel pair): the
+    // row sums from LDS, or an empty partial (m = -inf) when the workgroup is
+    // in the selected range but all of its pages are empty.
+    const bool fused = arrive != nullptr;
+    const bool holds = p0 < total;                      // active implies holds
+    const int nact = ceil_div(total, ppw);              // workgroups holding pages of (b, h)
+    if (holds) {
         for (int idx = 2 * (int)threadIdx.x; idx < GT * D; idx += 2 * (int)blockDim.x) {
             const int gg = idx / D, d = idx - gg * D;
             if (gg >= g.G) continue;
             float2 acc = make_float2(0.0f, 0.0f);
+            float mg = NEG, ls = 0.0f;
+            if (active) {
 #pragma unroll
-            for (int r = 0; r < kRows; ++r) {
-                const float2 v = *reinterpret_cast<const float2*>(&s_o[r][gg][d]);
-                acc.x += v.x;
-                acc.y += v.y;
-            }
-            const int64_t prow = ((int64_t)b * g.Hq + h * g.G + gg) * splits + split;
-            *reinterpret_cast<float2*>(part_o + prow * D + d) = acc;
-            if (d == 0) {
-                float ls = 0.0f;
+                for (int r = 0; r < kRows; ++r) {
+                    const float2 v = *reinterpret_cast<const float2*>(&s_o[r][gg][d]);
+                    acc.x += v.x;
+                    acc.y += v.y;
+                }
 #pragma unroll
                 for (int r = 0; r < kRows; ++r) ls += s_l[r][gg];
-                part_ml[prow * 2 + 0] = fmaxf(fmaxf(s_red[0][gg], s_red[1][gg]), fmaxf(s_red[2][gg], s_red[3][gg]));
-                part_ml[prow * 2 + 1] = ls;
+                mg = fmaxf(fmaxf(s_red[0][gg], s_red[1][gg]), fmaxf(s_red[2][gg], s_red[3][gg]));
+            }
+            const int64_t bi = (int64_t)b * g.Hq + h * g.G + gg;
+            const int64_t prow = bi * splits + split;
+            if (fused && nact == 1) {
+                write_output(out, lse, bi, d, acc, mg, ls, D);        // the only workgroup of (b, h)
+            } else if (fused) {
+                store2_agent(part_o + prow * D + d, acc.x, acc.y);
+                if (d == 0) store2_agent(part_ml + prow * 2, mg, ls);
+            } else {
+                *reinterpret_cast<float2*>(part_o + prow * D + d) = acc;
+                if (d == 0) {
+                    part_ml[prow * 2 + 0] = mg;
+                    part_ml[prow * 2 + 1] = ls;
+                }
             }
         }
-    } else if (p0 < total) {
-        // in the merged range but every page of it is empty (the tail of a
-        // partial last block): an empty partial
-        for (int gg = threadIdx.x; gg < g.G; gg += blockDim.x)
-            part_ml[(((int64_t)b * g.Hq + h * g.G + gg) * splits + split) * 2] = NEG;
+    } else if (fused && total == 0 && split == 0) {
+        // nothing selected for (b, h): zero output, lse = -inf
+        for (int idx = 2 * (int)threadIdx.x; idx < GT * D; idx += 2 * (int)blockDim.x) {
+            const int gg = idx / D, d = idx - gg * D;
+            if (gg < g.G)
+                write_output(out, lse, (int64_t)b * g.Hq + h * g.G + gg, d, make_float2(0.0f, 0.0f), NEG, 0.0f, D);
+        }
+    }
+    if (!fused || !holds || nact == 1) return;
+
+    // Hand-off: partials are written with agent-scope (L2 write-through)
+    // stores; once every thread's stores have completed, one agent-scope
+    // atomic counts the arrival.  The last of the nact workgroups resets the
+    // counter for the next call and merges, reading with agent-scope loads.
+    __shared__ int s_last;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int prev = __hip_atomic_fetch_add(arrive + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = prev == nact - 1;
+        if (prev == nact - 1) __hip_atomic_store(arrive + bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    for (int idx = 2 * (int)threadIdx.x; idx < GT * D; idx += 2 * (int)blockDim.x) {
+        const int gg = idx / D, d = idx - gg * D;
+        if (gg >= g.G) continue;
+        const int64_t bi = (int64_t)b * g.Hq + h * g.G + gg;
+        const float* ml = part_ml + bi * splits * 2;
+        const float* po = part_o + bi * splits * D + d;
+        float mg = NEG, ls = 0.0f;
+        float2 acc = make_float2(0.0f, 0.0f);
+        for (int s0 = 0; s0 < nact; s0 += 8) {
+            float2 mlv[8], ov[8];   // 16 loads in flight, then the online fold
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                mlv[k] = s0 + k < nact ? load2_agent(ml + 2 * (s0 + k)) : make_float2(NEG, 0.0f);
+                ov[k] = s0 + k < nact ? load2_agent(po + (int64_t)(s0 + k) * D) : make_float2(0.0f, 0.0f);
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                if (mlv[k].x == NEG) continue;
+                const float mn = fmaxf(mg, mlv[k].x);
+                const float a = mg == NEG ? 0.0f : exp2f(mg - mn);
+                const float w = exp2f(mlv[k].x - mn);
+                ls = ls * a + mlv[k].y * w;
+                acc.x = acc.x * a + ov[k].x * w;
+                acc.y = acc.y * a + ov[k].y * w;
+                mg = mn;
+            }
+        }
+        write_output(out, lse, bi, d, acc, mg, ls, D);
     }
 }
 
@@ -404,7 +499,8 @@ hipError_t decode_gt(const Geom& g, const DecodeArgs& a, hipStream_t s) {
     T* out = reinterpret_cast<T*>(a.out);
 #define ABS_DECODE(CH_, PIPE_, MF_)                                                                         \
     hipLaunchKernelGGL((k_sparse_decode<T, D, GT, CH_, PIPE_, MF_>), grid, dim3(256), 0, s, g, q, a.sel,    \
-                       a.sel_cap, a.count, qscale, a.part_ml, a.part_o, a.splits, a.pages_per_wg)
+                       a.sel_cap, a.count, qscale, a.part_ml, a.part_o, a.splits, a.pages_per_wg, a.arrive, out, \
+                       a.lse)
     constexpr bool kMatrix = ABS_DECODE_MATRIX && sizeof(T) == 2;   // bf16: q.k on the matrix cores
     // (a pipelined plan on a variant that does not fit runs the plain 8-page loop)
     // (fp32 rows of 8 query heads at D = 128 hold at most 4 pages at once)
@@ -421,8 +517,9 @@ hipError_t decode_gt(const Geom& g, const DecodeArgs& a, hipStream_t s) {
         }
     }
 #undef ABS_DECODE
-    hipLaunchKernelGGL((k_decode_merge<T, D>), dim3(g.B * g.Hq), dim3(256), 0, s, g, a.count, a.sel_cap,
-                       a.pages_per_wg, a.splits, a.part_ml, a.part_o, out, a.lse);
+    if (a.arrive == nullptr)
+        hipLaunchKernelGGL((k_decode_merge<T, D>), dim3(g.B * g.Hq), dim3(256), 0, s, g, a.count, a.sel_cap,
+                           a.pages_per_wg, a.splits, a.part_ml, a.part_o, out, a.lse);
     return hipGetLastError();
 }
 

@@ -69,6 +69,7 @@ struct DecodeArgs {
     float* lse;       // may be null
     float* part_ml;   // [B*Hq][splits][2]
     float* part_o;    // [B*Hq][splits][D]
+    int32_t* arrive;  // [B*Hkv] arrival counters, zero between calls; null: separate merge launch
     int pages_per_wg; // <= kMaxPagesPerWg, a multiple of chunk
     int chunk;        // pages held in registers at a time: 1, 2, 4 or 8
     bool pipelined;   // two chunks in flight (chunk 8, pages_per_wg a multiple of 16)

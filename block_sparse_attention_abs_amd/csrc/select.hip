@@ -3,7 +3,7 @@
 // figure after Figure 8: each head keeps K blocks, K set by its block size
 // so every head reads the same number of pages).
 //
-// score:  one workgroup per (tile of blocks, b*Hkv + h).  The group query
+// score:  one workgroup per (tile of 256 blocks, b*Hkv + h).  The group query
 //         qbar = sum of the G query heads of KV head h is folded with the
 //         per-channel dequantization once per workgroup:
 //             w_d = qbar_d * scale_d,   c0 = sum_d qbar_d * lo_d,
@@ -11,8 +11,8 @@
 //         (fp64 inside, stored as fp32 in a [b*Hkv+h][stride] scratch with
 //         16-byte aligned rows).  head_dim/32 lanes share one block row of
 //         INT4 codes, 16 bytes each, so one load instruction reads a
-//         contiguous 1 KiB run; the code loads are issued before the
-//         workgroup's query prologue.
+//         contiguous 1 KiB run per wavefront; all of a lane's code loads
+//         are issued before the workgroup's query prologue.
 // top-K:  one workgroup per (b, h); thread t owns block indices
 //         [t*KPT, (t+1)*KPT) as order-preserving 32-bit keys in registers.
 //         1. min/max of the scores; a 2048-bin histogram of the scores'
@@ -31,12 +31,13 @@
 namespace absk {
 namespace {
 
-template <typename T, int D, int GT>
+template <typename T, int D, int GT, int RPL>
 __global__ __launch_bounds__(256) void k_score(Geom g, const uint8_t* __restrict__ codes,
                                                const float* __restrict__ scale, const float* __restrict__ lo,
                                                const T* __restrict__ q, float* __restrict__ scores, int stride) {
     constexpr int LPB = D / 32;               // lanes per block row (16 B of codes each)
-    constexpr int BPW = 256 / LPB;            // blocks per workgroup
+    constexpr int GPW = 256 / LPB;            // lane groups per workgroup
+    constexpr int BPW = GPW * RPL;            // blocks per workgroup
     const int bh = blockIdx.y;
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
     const int N = ceil_div(g.seq_lens[b], g.block_size[h]);
@@ -44,10 +45,16 @@ __global__ __launch_bounds__(256) void k_score(Geom g, const uint8_t* __restrict
     if (j0 >= N) return;
     const int64_t row0 = g.off[bh];
     const int sub = threadIdx.x % LPB;
-    const int j = j0 + threadIdx.x / LPB;
+    const int grp = threadIdx.x / LPB;
 
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (j < N) v = *reinterpret_cast<const uint4*>(codes + (row0 + j) * (D / 2) + sub * 16);
+    // RPL block rows per lane group, GPW consecutive rows per step (contiguous runs)
+    uint4 v[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+        const int j = j0 + r * GPW + grp;
+        v[r] = make_uint4(0u, 0u, 0u, 0u);
+        if (j < N) v[r] = *reinterpret_cast<const uint4*>(codes + (row0 + j) * (D / 2) + sub * 16);
+    }
 
     // per channel: w_d = qbar_d * scale_d and z_d = qbar_d * lo_d (fp64, LDS)
     __shared__ double w[D], z[D];
@@ -66,17 +73,26 @@ __global__ __launch_bounds__(256) void k_score(Geom g, const uint8_t* __restrict
     }
     __syncthreads();
 
-    // this lane's 32 channels: sum_d (w_d * code_d + z_d); the lanes of a block then add up
-    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
-    const double* ws = w + sub * 32;
-    const double* zs = z + sub * 32;
-    double acc = 0.0;
+    // this lane's 32 channels: its share of sum_d z_d once, then sum_d w_d * code_d
+    // per row; the LPB lanes of a row then add up
+    double wr[32], c0 = 0.0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int n = 0; n < 32; ++n) {
+        wr[n] = w[sub * 32 + n];
+        c0 += z[sub * 32 + n];
+    }
 #pragma unroll
-        for (int n = 0; n < 8; ++n) acc += ws[i * 8 + n] * (double)((wd[i] >> (4 * n)) & 15u) + zs[i * 8 + n];
-    acc = lanes_sum_f64<LPB>(acc);
-    if (j < N && sub == 0) scores[(int64_t)bh * stride + j] = (float)acc;
+    for (int r = 0; r < RPL; ++r) {
+        const uint32_t wd[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+        double acc = c0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int n = 0; n < 8; ++n) acc = fma(wr[i * 8 + n], (double)((wd[i] >> (4 * n)) & 15u), acc);
+        acc = lanes_sum_f64<LPB>(acc);
+        const int j = j0 + r * GPW + grp;
+        if (j < N && sub == 0) scores[(int64_t)bh * stride + j] = (float)acc;
+    }
 }
 
 // Order-preserving map of a float to uint32 (larger float -> larger key);
@@ -91,7 +107,8 @@ __device__ __forceinline__ float key_float(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// Exclusive prefix sum over a workgroup of NT threads; `total` gets the sum.
+// Exclusive prefix sum over a workgroup of NT threads (one barrier); `total`
+// gets the sum.  s_wave must not be written again before the next barrier.
 template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -105,21 +122,8 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
         before += i < wave ? t : 0u;
         all += t;
     }
-    __syncthreads();
     *total = all;
     return before + x - v;
-}
-
-template <int NT>
-__device__ __forceinline__ float block_max(float v, float* s_wave) {
-    v = wave_max(v);
-    if ((threadIdx.x & 63) == 0) s_wave[threadIdx.x >> 6] = v;
-    __syncthreads();
-    float r = s_wave[0];
-#pragma unroll
-    for (int i = 1; i < NT / 64; ++i) r = fmaxf(r, s_wave[i]);
-    __syncthreads();
-    return r;
 }
 
 constexpr int kBins = 2048;
@@ -167,8 +171,8 @@ __global__ __launch_bounds__(NT) void k_topk(Geom g, const float* __restrict__ s
     }
 
     __shared__ uint32_t hist[kBins];
-    __shared__ uint32_t s_wave[NT / 64];
-    __shared__ float s_wf[NT / 64];
+    __shared__ uint32_t s_wave[3][NT / 64];          // one per scan: no barrier between reuses
+    __shared__ float s_wmax[NT / 64], s_wmin[NT / 64];
     __shared__ uint32_t s_cand_key[kCandCap];
     __shared__ int32_t s_cand_idx[kCandCap];
     __shared__ uint32_t s_bin, s_above, s_ncand, s_tau_key;
@@ -176,8 +180,19 @@ __global__ __launch_bounds__(NT) void k_topk(Geom g, const float* __restrict__ s
 
     for (int i = threadIdx.x; i < kBins; i += NT) hist[i] = 0u;
     if (threadIdx.x == 0) s_ncand = 0u;
-    mx = block_max<NT>(mx, s_wf);
-    mn = -block_max<NT>(-mn, s_wf);
+    // min and max of the row: wavefront shuffles, then one barrier
+    mx = wave_max(mx);
+    mn = -wave_max(-mn);
+    if ((threadIdx.x & 63) == 0) {
+        s_wmax[threadIdx.x >> 6] = mx;
+        s_wmin[threadIdx.x >> 6] = mn;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) {
+        mx = fmaxf(mx, s_wmax[i]);
+        mn = fminf(mn, s_wmin[i]);
+    }
     const float range = mx - mn;
     const float inv = (float)kBins / range;
     const bool binned = range > 0.0f && range <= 3.0e38f && inv > 0.0f && inv <= 3.0e38f;
@@ -201,7 +216,7 @@ __global__ __launch_bounds__(NT) void k_topk(Geom g, const float* __restrict__ s
             mine += c[i];
         }
         uint32_t total;
-        const uint32_t excl = block_exclusive_scan<NT>(mine, s_wave, &total);
+        const uint32_t excl = block_exclusive_scan<NT>(mine, s_wave[0], &total);
         if (excl < (uint32_t)K && (uint32_t)K <= excl + mine) {     // exactly one thread
             uint32_t above = excl;
 #pragma unroll
@@ -292,7 +307,7 @@ __global__ __launch_bounds__(NT) void k_topk(Geom g, const float* __restrict__ s
 #pragma unroll
         for (int e = 0; e < KPT; ++e) n_eq += (base + e < N && key[e] == tau_key) ? 1u : 0u;
         uint32_t total;
-        uint32_t r = block_exclusive_scan<NT>(n_eq, s_wave, &total);
+        uint32_t r = block_exclusive_scan<NT>(n_eq, s_wave[1], &total);
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
             if (base + e < N && key[e] == tau_key) {
@@ -305,32 +320,34 @@ __global__ __launch_bounds__(NT) void k_topk(Geom g, const float* __restrict__ s
     }
 
     // keep (key > tau_key) or (key == tau_key and index <= tau_idx): exactly K
-    uint32_t n_keep = 0;
+    uint64_t keep = 0;
 #pragma unroll
     for (int e = 0; e < KPT; ++e)
-        n_keep += (base + e < N && (key[e] > tau_key || (key[e] == tau_key && base + e <= tau_idx))) ? 1u : 0u;
+        keep |= (base + e < N && (key[e] > tau_key || (key[e] == tau_key && base + e <= tau_idx))) ? 1ull << e : 0ull;
     uint32_t total;
-    uint32_t pos = block_exclusive_scan<NT>(n_keep, s_wave, &total);
+    const uint32_t pos = block_exclusive_scan<NT>((uint32_t)__builtin_popcountll(keep), s_wave[2], &total);
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
-        const bool keep = base + e < N && (key[e] > tau_key || (key[e] == tau_key && base + e <= tau_idx));
-        if (keep && pos < (uint32_t)K) out[pos++] = base + e;
+        const uint32_t p = pos + (uint32_t)__builtin_popcountll(keep & ((1ull << e) - 1ull));
+        if (((keep >> e) & 1ull) && p < (uint32_t)K) out[p] = base + e;
     }
 }
 
 template <typename T, int D>
 hipError_t select_impl(const Geom& g, const SelectArgs& a, hipStream_t s) {
-    constexpr int BPW = 256 / (D / 32);
+    // 256 blocks per workgroup: D/32 lanes per block row, RPL rows per lane group
+    constexpr int RPL = 256 / (256 / (D / 32));
+    constexpr int BPW = 256;
     const dim3 sgrid(ceil_div(a.max_n, BPW), g.B * g.Hkv);
     const T* q = reinterpret_cast<const T*>(a.q);
-    if (g.G <= 1)
-        hipLaunchKernelGGL((k_score<T, D, 1>), sgrid, dim3(256), 0, s, g, a.codes, a.scale, a.lo, q, a.scores, a.stride);
-    else if (g.G <= 2)
-        hipLaunchKernelGGL((k_score<T, D, 2>), sgrid, dim3(256), 0, s, g, a.codes, a.scale, a.lo, q, a.scores, a.stride);
-    else if (g.G <= 4)
-        hipLaunchKernelGGL((k_score<T, D, 4>), sgrid, dim3(256), 0, s, g, a.codes, a.scale, a.lo, q, a.scores, a.stride);
-    else
-        hipLaunchKernelGGL((k_score<T, D, 8>), sgrid, dim3(256), 0, s, g, a.codes, a.scale, a.lo, q, a.scores, a.stride);
+#define ABS_SCORE(GT_)                                                                                       \
+    hipLaunchKernelGGL((k_score<T, D, GT_, RPL>), sgrid, dim3(256), 0, s, g, a.codes, a.scale, a.lo, q, a.scores, \
+                       a.stride)
+    if (g.G <= 1) ABS_SCORE(1);
+    else if (g.G <= 2) ABS_SCORE(2);
+    else if (g.G <= 4) ABS_SCORE(4);
+    else ABS_SCORE(8);
+#undef ABS_SCORE
     const dim3 tgrid(g.B * g.Hkv);
 #define ABS_TOPK(NT_, KPT_)                                                                                  \
     hipLaunchKernelGGL((k_topk<NT_, KPT_>), tgrid, dim3(NT_), 0, s, g, a.scores, a.stride, a.budget, a.sel, \

@@ -176,7 +176,8 @@ abs_status abs_score_select(const abs_paged_kv *kv, const abs_block_map *map,
  * Exact attention over the selected blocks only (Figure 1's sparse attention;
  * the "Attention" stage of the figure after Figure 13), split over pages with
  * an fp32 online softmax and a log-sum-exp merge (FlashAttention, in the
- * page's references); two kernel launches (split, merge).
+ * page's references); one kernel launch, in which the last workgroup to
+ * finish a (b, h) merges that head's partials.
  * For query head i of KV head h = i / G: the kept tokens are the union of
  * [j*bs_h, min((j+1)*bs_h, L_b)) over the first sel_count[b][h] entries j of
  * sel row (b, h); z_t = sm_scale * q_i . k_t;
@@ -185,8 +186,11 @@ abs_status abs_score_select(const abs_paged_kv *kv, const abs_block_map *map,
  *       sel_count[b][h] must not exceed K_{b,h} for it).
  *   out: device [num_seqs][num_q_heads][head_dim] in kv_dtype.
  *   lse: device f32 [num_seqs][num_q_heads], natural log; may be NULL.
- *   workspace: >= abs_workspace_bytes(ABS_OP_DECODE) bytes (fp32 partials;
- *       no initialization needed).
+ *   workspace: >= abs_workspace_bytes(ABS_OP_DECODE) bytes: per-(b, h)
+ *       arrival counters, then fp32 partials.  It must be zero-filled before
+ *       its first use; every completed call leaves the counters at zero, so a
+ *       workspace keeps working as long as nothing else writes to it.  Calls
+ *       that share a workspace must not overlap in time.
  */
 abs_status abs_sparse_decode(const abs_paged_kv *kv, const abs_block_map *map, const void *q,
                              const int32_t *sel, int32_t sel_cap, const int32_t *sel_count,
