@@ -48,6 +48,7 @@ struct Plan {
     int max_n = 0;            // largest N_{b,h}
     int sel_cap = 0;          // largest K_{b,h}
     int max_pages_read = 0;   // largest K_{b,h} * (bs_h / 16)
+    const int32_t* block_size_dev = nullptr;   // the descriptor's device copy (kernels use the host values)
 };
 
 abs_status check_geometry(const abs_paged_kv* kv, const abs_block_map* map, Plan* p) {
@@ -57,6 +58,8 @@ abs_status check_geometry(const abs_paged_kv* kv, const abs_block_map* map, Plan
     if (kv->num_q_heads % kv->num_kv_heads != 0)
         return fail(ABS_ERR_INVALID_ARG, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
                     kv->num_q_heads, kv->num_kv_heads);
+    if (kv->num_kv_heads > absk::kMaxKvHeads)
+        return fail(ABS_ERR_UNSUPPORTED, "num_kv_heads %d > %d", kv->num_kv_heads, absk::kMaxKvHeads);
     const int G = kv->num_q_heads / kv->num_kv_heads;
     if (G > 8) return fail(ABS_ERR_UNSUPPORTED, "query group size %d > 8", G);
     if (kv->head_dim != 64 && kv->head_dim != 128)
@@ -94,8 +97,13 @@ abs_status check_geometry(const abs_paged_kv* kv, const abs_block_map* map, Plan
     g.v = kv->v_cache;
     g.page_table = kv->page_table;
     g.seq_lens = kv->seq_lens;
-    g.block_size = map->block_size;
     g.off = map->centroid_off;
+    p->block_size_dev = map->block_size;
+    g.bs_log2[0] = g.bs_log2[1] = 0;
+    for (int h = 0; h < g.Hkv; ++h) {
+        const int bs = map->block_size_host[h];   // validated: 16, 32 or 64
+        g.bs_log2[h / 32] |= (uint64_t)(bs == 16 ? 0 : bs == 32 ? 1 : 2) << (2 * (h % 32));
+    }
     p->total_blocks = 0;
     p->max_n = 0;
     for (int b = 0; b < g.B; ++b)
@@ -127,7 +135,7 @@ abs_status require_device(const Plan& p, bool need_v) {
     if (g.k == nullptr || (need_v && g.v == nullptr)) return fail(ABS_ERR_INVALID_ARG, "null cache pointer");
     if (g.page_table == nullptr || g.seq_lens == nullptr)
         return fail(ABS_ERR_INVALID_ARG, "null page_table or seq_lens");
-    if (g.block_size == nullptr || g.off == nullptr)
+    if (p.block_size_dev == nullptr || g.off == nullptr)
         return fail(ABS_ERR_INVALID_ARG, "null block_size or centroid_off");
     return ok();
 }
@@ -329,6 +337,17 @@ abs_status abs_score_select(const abs_paged_kv* kv, const abs_block_map* map, co
     a.sel_cap = sel_cap;
     a.budget = token_budget;
     a.max_n = p.max_n;
+    // the exact list of score tiles, when it fits the kernel arguments
+    uint32_t tiles[absk::kMaxScoreTiles];
+    a.ntiles = 0;
+    for (int b = 0; b < p.g.B; ++b)
+        for (int h = 0; h < p.g.Hkv; ++h) {
+            const int64_t n = ceil_div64(ceil_div64(kv->seq_lens_host[b], map->block_size_host[h]),
+                                         absk::kScoreBlocksPerWg);
+            for (int64_t t = 0; t < n; ++t, ++a.ntiles)
+                if (a.ntiles < absk::kMaxScoreTiles) tiles[a.ntiles] = (uint32_t)(b * p.g.Hkv + h) << 8 | (uint32_t)t;
+        }
+    a.tiles_host = a.ntiles <= absk::kMaxScoreTiles ? tiles : nullptr;
     return hip_status(absk::launch_select(p.g, p.dt, a, static_cast<hipStream_t>(stream)), "score_select");
 }
 

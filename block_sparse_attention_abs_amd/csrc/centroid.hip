@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void k_centroid_mean(Geom g, float* __restrict
     const int bh = blockIdx.y;
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
     const int L = g.seq_lens[b];
-    const int bs = g.block_size[h];
+    const int bs = block_size_of(g, h);
     const int N = ceil_div(L, bs);
     const int j0 = blockIdx.x * kBuildTile;
     if (j0 >= N) return;                                  // uniform: whole workgroup leaves
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(D) void k_centroid_range(Geom g, const float* __res
                                                       float* __restrict__ scale, float* __restrict__ lo) {
     const int bh = blockIdx.x;
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
-    const int N = ceil_div(g.seq_lens[b], g.block_size[h]);
+    const int N = ceil_div(g.seq_lens[b], block_size_of(g, h));
     const int nt = ceil_div(N, kBuildTile);
     const int d = threadIdx.x;
     float a = __builtin_inff(), z = -__builtin_inff();
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(256) void k_centroid_quantize(Geom g, const float* 
     constexpr int ROWS = 256 / TPB;            // block rows per pass
     const int bh = blockIdx.y;
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
-    const int N = ceil_div(g.seq_lens[b], g.block_size[h]);
+    const int N = ceil_div(g.seq_lens[b], block_size_of(g, h));
     const int j0 = blockIdx.x * kBuildTile;
     if (j0 >= N) return;
     const int64_t row0 = g.off[bh];

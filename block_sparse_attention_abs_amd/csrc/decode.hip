@@ -55,6 +55,10 @@ constexpr bool kPipeFits = sizeof(T) == 2 && (D == 64 || GT <= 4);
 #ifndef ABS_DECODE_MATRIX
 #define ABS_DECODE_MATRIX 1
 #endif
+// Row groups of the double-buffered matrix-core kernel (1 or 2).
+#ifndef ABS_DECODE_ROWGROUPS
+#define ABS_DECODE_ROWGROUPS 1
+#endif
 
 // Agent-scope (device-coherent) 8-byte store and load: relaxed atomics, which
 // write through and read past the per-XCD L2.
@@ -88,8 +92,13 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // rows of the A operand are the group's heads repeated 4x, so lane l receives
 // S[head][token l%16] for all heads.  The scores go through LDS (one barrier
 // per chunk, double-buffered) to the row layout the V side uses.
-template <typename T, int D, int GT, int CH, bool PIPE, bool MF>
-__global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT, PIPE, MF>::value)) void k_sparse_decode(Geom g, const T* __restrict__ q,
+//
+// RG row groups (RG = 2 only with MF): 256*RG threads; row group rg folds the
+// pages rg, rg + RG, ... of each chunk into its own 16 rows, so each
+// wavefront does 1/RG of the softmax and P.V work of a chunk and RG
+// wavefronts share each SIMD.
+template <typename T, int D, int GT, int CH, bool PIPE, bool MF, int RG>
+__global__ __launch_bounds__(256 * RG, (DecodeOccupancy<T, D, GT, PIPE, MF>::value)) void k_sparse_decode(Geom g, const T* __restrict__ q,
                                                           const int32_t* __restrict__ sel, int sel_cap,
                                                           const int32_t* __restrict__ count, float qscale,
                                                           float* __restrict__ part_ml, float* __restrict__ part_o,
@@ -101,17 +110,47 @@ __global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT, PIPE, MF>::value)) 
     const int split = blockIdx.x;
     const int bh = blockIdx.y;
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
-    const int row = threadIdx.x / kRowLanes;
+    const int row = (threadIdx.x & 255) / kRowLanes;
+    const int rg = threadIdx.x >> 8;                     // row group
     const int lane = threadIdx.x & (kRowLanes - 1);
     const int wave = threadIdx.x / 64;
     const int wl = threadIdx.x & 63;
 
     constexpr int KSTEPS = D / 32;                       // MFMA k-steps per key row
     constexpr int GP = (GT + 3) / 4;                     // MFMA passes (4 heads each)
-    constexpr int KW = MF ? 2 * KSTEPS : CH;             // K words held per chunk
+    constexpr int PPC = CH / RG;                         // pages of a chunk per row group (V side)
+    constexpr int PWV = 2 / RG;                          // MF: pages of a chunk per wavefront (K side)
+    constexpr int KW = MF ? PWV * KSTEPS : CH;           // K words held per chunk
     static_assert(!MF || (CH == 8 && sizeof(T) == 2), "matrix-core path: bf16, 8-page chunks");
+    static_assert(RG == 1 || (MF && RG == 2), "two row groups only with the matrix-core path");
 
-    // The group's queries: independent of everything else, so issued first.
+    // Resolve this workgroup's pages lane-parallel: lane i of every wavefront
+    // follows selection entry -> logical page -> physical page for page p0 + i
+    // (the selection row is read speculatively up to sel_cap, before the
+    // sequence length and the count arrive); readlane then broadcasts them.
+    const int spb = block_size_of(g, h) / kPage;      // pages per block (stride): 1, 2 or 4
+    const int sh = __builtin_ctz(spb);
+    const int p0 = split * ppw;                        // ppw <= 64
+    const int gp = p0 + wl;
+    const bool in_row = wl < ppw && gp < sel_cap * spb;
+    const int sv = sel[(int64_t)bh * sel_cap + min(gp >> sh, sel_cap - 1)];   // unconditional, clamped
+    const int L = g.seq_lens[b];
+    const int npages = ceil_div(L, kPage);
+    const int N = ceil_div(L, spb * kPage);
+    const int K = min(max(count[bh], 0), sel_cap);
+    const int total = min(K * spb, splits * ppw);      // selected pages of (b, h)
+    int ph = -1, lp = 0;
+    if (in_row) {
+        lp = min(max(sv, 0), N - 1) * spb + (gp & (spb - 1));
+        if (lp < npages) {
+            const int pg = g.page_table[(int64_t)b * g.max_pages + lp];
+            if (pg >= 0 && pg < g.num_pages) ph = pg;
+        }
+    }
+    if (gp >= total) ph = -1;
+
+    // The group's queries, issued after the page resolution's first load so
+    // that they do not queue ahead of it.
     Words<NW> qw[MF ? 1 : GT];
     Words<4> qa[MF ? GP : 1][MF ? KSTEPS : 1];
     if constexpr (MF) {
@@ -131,35 +170,8 @@ __global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT, PIPE, MF>::value)) 
         }
     }
 
-    const int L = g.seq_lens[b];
-    const int bs = g.block_size[h];
-    const int spb = bs / kPage;                        // pages per block (stride)
-    const int npages = ceil_div(L, kPage);
-    const int N = ceil_div(L, bs);
-    const int K = min(max(count[bh], 0), sel_cap);
-    const int total = min(K * spb, splits * ppw);      // selected pages of (b, h)
-    const int p0 = split * ppw;                        // ppw <= 64
-
-    // Resolve this workgroup's pages lane-parallel: lane i of every wavefront
-    // follows selection entry -> logical page -> physical page for page p0 + i
-    // (the selection row is read speculatively up to sel_cap, so the page-table
-    // read does not wait for the count); readlane then broadcasts them.
-    int ph = -1, lp = 0;
-    {
-        const int gp = p0 + wl;
-        if (wl < ppw && gp < sel_cap * spb) {
-            const int blk = min(max(sel[(int64_t)bh * sel_cap + gp / spb], 0), N - 1);
-            lp = blk * spb + gp % spb;
-            if (lp < npages) {
-                const int pg = g.page_table[(int64_t)b * g.max_pages + lp];
-                if (pg >= 0 && pg < g.num_pages) ph = pg;
-            }
-        }
-        if (gp >= total) ph = -1;
-    }
-
-    __shared__ float s_red[4][GT];
-    constexpr int kRows = 256 / kRowLanes;
+    __shared__ float s_red[4 * RG][GT];
+    constexpr int kRows = 256 * RG / kRowLanes;
     __shared__ __align__(16) float s_o[kRows][GT][D];   // epilogue: each row's rescaled output
     __shared__ float s_l[kRows][GT];
     __shared__ float s_sc[MF ? 2 : 1][MF ? CH : 1][MF ? 16 : 1][GT];   // MF: scores, double-buffered per chunk
@@ -182,13 +194,13 @@ __global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT, PIPE, MF>::value)) 
         const T* vc = reinterpret_cast<const T*>(g.v);
         const uint32_t lane_off = (uint32_t)((row * D + lane * VEC) * sizeof(T));
         // issue every K and V load of the chunk of CH pages starting at c0
-        auto issue = [&](int c0, Words<MF ? 4 : NW>(&kw)[KW], Words<NW>(&vw)[CH]) {
+        auto issue = [&](int c0, Words<MF ? 4 : NW>(&kw)[KW], Words<NW>(&vw)[PPC]) {
             if constexpr (MF) {
-                // this wavefront's two pages, B-operand layout
+                // this wavefront's pages (wave, wave + 4*RG), B-operand layout
                 const uint32_t k_off = (uint32_t)(((wl & 15) * D + (wl >> 4) * 8) * sizeof(T));
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int pg = __builtin_amdgcn_readlane(ph, c0 + wave + 4 * j);
+                for (int j = 0; j < PWV; ++j) {
+                    const int pg = __builtin_amdgcn_readlane(ph, c0 + wave + 4 * RG * j);
                     const int64_t base = ((int64_t)(pg >= 0 ? pg : 0) * g.Hkv + h) * (kPage * D);
 #pragma unroll
                     for (int st = 0; st < KSTEPS; ++st)
@@ -203,21 +215,21 @@ __global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT, PIPE, MF>::value)) 
                 }
             }
 #pragma unroll
-            for (int i = 0; i < CH; ++i) {
-                const int pg = __builtin_amdgcn_readlane(ph, c0 + i);
+            for (int k = 0; k < PPC; ++k) {   // this row group's pages rg, rg + RG, ...
+                const int pg = __builtin_amdgcn_readlane(ph, c0 + RG * k + rg);
                 const int64_t base = ((int64_t)(pg >= 0 ? pg : 0) * g.Hkv + h) * (kPage * D);
-                vw[i] = load_words_at<NW>(vc + base, lane_off);
+                vw[k] = load_words_at<NW>(vc + base, lane_off);
             }
         };
         // fold the chunk at c0 into this row's running (m, l, o)
-        auto consume = [&](int c0, const Words<MF ? 4 : NW>(&kw)[KW], const Words<NW>(&vw)[CH]) {
-            float sc[CH][GT], cm[GT];
+        auto consume = [&](int c0, const Words<MF ? 4 : NW>(&kw)[KW], const Words<NW>(&vw)[PPC]) {
+            float sc[PPC][GT], cm[GT];
 #pragma unroll
             for (int gg = 0; gg < GT; ++gg) cm[gg] = m[gg];
             if constexpr (MF) {
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int pi = wave + 4 * j;
+                for (int j = 0; j < PWV; ++j) {
+                    const int pi = wave + 4 * RG * j;
                     const int pg = __builtin_amdgcn_readlane(ph, c0 + pi);
                     const int t0 = __builtin_amdgcn_readlane(lp, c0 + pi) * kPage;
                     const bool valid = pg >= 0 && t0 + (wl & 15) < L;
@@ -238,11 +250,11 @@ __global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT, PIPE, MF>::value)) 
                 }
                 __syncthreads();
 #pragma unroll
-                for (int i = 0; i < CH; ++i)
+                for (int k = 0; k < PPC; ++k)
 #pragma unroll
                     for (int gg = 0; gg < GT; ++gg) {
-                        sc[i][gg] = s_sc[sbuf][i][row][gg];
-                        cm[gg] = fmaxf(cm[gg], sc[i][gg]);
+                        sc[k][gg] = s_sc[sbuf][RG * k + rg][row][gg];
+                        cm[gg] = fmaxf(cm[gg], sc[k][gg]);
                     }
                 sbuf ^= 1;
             } else {
@@ -273,7 +285,7 @@ __global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT, PIPE, MF>::value)) 
                 for (int e = 0; e < VEC; ++e) o[gg][e] *= alpha;
             }
 #pragma unroll
-            for (int i = 0; i < CH; ++i) {
+            for (int i = 0; i < PPC; ++i) {
                 float p[GT];
 #pragma unroll
                 for (int gg = 0; gg < GT; ++gg) {
@@ -292,7 +304,7 @@ __global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT, PIPE, MF>::value)) 
         if constexpr (PIPE) {
             // double-buffered: the next chunk's loads are in flight while this one is folded
             Words<MF ? 4 : NW> ka[KW], kb[KW];
-            Words<NW> va[CH], vb[CH];
+            Words<NW> va[PPC], vb[PPC];
             issue(0, ka, va);
             for (int c0 = 0;; c0 += 2 * CH) {
                 const bool nb = has_chunk(c0 + CH);
@@ -307,7 +319,7 @@ __global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT, PIPE, MF>::value)) 
         } else {
             for (int c0 = 0; has_chunk(c0); c0 += CH) {
                 Words<MF ? 4 : NW> kw[KW];
-                Words<NW> vw[CH];
+                Words<NW> vw[PPC];
                 issue(c0, kw, vw);
                 consume(c0, kw, vw);
             }
@@ -325,13 +337,16 @@ __global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT, PIPE, MF>::value)) 
         __syncthreads();
 #pragma unroll
         for (int gg = 0; gg < GT; ++gg) {
-            M[gg] = fmaxf(fmaxf(s_red[0][gg], s_red[1][gg]), fmaxf(s_red[2][gg], s_red[3][gg]));
+            M[gg] = s_red[0][gg];
+#pragma unroll
+            for (int w = 1; w < 4 * RG; ++w) M[gg] = fmaxf(M[gg], s_red[w][gg]);
             const float f = m[gg] == NEG ? 0.0f : exp2_approx(m[gg] - M[gg]);
+            const int r = rg * 16 + row;
 #pragma unroll
             for (int e = 0; e < VEC; e += 4)
-                *reinterpret_cast<float4*>(&s_o[row][gg][lane * VEC + e]) =
+                *reinterpret_cast<float4*>(&s_o[r][gg][lane * VEC + e]) =
                     make_float4(o[gg][e] * f, o[gg][e + 1] * f, o[gg][e + 2] * f, o[gg][e + 3] * f);
-            if (lane == 0) s_l[row][gg] = l[gg] * f;
+            if (lane == 0) s_l[r][gg] = l[gg] * f;
         }
         __syncthreads();
     }
@@ -357,7 +372,9 @@ __global__ __launch_bounds__(256, (DecodeOccupancy<T, D, GT, PIPE, MF>::value)) 
                 }
 #pragma unroll
                 for (int r = 0; r < kRows; ++r) ls += s_l[r][gg];
-                mg = fmaxf(fmaxf(s_red[0][gg], s_red[1][gg]), fmaxf(s_red[2][gg], s_red[3][gg]));
+                mg = s_red[0][gg];
+#pragma unroll
+                for (int w = 1; w < 4 * RG; ++w) mg = fmaxf(mg, s_red[w][gg]);
             }
             const int64_t bi = (int64_t)b * g.Hq + h * g.G + gg;
             const int64_t prow = bi * splits + split;
@@ -445,7 +462,7 @@ __global__ __launch_bounds__(256) void k_decode_merge(Geom g, const int32_t* __r
     const int b = bi / g.Hq, head = bi - b * g.Hq;
     const int h = head / g.G;
     const int bh = b * g.Hkv + h;
-    const int spb = g.block_size[h] / kPage;
+    const int spb = block_size_of(g, h) / kPage;
     const int K = min(max(count[bh], 0), sel_cap);
     const int total = min(K * spb, splits * ppw);
     const int nact = max(1, ceil_div(total, ppw));
@@ -491,32 +508,36 @@ __global__ __launch_bounds__(256) void k_decode_merge(Geom g, const int32_t* __r
     if (lse != nullptr && d == 0) lse[bi] = lsum > 0.0f ? (M + log2f(lsum)) * kLn2 : NEG;
 }
 
+// One split launch: 256 * RG threads per workgroup, as the kernel assumes.
+template <typename T, int D, int GT, int CH, bool PIPE, bool MF, int RG>
+void launch_split(dim3 grid, const Geom& g, const DecodeArgs& a, float qscale, hipStream_t s) {
+    constexpr int kThreads = 256 * RG;
+    hipLaunchKernelGGL((k_sparse_decode<T, D, GT, CH, PIPE, MF, RG>), grid, dim3(kThreads), 0, s, g,
+                       reinterpret_cast<const T*>(a.q), a.sel, a.sel_cap, a.count, qscale, a.part_ml, a.part_o,
+                       a.splits, a.pages_per_wg, a.arrive, reinterpret_cast<T*>(a.out), a.lse);
+}
+
 template <typename T, int D, int GT>
 hipError_t decode_gt(const Geom& g, const DecodeArgs& a, hipStream_t s) {
     const dim3 grid(a.splits, g.B * g.Hkv);
     const float qscale = a.sm_scale * kLog2e;
-    const T* q = reinterpret_cast<const T*>(a.q);
     T* out = reinterpret_cast<T*>(a.out);
-#define ABS_DECODE(CH_, PIPE_, MF_)                                                                         \
-    hipLaunchKernelGGL((k_sparse_decode<T, D, GT, CH_, PIPE_, MF_>), grid, dim3(256), 0, s, g, q, a.sel,    \
-                       a.sel_cap, a.count, qscale, a.part_ml, a.part_o, a.splits, a.pages_per_wg, a.arrive, out, \
-                       a.lse)
     constexpr bool kMatrix = ABS_DECODE_MATRIX && sizeof(T) == 2;   // bf16: q.k on the matrix cores
+    constexpr int kRowGroups = kMatrix ? ABS_DECODE_ROWGROUPS : 1;
     // (a pipelined plan on a variant that does not fit runs the plain 8-page loop)
     // (fp32 rows of 8 query heads at D = 128 hold at most 4 pages at once)
     constexpr bool kWide = sizeof(T) == 4 && D * GT >= 1024;
     if (a.pipelined && kPipeFits<T, D, GT>) {
-        if constexpr (kPipeFits<T, D, GT>) ABS_DECODE(8, true, kMatrix);
+        if constexpr (kPipeFits<T, D, GT>) launch_split<T, D, GT, 8, true, kMatrix, kRowGroups>(grid, g, a, qscale, s);
     } else if ((a.chunk == 8 || a.pipelined) && !kWide) {
-        if constexpr (!kWide) ABS_DECODE(8, false, kMatrix);
+        if constexpr (!kWide) launch_split<T, D, GT, 8, false, kMatrix, 1>(grid, g, a, qscale, s);
     } else {
         switch (a.chunk) {
-            case 1: ABS_DECODE(1, false, false); break;
-            case 2: ABS_DECODE(2, false, false); break;
-            default: ABS_DECODE(4, false, false); break;
+            case 1: launch_split<T, D, GT, 1, false, false, 1>(grid, g, a, qscale, s); break;
+            case 2: launch_split<T, D, GT, 2, false, false, 1>(grid, g, a, qscale, s); break;
+            default: launch_split<T, D, GT, 4, false, false, 1>(grid, g, a, qscale, s); break;
         }
     }
-#undef ABS_DECODE
     if (a.arrive == nullptr)
         hipLaunchKernelGGL((k_decode_merge<T, D>), dim3(g.B * g.Hq), dim3(256), 0, s, g, a.count, a.sel_cap,
                            a.pages_per_wg, a.splits, a.part_ml, a.part_o, out, a.lse);

@@ -10,6 +10,9 @@
 namespace absk {
 
 // Geometry of one layer's paged cache and block map, passed by value to kernels.
+// The block sizes travel in the kernel arguments, 2 bits per KV head
+// (log2(bs / 16)), so no workgroup waits on a memory read for them.
+constexpr int kMaxKvHeads = 64;
 struct Geom {
     int B, Hq, Hkv, D, G, max_pages;
     int64_t num_pages;
@@ -17,9 +20,14 @@ struct Geom {
     const void* v;
     const int32_t* page_table;
     const int32_t* seq_lens;
-    const int32_t* block_size;
     const int64_t* off;
+    uint64_t bs_log2[kMaxKvHeads / 32];
 };
+
+__device__ __forceinline__ int block_size_of(const Geom& g, int h) {
+    const uint64_t w = h < 32 ? g.bs_log2[0] : g.bs_log2[1];
+    return 16 << (int)((w >> (2 * (h & 31))) & 3u);
+}
 
 enum class DType { F32 = 0, BF16 = 1 };
 
@@ -42,6 +50,16 @@ hipError_t launch_build(const Geom& g, DType dt, const BuildArgs& a, hipStream_t
 // Score + select.
 constexpr int kMaxBlocksPerHead = 65536;   // top-K keeps N_{b,h} keys in registers: 1024 x 64
 
+// The score launch: 512 threads per workgroup, 256 blocks per workgroup.
+// When the tiles of all heads fit kMaxScoreTiles, they are listed in the
+// kernel arguments ((b*Hkv + h) << 8 | tile) and the grid has exactly that
+// many workgroups; otherwise the grid is (max tiles per head, B*Hkv).
+constexpr int kScoreBlocksPerWg = 256;
+constexpr int kMaxScoreTiles = 512;
+struct ScoreTiles {
+    uint32_t t[kMaxScoreTiles];
+};
+
 struct SelectArgs {
     const uint8_t* codes;
     const float* scale;
@@ -54,6 +72,8 @@ struct SelectArgs {
     int sel_cap;
     int budget;
     int max_n;        // largest N_{b,h}
+    int ntiles;       // score tiles over all heads
+    const uint32_t* tiles_host;   // their list (host, valid during the call) or null
 };
 
 hipError_t launch_select(const Geom& g, DType dt, const SelectArgs& a, hipStream_t s);

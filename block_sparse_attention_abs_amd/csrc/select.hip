@@ -3,7 +3,8 @@
 // figure after Figure 8: each head keeps K blocks, K set by its block size
 // so every head reads the same number of pages).
 //
-// score:  one workgroup per (tile of 256 blocks, b*Hkv + h).  The group query
+// score:  one workgroup per (tile of 256 blocks, b*Hkv + h);
+//         the tiles are listed in the launch when the list is short.  The group query
 //         qbar = sum of the G query heads of KV head h is folded with the
 //         per-channel dequantization once per workgroup:
 //             w_d = qbar_d * scale_d,   c0 = sum_d qbar_d * lo_d,
@@ -31,17 +32,24 @@
 namespace absk {
 namespace {
 
-template <typename T, int D, int GT, int RPL>
-__global__ __launch_bounds__(256) void k_score(Geom g, const uint8_t* __restrict__ codes,
-                                               const float* __restrict__ scale, const float* __restrict__ lo,
-                                               const T* __restrict__ q, float* __restrict__ scores, int stride) {
+// Build-time tuning: threads of a score workgroup (256 or 512).
+#ifndef ABS_SCORE_NT
+#define ABS_SCORE_NT 512
+#endif
+
+// One tile of 256 blocks of (b, h) = bh, by an ABS_SCORE_NT-thread workgroup.
+template <typename T, int D, int GT>
+__device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restrict__ codes,
+                                           const float* __restrict__ scale, const float* __restrict__ lo,
+                                           const T* __restrict__ q, float* __restrict__ scores, int stride, int bh,
+                                           int tile) {
+    constexpr int NT = ABS_SCORE_NT;
     constexpr int LPB = D / 32;               // lanes per block row (16 B of codes each)
-    constexpr int GPW = 256 / LPB;            // lane groups per workgroup
-    constexpr int BPW = GPW * RPL;            // blocks per workgroup
-    const int bh = blockIdx.y;
+    constexpr int GPW = NT / LPB;             // lane groups per workgroup
+    constexpr int RPL = kScoreBlocksPerWg / GPW;   // block rows per lane group
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
-    const int N = ceil_div(g.seq_lens[b], g.block_size[h]);
-    const int j0 = blockIdx.x * BPW;
+    const int N = ceil_div(g.seq_lens[b], block_size_of(g, h));
+    const int j0 = tile * kScoreBlocksPerWg;
     if (j0 >= N) return;
     const int64_t row0 = g.off[bh];
     const int sub = threadIdx.x % LPB;
@@ -74,7 +82,7 @@ __global__ __launch_bounds__(256) void k_score(Geom g, const uint8_t* __restrict
     __syncthreads();
 
     // this lane's 32 channels: its share of sum_d z_d once, then sum_d w_d * code_d
-    // per row; the LPB lanes of a row then add up
+    // per row (two accumulators per row); the LPB lanes of a row then add up
     double wr[32], c0 = 0.0;
 #pragma unroll
     for (int n = 0; n < 32; ++n) {
@@ -84,15 +92,32 @@ __global__ __launch_bounds__(256) void k_score(Geom g, const uint8_t* __restrict
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
         const uint32_t wd[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
-        double acc = c0;
+        double acc[2] = {c0, 0.0};
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int n = 0; n < 8; ++n) acc = fma(wr[i * 8 + n], (double)((wd[i] >> (4 * n)) & 15u), acc);
-        acc = lanes_sum_f64<LPB>(acc);
+            for (int n = 0; n < 8; ++n)
+                acc[i >> 1] = fma(wr[i * 8 + n], (double)((wd[i] >> (4 * n)) & 15u), acc[i >> 1]);
+        const double sum = lanes_sum_f64<LPB>(acc[0] + acc[1]);
         const int j = j0 + r * GPW + grp;
-        if (j < N && sub == 0) scores[(int64_t)bh * stride + j] = (float)acc;
+        if (j < N && sub == 0) scores[(int64_t)bh * stride + j] = (float)sum;
     }
+}
+
+template <typename T, int D, int GT>
+__global__ __launch_bounds__(ABS_SCORE_NT) void k_score_grid(Geom g, const uint8_t* __restrict__ codes,
+                                                    const float* __restrict__ scale, const float* __restrict__ lo,
+                                                    const T* __restrict__ q, float* __restrict__ scores, int stride) {
+    score_tile<T, D, GT>(g, codes, scale, lo, q, scores, stride, blockIdx.y, blockIdx.x);
+}
+
+template <typename T, int D, int GT>
+__global__ __launch_bounds__(ABS_SCORE_NT) void k_score_list(Geom g, const uint8_t* __restrict__ codes,
+                                                    const float* __restrict__ scale, const float* __restrict__ lo,
+                                                    const T* __restrict__ q, float* __restrict__ scores, int stride,
+                                                    const ScoreTiles tl) {
+    const uint32_t e = tl.t[blockIdx.x];
+    score_tile<T, D, GT>(g, codes, scale, lo, q, scores, stride, (int)(e >> 8), (int)(e & 255u));
 }
 
 // Order-preserving map of a float to uint32 (larger float -> larger key);
@@ -126,6 +151,11 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
     return before + x - v;
 }
 
+// Build-time tuning: threads of the top-K workgroup.
+#ifndef ABS_TOPK_NT
+#define ABS_TOPK_NT 512
+#endif
+
 constexpr int kBins = 2048;
 constexpr int kCandCap = 512;
 
@@ -134,7 +164,7 @@ __global__ __launch_bounds__(NT) void k_topk(Geom g, const float* __restrict__ s
                                              int32_t* __restrict__ sel, int sel_cap, int32_t* __restrict__ count) {
     const int bh = blockIdx.x;
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
-    const int bs = g.block_size[h];
+    const int bs = block_size_of(g, h);
     const int N = ceil_div(g.seq_lens[b], bs);
     const int K = min(N, max(1, budget / bs));
     int32_t* out = sel + (int64_t)bh * sel_cap;
@@ -335,30 +365,42 @@ __global__ __launch_bounds__(NT) void k_topk(Geom g, const float* __restrict__ s
 
 template <typename T, int D>
 hipError_t select_impl(const Geom& g, const SelectArgs& a, hipStream_t s) {
-    // 256 blocks per workgroup: D/32 lanes per block row, RPL rows per lane group
-    constexpr int RPL = 256 / (256 / (D / 32));
-    constexpr int BPW = 256;
-    const dim3 sgrid(ceil_div(a.max_n, BPW), g.B * g.Hkv);
     const T* q = reinterpret_cast<const T*>(a.q);
+    if (a.tiles_host != nullptr && a.ntiles <= kMaxScoreTiles) {
+        ScoreTiles tl;
+        for (int i = 0; i < a.ntiles; ++i) tl.t[i] = a.tiles_host[i];
 #define ABS_SCORE(GT_)                                                                                       \
-    hipLaunchKernelGGL((k_score<T, D, GT_, RPL>), sgrid, dim3(256), 0, s, g, a.codes, a.scale, a.lo, q, a.scores, \
-                       a.stride)
-    if (g.G <= 1) ABS_SCORE(1);
-    else if (g.G <= 2) ABS_SCORE(2);
-    else if (g.G <= 4) ABS_SCORE(4);
-    else ABS_SCORE(8);
+    hipLaunchKernelGGL((k_score_list<T, D, GT_>), dim3(a.ntiles), dim3(ABS_SCORE_NT), 0, s, g, a.codes, a.scale, a.lo, q, \
+                       a.scores, a.stride, tl)
+        if (g.G <= 1) ABS_SCORE(1);
+        else if (g.G <= 2) ABS_SCORE(2);
+        else if (g.G <= 4) ABS_SCORE(4);
+        else ABS_SCORE(8);
 #undef ABS_SCORE
+    } else {
+        const dim3 sgrid(ceil_div(a.max_n, kScoreBlocksPerWg), g.B * g.Hkv);
+#define ABS_SCORE(GT_)                                                                                       \
+    hipLaunchKernelGGL((k_score_grid<T, D, GT_>), sgrid, dim3(ABS_SCORE_NT), 0, s, g, a.codes, a.scale, a.lo, q, a.scores, \
+                       a.stride)
+        if (g.G <= 1) ABS_SCORE(1);
+        else if (g.G <= 2) ABS_SCORE(2);
+        else if (g.G <= 4) ABS_SCORE(4);
+        else ABS_SCORE(8);
+#undef ABS_SCORE
+    }
     const dim3 tgrid(g.B * g.Hkv);
 #define ABS_TOPK(NT_, KPT_)                                                                                  \
     hipLaunchKernelGGL((k_topk<NT_, KPT_>), tgrid, dim3(NT_), 0, s, g, a.scores, a.stride, a.budget, a.sel, \
                        a.sel_cap, a.count)
+    // ABS_TOPK_NT threads, each holding up to 32 keys; 1024 x 64 beyond that
+    constexpr int NT = ABS_TOPK_NT;
     const int n = a.max_n;
-    if (n <= 512 * 1) ABS_TOPK(512, 1);
-    else if (n <= 512 * 2) ABS_TOPK(512, 2);
-    else if (n <= 512 * 4) ABS_TOPK(512, 4);
-    else if (n <= 512 * 8) ABS_TOPK(512, 8);
-    else if (n <= 512 * 16) ABS_TOPK(512, 16);
-    else if (n <= 512 * 32) ABS_TOPK(512, 32);
+    if (n <= NT * 1) ABS_TOPK(NT, 1);
+    else if (n <= NT * 2) ABS_TOPK(NT, 2);
+    else if (n <= NT * 4) ABS_TOPK(NT, 4);
+    else if (n <= NT * 8) ABS_TOPK(NT, 8);
+    else if (n <= NT * 16) ABS_TOPK(NT, 16);
+    else if (n <= NT * 32) ABS_TOPK(NT, 32);
     else ABS_TOPK(1024, 64);
 #undef ABS_TOPK
     return hipGetLastError();

@@ -72,8 +72,8 @@ typedef enum abs_op {
  *   seq_lens: device, int32 [num_seqs], L_b = cached tokens of sequence b,
  *       the current decode token included.  seq_lens_host: the same values on
  *       the host (launch sizes are computed from it; it must equal seq_lens).
- * Supported: page_size 16, head_dim 64 or 128, num_q_heads / num_kv_heads in
- * 1..8, 1 <= L_b <= max_pages_per_seq * 16.
+ * Supported: page_size 16, head_dim 64 or 128, num_kv_heads <= 64,
+ * num_q_heads / num_kv_heads in 1..8, 1 <= L_b <= max_pages_per_seq * 16.
  */
 typedef struct abs_paged_kv {
     int32_t num_seqs;
@@ -96,7 +96,9 @@ typedef struct abs_paged_kv {
  * Block-size map of one layer (the per-head block-size heatmap printed after
  * Figure 3; static per Figure 5's text).
  *   block_size_host / block_size: host / device int32 [num_kv_heads], each in
- *       {16, 32, 64}; bs_h / 16 is the head's page stride.
+ *       {16, 32, 64}; bs_h / 16 is the head's page stride.  The two must hold
+ *       the same values; this build's kernels take them from the host copy
+ *       (passed in the launch), the device copy must still be non-null.
  *   centroid_off: device int64 [num_seqs * num_kv_heads + 1]; the first
  *       centroid row of (b, h) is centroid_off[b * num_kv_heads + h], with
  *       N_{b,h} = ceil(L_b / bs_h) rows.  Fill it with abs_centroid_offsets().
