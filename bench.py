@@ -3,8 +3,8 @@
 
 One step = the whole decode hot path for one layer over one batch:
 abs_score_select (INT4 centroid scoring + top-K) then abs_sparse_decode
-(split attention over the selected pages + merge), on inputs already resident
-in HBM.  The centroid build (prefill-time) is timed separately and reported
+(split attention over the selected pages, merged in the same launch), on
+inputs already resident in HBM.  The centroid build (prefill-time) is timed separately and reported
 under "build".
 
 Cold-cache honesty: the 256 MB Infinity Cache would hold a step's selected
@@ -17,6 +17,9 @@ Prints ONE JSON line (see the "metric" field).  Options:
     --workload cfgN        0..4 (default 3: batch 4, 128K context, budget 4096)
     --replicas R           layer copies cycled through (default 8)
     --no-cpu-baseline      skip timing the CPU oracle
+    --calibrate-copy MIB   before the timed region, copy MIB MiB device to
+                           device three times (a plain copy kernel of known
+                           size, the scale for hardware byte counters)
     --gpus N               must be 1 (this build runs on one GPU)
 """
 from __future__ import annotations
@@ -34,6 +37,23 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+METRIC = "sparse decode attn queries/s per layer at 32K/128K ctx; achieved HBM GB/s vs peak"
+
+# HBM bytes per launch of the split kernel from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE, each scaled by the same counter's reading for a plain copy of
+# known size (see profiles/), keyed by workload and by a hash of the kernel
+# sources they were taken with; any other source reports null.
+TRAFFIC = {("llama8b-128k-b4-bf16", "e55c41b90776284b"): 68955197}
+KERNEL_SOURCES = ("decode.hip", "device.hpp", "launch.hpp")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_sparse_attention_abs_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -45,6 +65,7 @@ def parse():
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0)
     return ap.parse_args()
 
 
@@ -142,6 +163,15 @@ def main():
     for i in range(max(args.warmup, R)):
         step(i, sh)
     torch.cuda.synchronize()
+    recall = needle_recall(x, sel.cpu().numpy(), cnt.cpu().numpy())
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def capture(fn, n=R):
         g = torch.cuda.CUDAGraph()
@@ -191,8 +221,9 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x, budget, sm, args.cpu_seconds)
 
+    traffic = TRAFFIC.get((w.name, kernel_source_hash()))
     rec = {
-        "metric": "sparse decode attn queries/s per layer at 128K ctx (B=4, budget 4096); achieved HBM GB/s vs peak",
+        "metric": METRIC,
         "value": round(queries_per_s, 1),
         "unit": "queries/s",
         "n_gpus": 1,
@@ -207,9 +238,9 @@ def main():
         "config": {"workload": w.name, "batch": B, "context": int(w.context), "q_heads": Hq,
                    "kv_heads": w.num_kv_heads, "head_dim": D, "token_budget": budget, "page_size": 16,
                    "block_sizes": x.block_size.tolist(), "kv_replicas": R},
-        "roofline": {"bound": "hbm", "kernel": "abs_sparse_decode (split + merge)",
+        "roofline": {"bound": "hbm", "kernel": "k_sparse_decode (abs_sparse_decode: split, merge in the same launch)",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes": ab["decode"], "avg_us": round(dec_avg, 3)},
         "cpu_baseline": cpu,
         "step": {"algorithmic_bytes": ab["step"], "hbm_gbs": round(ab["step"] / (ms_per_step * 1e-3) / 1e9, 1),
@@ -219,8 +250,24 @@ def main():
                  "wall_s": round(wall, 4)},
         "build": {"ms": round(build_med, 4), "algorithmic_bytes": build_bytes,
                   "hbm_gbs": round(build_bytes / (build_med * 1e-3) / 1e9, 1)},
+        "needle_recall": recall,
     }
     print(json.dumps(rec), flush=True)
+
+
+def needle_recall(x, sel, cnt):
+    """Diagnostic, not asserted: per block size, the fraction of planted
+    needles whose block the GPU selected."""
+    hit, tot = {}, {}
+    for (b, h), k in np.ndenumerate(cnt):
+        bs = int(x.block_size[h])
+        chosen = set(sel[b, h, :k].tolist())
+        for t in x.needle_pos[b, h]:
+            if t < 0:
+                continue
+            tot[bs] = tot.get(bs, 0) + 1
+            hit[bs] = hit.get(bs, 0) + (int(t) // bs in chosen)
+    return {str(bs): round(hit[bs] / tot[bs], 4) for bs in sorted(tot)}
 
 
 def cpu_baseline(x, budget, sm, seconds):
