@@ -50,7 +50,7 @@ hipError_t launch_build(const Geom& g, DType dt, const BuildArgs& a, hipStream_t
 // Score + select.
 constexpr int kMaxBlocksPerHead = 65536;   // top-K keeps N_{b,h} keys in registers: 1024 x 64
 
-// The score launch: 512 threads per workgroup, 256 blocks per workgroup.
+// The score launch: 256 blocks per workgroup.
 // When the tiles of all heads fit kMaxScoreTiles, they are listed in the
 // kernel arguments ((b*Hkv + h) << 8 | tile) and the grid has exactly that
 // many workgroups; otherwise the grid is (max tiles per head, B*Hkv).

@@ -27,6 +27,8 @@
 //            keys gives the same pair instead;
 //         4. keep key > tau_key, or key == tau_key and index <= tau_index;
 //            a block scan writes the kept indices in ascending order.
+#include <type_traits>
+
 #include "device.hpp"
 
 namespace absk {
@@ -34,7 +36,7 @@ namespace {
 
 // Build-time tuning: threads of a score workgroup (256 or 512).
 #ifndef ABS_SCORE_NT
-#define ABS_SCORE_NT 512
+#define ABS_SCORE_NT 256
 #endif
 
 // One tile of 256 blocks of (b, h) = bh, by an ABS_SCORE_NT-thread workgroup.
@@ -174,36 +176,52 @@ __global__ __launch_bounds__(NT) void k_topk(Geom g, const float* __restrict__ s
         return;
     }
 
+    // Thread t owns indices [t*KPT, t*KPT + nv); most threads are full (nv =
+    // KPT) and run the unguarded forms of the loops below.
     const int base = threadIdx.x * KPT;
+    const int nv = min(max(N - base, 0), KPT);
+    const bool full = nv == KPT;
     const float* row = scores + (int64_t)bh * stride;
-    uint32_t key[KPT];
-    if constexpr (KPT % 4 == 0) {
+    float f[KPT];
+    if (full) {
+        if constexpr (KPT % 4 == 0) {
 #pragma unroll
-        for (int e = 0; e < KPT; e += 4) {
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (base + e < N) v = *reinterpret_cast<const float4*>(row + base + e);   // rows are padded to 4
-            key[e] = float_key(v.x);
-            key[e + 1] = float_key(v.y);
-            key[e + 2] = float_key(v.z);
-            key[e + 3] = float_key(v.w);
+            for (int e = 0; e < KPT; e += 4) {
+                const float4 v = *reinterpret_cast<const float4*>(row + base + e);
+                f[e] = v.x;
+                f[e + 1] = v.y;
+                f[e + 2] = v.z;
+                f[e + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) f[e] = row[base + e];
         }
     } else {
 #pragma unroll
-        for (int e = 0; e < KPT; ++e) key[e] = float_key(base + e < N ? row[base + e] : 0.0f);
+        for (int e = 0; e < KPT; ++e) f[e] = e < nv ? row[base + e] : 0.0f;
     }
     float mn = __builtin_inff(), mx = -__builtin_inff();
+    if (full) {
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) {
-        if (base + e < N) {
-            mn = fminf(mn, key_float(key[e]));
-            mx = fmaxf(mx, key_float(key[e]));
+        for (int e = 0; e < KPT; ++e) {
+            mn = fminf(mn, f[e]);
+            mx = fmaxf(mx, f[e]);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            if (e < nv) {
+                mn = fminf(mn, f[e]);
+                mx = fmaxf(mx, f[e]);
+            }
         }
     }
 
     __shared__ uint32_t hist[kBins];
     __shared__ uint32_t s_wave[3][NT / 64];          // one per scan: no barrier between reuses
     __shared__ float s_wmax[NT / 64], s_wmin[NT / 64];
-    __shared__ uint32_t s_cand_key[kCandCap];
+    __shared__ float s_cand_val[kCandCap];
     __shared__ int32_t s_cand_idx[kCandCap];
     __shared__ uint32_t s_bin, s_above, s_ncand, s_tau_key;
     __shared__ int32_t s_tau_idx;
@@ -227,15 +245,27 @@ __global__ __launch_bounds__(NT) void k_topk(Geom g, const float* __restrict__ s
     const float inv = (float)kBins / range;
     const bool binned = range > 0.0f && range <= 3.0e38f && inv > 0.0f && inv <= 3.0e38f;
 
-    uint32_t tau_key = 0u;
+    // The threshold: the K-th element in (score desc, index asc) order, as
+    // (tau score, tau index).  Scores compare as floats (-0 == +0).
+    float tau_f = 0.0f;
     int32_t tau_idx = -1;
     bool resolved = false;
-    // bin of a score: monotone non-decreasing in the score
-    auto bin_of = [&](uint32_t k) { return min(kBins - 1, (int)((key_float(k) - mn) * inv)); };
     if (binned) {
+        // bin of a score: monotone non-decreasing in the score; -1 marks an empty slot
+        int bin[KPT];
+        if (full) {
 #pragma unroll
-        for (int e = 0; e < KPT; ++e)
-            if (base + e < N) atomicAdd(&hist[bin_of(key[e])], 1u);
+            for (int e = 0; e < KPT; ++e) {
+                bin[e] = min(kBins - 1, (int)((f[e] - mn) * inv));
+                atomicAdd(&hist[bin[e]], 1u);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) {
+                bin[e] = e < nv ? min(kBins - 1, (int)((f[e] - mn) * inv)) : -1;
+                if (e < nv) atomicAdd(&hist[bin[e]], 1u);
+            }
+        }
         __syncthreads();
         // thread t sums bins kBins-1-t*BPT ... downwards; scan from the top
         constexpr int BPT = kBins / NT;
@@ -264,10 +294,10 @@ __global__ __launch_bounds__(NT) void k_topk(Geom g, const float* __restrict__ s
         const uint32_t need = (uint32_t)K - s_above;                 // 1 <= need <= |bin b*|
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
-            if (base + e < N && bin_of(key[e]) == bstar) {
+            if (bin[e] == bstar) {
                 const uint32_t slot = atomicAdd(&s_ncand, 1u);
                 if (slot < (uint32_t)kCandCap) {
-                    s_cand_key[slot] = key[e];
+                    s_cand_val[slot] = f[e];
                     s_cand_idx[slot] = base + e;
                 }
             }
@@ -276,34 +306,37 @@ __global__ __launch_bounds__(NT) void k_topk(Geom g, const float* __restrict__ s
         const uint32_t nc = s_ncand;
         if (nc <= (uint32_t)kCandCap) {
             for (uint32_t t = threadIdx.x; t < nc; t += NT) {
-                const uint32_t kt = s_cand_key[t];
+                const float vt = s_cand_val[t];
                 const int32_t it = s_cand_idx[t];
                 uint32_t rank = 0;
                 for (uint32_t u = 0; u < nc; ++u) {
-                    const uint32_t ku = s_cand_key[u];
-                    rank += (ku > kt || (ku == kt && s_cand_idx[u] < it)) ? 1u : 0u;
+                    const float vu = s_cand_val[u];
+                    rank += (vu > vt || (vu == vt && s_cand_idx[u] < it)) ? 1u : 0u;
                 }
                 if (rank == need - 1) {
-                    s_tau_key = kt;
+                    s_tau_key = __float_as_uint(vt);
                     s_tau_idx = it;
                 }
             }
             __syncthreads();
-            tau_key = s_tau_key;
+            tau_f = __uint_as_float(s_tau_key);
             tau_idx = s_tau_idx;
             resolved = true;
         }
     }
     if (!resolved) {
-        // crowded threshold bin or degenerate range: 8-bit radix select on the keys
+        // crowded threshold bin or degenerate range: 8-bit radix select on the
+        // order-preserving keys
         uint32_t prefix = 0, mask = 0, need = (uint32_t)K;
         for (int shift = 24; shift >= 0; shift -= 8) {
             __syncthreads();
             for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0u;
             __syncthreads();
 #pragma unroll
-            for (int e = 0; e < KPT; ++e)
-                if (base + e < N && (key[e] & mask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 255u], 1u);
+            for (int e = 0; e < KPT; ++e) {
+                const uint32_t k = float_key(f[e]);
+                if (e < nv && (k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+            }
             __syncthreads();
             if (threadIdx.x < 64) {
                 const int lane = threadIdx.x;   // lane l holds digits 255-4l .. 252-4l
@@ -331,35 +364,45 @@ __global__ __launch_bounds__(NT) void k_topk(Geom g, const float* __restrict__ s
             mask |= 255u << shift;
             need = s_above;
         }
-        tau_key = prefix;
-        // the need-th lowest index among keys equal to tau
+        // the need-th lowest index among keys equal to the threshold key
         uint32_t n_eq = 0;
 #pragma unroll
-        for (int e = 0; e < KPT; ++e) n_eq += (base + e < N && key[e] == tau_key) ? 1u : 0u;
+        for (int e = 0; e < KPT; ++e) n_eq += (e < nv && float_key(f[e]) == prefix) ? 1u : 0u;
         uint32_t total;
         uint32_t r = block_exclusive_scan<NT>(n_eq, s_wave[1], &total);
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
-            if (base + e < N && key[e] == tau_key) {
+            if (e < nv && float_key(f[e]) == prefix) {
                 if (r == need - 1) s_tau_idx = base + e;
                 ++r;
             }
         }
         __syncthreads();
+        tau_f = key_float(prefix);
         tau_idx = s_tau_idx;
     }
 
-    // keep (key > tau_key) or (key == tau_key and index <= tau_idx): exactly K
-    uint64_t keep = 0;
+    // keep (score > tau) or (score == tau and index <= tau index): exactly K
+    using Mask = std::conditional_t<(KPT > 32), uint64_t, uint32_t>;
+    Mask keep = 0;
+    const int tau_rel = tau_idx - base;                 // the tie cut in this thread's indices
+    if (full) {
 #pragma unroll
-    for (int e = 0; e < KPT; ++e)
-        keep |= (base + e < N && (key[e] > tau_key || (key[e] == tau_key && base + e <= tau_idx))) ? 1ull << e : 0ull;
+        for (int e = 0; e < KPT; ++e)
+            keep |= (f[e] > tau_f || (f[e] == tau_f && e <= tau_rel)) ? (Mask)1 << e : (Mask)0;
+    } else {
+#pragma unroll
+        for (int e = 0; e < KPT; ++e)
+            keep |= (e < nv && (f[e] > tau_f || (f[e] == tau_f && e <= tau_rel))) ? (Mask)1 << e : (Mask)0;
+    }
     uint32_t total;
-    const uint32_t pos = block_exclusive_scan<NT>((uint32_t)__builtin_popcountll(keep), s_wave[2], &total);
+    const uint32_t pos = block_exclusive_scan<NT>((uint32_t)__builtin_popcountll((uint64_t)keep), s_wave[2], &total);
+    if (keep != 0) {
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) {
-        const uint32_t p = pos + (uint32_t)__builtin_popcountll(keep & ((1ull << e) - 1ull));
-        if (((keep >> e) & 1ull) && p < (uint32_t)K) out[p] = base + e;
+        for (int e = 0; e < KPT; ++e) {
+            const uint32_t p = pos + (uint32_t)__builtin_popcountll((uint64_t)(keep & (((Mask)1 << e) - 1)));
+            if (((keep >> e) & 1) && p < (uint32_t)K) out[p] = base + e;
+        }
     }
 }
 
