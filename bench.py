@@ -207,10 +207,15 @@ def main():
     total_ms = timed(g_step, reps, g_tail)
     wall = time.perf_counter() - wall0
     ms_per_step = total_ms / K
+    # spread: each replay of R steps timed on its own
+    per_rep = np.array([timed(g_step, 1) / R * 1e3 for _ in range(max(10, min(reps, 50)))])
     # per-stage: the same graphs of one stage only, timed the same way
     sreps = max(1, min(reps, 32))
     sel_us = np.array([timed(g_sel, sreps) / (sreps * R) * 1e3 for _ in range(5)])
     dec_us = np.array([timed(g_dec, sreps) / (sreps * R) * 1e3 for _ in range(5)])
+    # warm Infinity Cache, for reference: R steps on the same layer copy
+    g_warm = capture(lambda i, st: step(0, st))
+    warm_us = float(np.median([timed(g_warm, sreps) / (sreps * R) * 1e3 for _ in range(5)]))
 
     ab = algorithmic_bytes(x, budget, lambda L, bs: min(L, max(1, budget // bs) * bs))
     dec_avg = float(np.median(dec_us))
@@ -247,6 +252,9 @@ def main():
                  "hbm_frac": round(ab["step"] / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                  "score_select_us": round(float(np.median(sel_us)), 3), "sparse_decode_us": round(dec_avg, 3),
                  "sparse_decode_us_min_max": [round(float(dec_us.min()), 3), round(float(dec_us.max()), 3)],
+                 "step_us_p10_p50_p90": [round(float(np.percentile(per_rep, q)), 3) for q in (10, 50, 90)],
+                 "warm_cache_step_us": round(warm_us, 3),
+                 "build_plus_step_us": round(build_med * 1e3 + ms_per_step * 1e3, 3),
                  "wall_s": round(wall, 4)},
         "build": {"ms": round(build_med, 4), "algorithmic_bytes": build_bytes,
                   "hbm_gbs": round(build_bytes / (build_med * 1e-3) / 1e9, 1)},
@@ -273,25 +281,45 @@ def needle_recall(x, sel, cnt):
 def cpu_baseline(x, budget, sm, seconds):
     """The oracle as it stands (oracle/, plain C, fp64, OpenMP over (b, h)) on
     the same host arrays: whole decode steps (score + select + attend over the
-    full batch) repeated for about `seconds`; its centroids are built once,
-    outside the timing."""
+    full batch) repeated for about `seconds` on all host threads, with the
+    stages timed apart; then one step on a single thread.  Its centroids are
+    built once, timed on their own."""
     import oracle as O
+    t0 = time.perf_counter()
     c = O.centroids(x.k_cache, x.page_table, x.seq_lens, x.block_size, x.dtype)
     qz = O.quantize(c, x.seq_lens, x.block_size)
+    build_s = time.perf_counter() - t0
     cap = O.sel_capacity(x.seq_lens, x.block_size, budget)
-    n, t0 = 0, time.perf_counter()
-    while True:
+
+    def one_step():
+        a = time.perf_counter()
         s = O.scores(x.q, qz, x.seq_lens, x.block_size, x.dtype)
         sel, cnt = O.select(s, x.seq_lens, x.block_size, budget, cap)
+        b = time.perf_counter()
         O.attend(x.q, x.k_cache, x.v_cache, x.page_table, x.seq_lens, x.block_size, sel, cnt, sm, x.dtype)
+        return b - a, time.perf_counter() - b
+
+    threads = O.max_threads()
+    n, t_sel, t_att, t0 = 0, 0.0, 0.0, time.perf_counter()
+    while True:
+        a, b = one_step()
+        t_sel += a
+        t_att += b
         n += 1
         el = time.perf_counter() - t0
         if el >= seconds:
             break
+    O.set_threads(1)
+    try:
+        a, b = one_step()
+    finally:
+        O.set_threads(threads)
     B = x.q.shape[0]
-    return {"value": round(n * B / el, 3), "unit": "queries/s", "cores": O.max_threads(), "kind": "oracle",
-            "sample": f"{n} full decode steps (batch {B}) of the same workload, {el:.1f}s; centroids built once "
-                      f"outside the timing"}
+    return {"value": round(n * B / el, 3), "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} full decode steps (batch {B}) of the same workload, {el:.1f}s on {threads} threads; "
+                      f"centroids built once outside the timing",
+            "score_select_ms": round(t_sel / n * 1e3, 3), "attend_ms": round(t_att / n * 1e3, 3),
+            "build_ms": round(build_s * 1e3, 1), "single_thread_step_ms": round((a + b) * 1e3, 2)}
 
 
 if __name__ == "__main__":

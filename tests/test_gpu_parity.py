@@ -157,14 +157,15 @@ def test_largest_head_65536_blocks(oracle_mod):
     _run_and_compare(oracle_mod, x, budget=4096)
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3])
-def test_full_size_sampled(oracle_mod, cfg):
-    """Full-size workload in the benchmark's launch configuration; the oracle
-    recomputes the first and last sequence on their own."""
+@pytest.mark.parametrize("cfg,layer", [(1, 0), (2, 0), (3, 0), (4, 0), (4, 35)])
+def test_full_size_sampled(oracle_mod, cfg, layer):
+    """Full-size workload (one layer of it) in the benchmark's launch
+    configuration; the oracle recomputes the first and last sequence on
+    their own."""
     w = P[cfg]
-    x = W.make_layer(w)
+    x = W.make_layer(w, layer)
     sm = default_scale(w.head_dim)
-    print(f"[gpu parity] full size cfg {cfg}: {w.name} bs={x.block_size.tolist()}", flush=True)
+    print(f"[gpu parity] full size cfg {cfg} layer {layer}: {w.name} bs={x.block_size.tolist()}", flush=True)
     g = GpuLayer(x)
     r = g.run(w.token_budget, sm)
     off = g.kv.centroid_off.cpu().numpy()
