@@ -179,6 +179,69 @@ void oracle_quantize(int B, int Hkv, int D, const int32_t *seq_lens, const int32
     }
 }
 
+/* ---- stage 1c: centroids kept current while decoding -------------------- */
+
+/* The page fixes a static block size per head (Figure 5's text) and INT4
+ * per-channel centroids (Figure 8) but not how they follow appended tokens.
+ * Reading: after sequence b grew from prev_b to L_b tokens (1 <= prev_b <=
+ * L_b), every block holding one of the tokens [prev_b - 1, L_b) -- blocks
+ * j = (prev_b - 1) / bs .. N - 1, so the last, possibly partial block is
+ * always redone -- gets its centroid recomputed exactly as in
+ * oracle_centroids and coded with the head's stored (scale, lo) exactly as
+ * in oracle_quantize, the code clamped to 0..15.  out_of_range[b][h] counts
+ * the (block, channel) codes that were clamped: the rounded quotient fell
+ * outside 0..15, or, in a constant channel (scale 0), the centroid differs
+ * from lo.  A caller rebuilds the whole layer when it wants a new range.
+ * Block j of (b, h) is row row_off[b*Hkv + h] + j of codes (one byte per
+ * channel here), so the offsets may leave room for blocks still to come. */
+void oracle_update(int B, int Hkv, int D, int max_pages, int is_bf16,
+                   const void *k_cache, const int32_t *page_table,
+                   const int32_t *seq_lens, const int32_t *prev_lens, const int32_t *block_size,
+                   const int64_t *row_off, const float *scale, const float *lo,
+                   uint8_t *codes /* [rows][D] */, int32_t *out_of_range /* [B][Hkv] */)
+{
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        for (int h = 0; h < Hkv; ++h) {
+            int64_t L = seq_lens[b];
+            int bs = block_size[h];
+            int64_t N = n_blocks(L, bs);
+            int64_t j_first = (prev_lens[b] - 1) / bs;
+            int64_t row0 = row_off[(int64_t)b * Hkv + h];
+            const float *sc = scale + ((size_t)b * Hkv + h) * D;
+            const float *zp = lo + ((size_t)b * Hkv + h) * D;
+            double *acc = (double *)malloc(sizeof(double) * D);
+            int32_t clamped = 0;
+            for (int64_t j = j_first; j < N; ++j) {
+                int64_t t0 = j * bs;
+                int64_t t1 = t0 + bs < L ? t0 + bs : L;
+                for (int d = 0; d < D; ++d) acc[d] = 0.0;
+                for (int64_t t = t0; t < t1; ++t)
+                    for (int d = 0; d < D; ++d)
+                        acc[d] += cache_at(k_cache, is_bf16, page_table, max_pages, Hkv, D, b, h, t, d);
+                for (int d = 0; d < D; ++d) {
+                    float c = (float)(acc[d] / (double)(t1 - t0));
+                    uint8_t code = 0;
+                    if (sc[d] > 0.0f) {
+                        volatile float diff = c - zp[d];
+                        volatile float quot = diff / sc[d];
+                        float r = rintf(quot);
+                        if (r < 0.0f || r > 15.0f) ++clamped;
+                        if (r < 0.0f) r = 0.0f;
+                        if (r > 15.0f) r = 15.0f;
+                        code = (uint8_t)r;
+                    } else if (c != zp[d]) {
+                        ++clamped;
+                    }
+                    codes[(row0 + j) * D + d] = code;
+                }
+            }
+            out_of_range[(int64_t)b * Hkv + h] = clamped;
+            free(acc);
+        }
+    }
+}
+
 /* ---- stage 2: dot-product estimation ------------------------------------ */
 
 /* Importance score of block j of (b, h): the group query qbar = sum of the

@@ -134,6 +134,106 @@ def test_int4_constant_channel_is_exact(oracle_mod):
     assert (qz.scale[0, 0, np.arange(8) != 3] > 0).all()
 
 
+# ---------------------------------------------------------------- centroids during decode
+
+def _spread_rows(codes, seq_lens, block_size, off):
+    """Compact CSR rows -> the same rows placed at the offsets `off`."""
+    out = np.zeros((int(off[-1]), codes.shape[1]), dtype=np.uint8)
+    r = 0
+    for i, (L, bs) in enumerate([(L, bs) for L in seq_lens for bs in block_size]):
+        n = (int(L) + int(bs) - 1) // int(bs)
+        out[off[i]:off[i] + n] = codes[r:r + n]
+        r += n
+    return out
+
+
+def _code_with_range(c, s, lo):
+    """The quantizer's fp32 steps, written out in numpy: rint((c - lo) / s),
+    clamped; also whether it had to be clamped (scale 0: c != lo)."""
+    c, s, lo = np.float32(c), np.float32(s), np.float32(lo)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.rint(np.float32(np.float32(c - lo) / s))
+    ok = s > 0
+    clamped = np.where(ok, (q < 0) | (q > 15), c != lo)
+    code = np.where(ok, np.clip(q, 0, 15), 0).astype(np.uint8)
+    return code, clamped
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_update_without_appends_reproduces_the_build(oracle_mod, dtype):
+    """Nothing appended: recomputing the last block of every head gives the
+    build's codes, and nothing is out of the range it was built with."""
+    x = W.make_layer(small(dtype, fixed_block_sizes=(16, 32)), seq_lens=[300, 211])
+    c = oracle_mod.centroids(x.k_cache, x.page_table, x.seq_lens, x.block_size, dtype)
+    qz = oracle_mod.quantize(c, x.seq_lens, x.block_size)
+    off = oracle_mod.csr_offsets(x.seq_lens, x.block_size)
+    codes, oor = oracle_mod.update(x.k_cache, x.page_table, x.seq_lens, x.seq_lens, x.block_size, off, qz, dtype)
+    np.testing.assert_array_equal(codes, qz.codes)
+    assert (oor == 0).all()
+
+
+@pytest.mark.parametrize("grow", [1, 15, 16, 17, 100])
+def test_update_after_appends_codes_new_blocks_with_the_old_range(oracle_mod, grow):
+    """Build at L0, append `grow` tokens: blocks holding tokens L0-1 .. L-1
+    get the exact mean of their valid tokens (fsum) coded with the stored
+    (scale, lo) by the quantizer's fp32 steps; earlier blocks are untouched;
+    out_of_range counts the clamped codes.  Rows sit at capacity offsets."""
+    dtype = "bf16"
+    L = np.array([300, 211], dtype=np.int32)
+    L0 = L - grow
+    x = W.make_layer(small(dtype, fixed_block_sizes=(16, 64)), seq_lens=L.tolist())
+    c0 = oracle_mod.centroids(x.k_cache, x.page_table, L0, x.block_size, dtype)
+    qz = oracle_mod.quantize(c0, L0, x.block_size)
+    off = oracle_mod.csr_offsets(L0, x.block_size, capacity_tokens=int(L.max()))
+    start = _spread_rows(qz.codes, L0, x.block_size, off)
+    got, oor = oracle_mod.update(x.k_cache, x.page_table, L, L0, x.block_size, off,
+                                 oracle_mod.Quantized(start, qz.scale, qz.lo), dtype)
+    want = start.copy()
+    for b in range(2):
+        keys = W.contiguous_kv(x, "k", b).astype(np.float64)
+        for h, bs in enumerate(x.block_size.tolist()):
+            n = (int(L[b]) + bs - 1) // bs
+            clamped = 0
+            for j in range((int(L0[b]) - 1) // bs, n):
+                blk = keys[h, j * bs:min((j + 1) * bs, int(L[b]))]
+                cj = np.float32([math.fsum(blk[:, d]) / len(blk) for d in range(blk.shape[1])])
+                code, cl = _code_with_range(cj, qz.scale[b, h], qz.lo[b, h])
+                want[off[b * 2 + h] + j] = code
+                clamped += int(cl.sum())
+            assert oor[b, h] == clamped
+    np.testing.assert_array_equal(got, want)
+
+
+def test_update_counts_clamped_channels(oracle_mod):
+    """Keys appended far outside the built range: the new block's codes clamp
+    to 0 or 15 and every channel of it is counted."""
+    dtype = "f32"
+    x = W.make_layer(small(dtype, fixed_block_sizes=(16, 16), needles_per_head=0), seq_lens=[160, 160])
+    x.k_cache[:, :, :, 0] = np.float32(0.5)          # channel 0 constant: scale 0 when built
+    L0 = np.array([144, 144], dtype=np.int32)
+    c0 = oracle_mod.centroids(x.k_cache, x.page_table, L0, x.block_size, dtype)
+    qz = oracle_mod.quantize(c0, L0, x.block_size)
+    # tokens 144..159 (one new block of 16 per sequence) become large
+    for b in range(2):
+        for t in range(144, 160):
+            pg = x.page_table[b, t // 16]
+            x.k_cache[pg, :, t % 16, :] = np.float32(1e3)
+    off = oracle_mod.csr_offsets(L0, x.block_size, capacity_tokens=160)
+    start = _spread_rows(qz.codes, L0, x.block_size, off)
+    got, oor = oracle_mod.update(x.k_cache, x.page_table, [160, 160], L0, x.block_size, off,
+                                 oracle_mod.Quantized(start, qz.scale, qz.lo), dtype)
+    D = x.k_cache.shape[3]
+    # block 8 (tokens 128..143) is recomputed too, unchanged and in range;
+    # block 9's centroid is 1000 in every channel, above every built range
+    # (channel 0: scale 0, and 1000 != lo)
+    assert (qz.scale[:, :, 0] == 0).all()
+    assert (oor == D).all()
+    for b in range(2):
+        for h in range(2):
+            assert (got[off[b * 2 + h] + 9][1:] == 15).all() and got[off[b * 2 + h] + 9][0] == 0
+            np.testing.assert_array_equal(got[off[b * 2 + h] + 8], start[off[b * 2 + h] + 8])
+
+
 # ---------------------------------------------------------------- estimation
 
 def test_scores_are_group_query_dot_dequantized_centroid(oracle_mod):
