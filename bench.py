@@ -216,6 +216,16 @@ def main():
     # warm Infinity Cache, for reference: R steps on the same layer copy
     g_warm = capture(lambda i, st: step(0, st))
     warm_us = float(np.median([timed(g_warm, sreps) / (sreps * R) * 1e3 for _ in range(5)]))
+    # keeping the centroids current after one appended token per sequence
+    # (abs_update_centroids; the last block of every head is recomputed)
+    oor = torch.zeros((B, w.num_kv_heads), dtype=torch.int32, device=dev)
+
+    def update_call(i, st):
+        r = i % R
+        A.abs_update_centroids(layers[r].kv, layers[r].bmap, cents[r].desc, 1, int(oor.data_ptr()), st)
+
+    g_upd = capture(update_call)
+    upd_us = float(np.median([timed(g_upd, sreps) / (sreps * R) * 1e3 for _ in range(5)]))
 
     ab = algorithmic_bytes(x, budget, lambda L, bs: min(L, max(1, budget // bs) * bs))
     dec_avg = float(np.median(dec_us))
@@ -254,6 +264,7 @@ def main():
                  "sparse_decode_us_min_max": [round(float(dec_us.min()), 3), round(float(dec_us.max()), 3)],
                  "step_us_p10_p50_p90": [round(float(np.percentile(per_rep, q)), 3) for q in (10, 50, 90)],
                  "warm_cache_step_us": round(warm_us, 3),
+                 "update_centroids_us": round(upd_us, 3),
                  "build_plus_step_us": round(build_med * 1e3 + ms_per_step * 1e3, 3),
                  "wall_s": round(wall, 4)},
         "build": {"ms": round(build_med, 4), "algorithmic_bytes": build_bytes,

@@ -26,8 +26,8 @@ ABS_F32, ABS_BF16 = 0, 1
 ABS_OP_BUILD, ABS_OP_SELECT, ABS_OP_DECODE = 0, 1, 2
 
 EXPORTS = ("abs_status_str", "abs_last_error", "abs_total_blocks", "abs_centroid_offsets",
-           "abs_select_capacity", "abs_workspace_bytes", "abs_build_centroids", "abs_score_select",
-           "abs_sparse_decode")
+           "abs_centroid_offsets_capacity", "abs_select_capacity", "abs_workspace_bytes", "abs_build_centroids",
+           "abs_update_centroids", "abs_score_select", "abs_sparse_decode")
 
 
 class abs_paged_kv(C.Structure):
@@ -72,12 +72,16 @@ def lib():
         L.abs_total_blocks.argtypes = [KV, MAP, C.POINTER(C.c_int64)]
         L.abs_centroid_offsets.restype = st
         L.abs_centroid_offsets.argtypes = [KV, MAP, P]
+        L.abs_centroid_offsets_capacity.restype = st
+        L.abs_centroid_offsets_capacity.argtypes = [KV, MAP, i32, P]
         L.abs_select_capacity.restype = st
         L.abs_select_capacity.argtypes = [KV, MAP, i32, C.POINTER(C.c_int32)]
         L.abs_workspace_bytes.restype = st
         L.abs_workspace_bytes.argtypes = [KV, MAP, i32, st, C.POINTER(C.c_size_t)]
         L.abs_build_centroids.restype = st
         L.abs_build_centroids.argtypes = [KV, MAP, CEN, P, C.c_size_t, P]
+        L.abs_update_centroids.restype = st
+        L.abs_update_centroids.argtypes = [KV, MAP, CEN, i32, P, P]
         L.abs_score_select.restype = st
         L.abs_score_select.argtypes = [KV, MAP, CEN, P, i32, P, i32, P, P, C.c_size_t, P]
         L.abs_sparse_decode.restype = st
@@ -114,6 +118,13 @@ def abs_centroid_offsets(kv: abs_paged_kv, bmap: abs_block_map) -> np.ndarray:
     return off
 
 
+def abs_centroid_offsets_capacity(kv: abs_paged_kv, bmap: abs_block_map, capacity_tokens: int) -> np.ndarray:
+    off = np.zeros(kv.num_seqs * kv.num_kv_heads + 1, dtype=np.int64)
+    _check(lib().abs_centroid_offsets_capacity(C.byref(kv), C.byref(bmap), capacity_tokens, off.ctypes.data),
+           "abs_centroid_offsets_capacity")
+    return off
+
+
 def abs_select_capacity(kv: abs_paged_kv, bmap: abs_block_map, token_budget: int) -> int:
     cap = C.c_int32()
     _check(lib().abs_select_capacity(C.byref(kv), C.byref(bmap), token_budget, C.byref(cap)),
@@ -131,6 +142,11 @@ def abs_workspace_bytes(kv: abs_paged_kv, bmap: abs_block_map, token_budget: int
 def abs_build_centroids(kv, bmap, cents, ws_ptr: int, ws_bytes: int, stream: int) -> None:
     _check(lib().abs_build_centroids(C.byref(kv), C.byref(bmap), C.byref(cents), ws_ptr, ws_bytes, stream),
            "abs_build_centroids")
+
+
+def abs_update_centroids(kv, bmap, cents, appended: int, out_of_range_ptr: Optional[int], stream: int) -> None:
+    _check(lib().abs_update_centroids(C.byref(kv), C.byref(bmap), C.byref(cents), appended, out_of_range_ptr,
+                                      stream), "abs_update_centroids")
 
 
 def abs_score_select(kv, bmap, cents, q_ptr: int, token_budget: int, sel_ptr: int, sel_cap: int,
@@ -196,7 +212,10 @@ class PagedKV:
 
     @classmethod
     def from_host(cls, q_heads: int, k_cache: np.ndarray, v_cache: np.ndarray, page_table: np.ndarray,
-                  seq_lens: np.ndarray, block_size: np.ndarray, kv_dtype: str, device="cuda") -> "PagedKV":
+                  seq_lens: np.ndarray, block_size: np.ndarray, kv_dtype: str, device="cuda",
+                  capacity_tokens: Optional[int] = None) -> "PagedKV":
+        """capacity_tokens: leave centroid rows for sequences of up to that
+        many tokens (abs_centroid_offsets_capacity), for later appends."""
         import torch
         sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
         bs = np.ascontiguousarray(block_size, dtype=np.int32)
@@ -204,9 +223,20 @@ class PagedKV:
                    upload(np.ascontiguousarray(page_table, dtype=np.int32), device),
                    upload(sl, device), sl, upload(bs, device), bs,
                    torch.zeros(len(sl) * len(bs) + 1, dtype=torch.int64, device=device), q_heads, kv_dtype)
-        off = abs_centroid_offsets(self.kv, self.bmap)
+        off = (abs_centroid_offsets(self.kv, self.bmap) if capacity_tokens is None
+               else abs_centroid_offsets_capacity(self.kv, self.bmap, capacity_tokens))
         self.centroid_off.copy_(torch.from_numpy(off))
+        self.centroid_rows = int(off[-1])
         return self
+
+    def with_lengths(self, seq_lens: np.ndarray) -> "PagedKV":
+        """The same cache, page table and centroid offsets, other sequence
+        lengths (tokens appended in place); the offsets must have room."""
+        sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        out = PagedKV(self.k_cache, self.v_cache, self.page_table, upload(sl, self.k_cache.device), sl,
+                      self.block_size, self.block_size_host, self.centroid_off, self.num_q_heads, self.kv_dtype)
+        out.centroid_rows = self.centroid_rows
+        return out
 
     @property
     def head_dim(self) -> int:
@@ -237,7 +267,8 @@ class Centroids:
         import torch
         dev = kv.k_cache.device
         B, Hkv, D = kv.kv.num_seqs, kv.kv.num_kv_heads, kv.kv.head_dim
-        return cls(torch.empty(kv.total_blocks(), D // 2, dtype=torch.uint8, device=dev),
+        rows = getattr(kv, "centroid_rows", None) or kv.total_blocks()
+        return cls(torch.zeros(rows, D // 2, dtype=torch.uint8, device=dev),
                    torch.empty(B, Hkv, D, dtype=torch.float32, device=dev),
                    torch.empty(B, Hkv, D, dtype=torch.float32, device=dev))
 
@@ -259,6 +290,13 @@ def build_centroids(kv: PagedKV, cents: Centroids, ws=None, stream: Optional[int
     abs_build_centroids(kv.kv, kv.bmap, cents.desc, _ptr(ws), ws.numel(),
                         current_stream() if stream is None else stream)
     return cents
+
+
+def update_centroids(kv: PagedKV, cents: Centroids, appended: int, out_of_range=None,
+                     stream: Optional[int] = None) -> None:
+    abs_update_centroids(kv.kv, kv.bmap, cents.desc, appended,
+                         _ptr(out_of_range) if out_of_range is not None else None,
+                         current_stream() if stream is None else stream)
 
 
 def score_select(kv: PagedKV, cents: Centroids, q, budget: int, sel, count, ws=None,

@@ -151,8 +151,8 @@ BuildLayout build_layout(const Plan& p) {
     BuildLayout l;
     l.tiles = (int)ceil_div64(p.max_n, absk::kBuildTile);
     const size_t part = align_up((size_t)p.g.B * p.g.Hkv * l.tiles * p.g.D * sizeof(float));
-    l.staging = 0;
-    l.pmin = align_up((size_t)p.total_blocks * p.g.D * sizeof(float));
+    l.staging = 0;   // per (b, h): tiles * kBuildTile rows, whatever the centroid offsets
+    l.pmin = align_up((size_t)p.g.B * p.g.Hkv * l.tiles * absk::kBuildTile * p.g.D * sizeof(float));
     l.pmax = l.pmin + part;
     l.bytes = l.pmax + part;
     return l;
@@ -261,6 +261,25 @@ abs_status abs_centroid_offsets(const abs_paged_kv* kv, const abs_block_map* map
     return ok();
 }
 
+abs_status abs_centroid_offsets_capacity(const abs_paged_kv* kv, const abs_block_map* map, int32_t capacity_tokens,
+                                         int64_t* off_host) {
+    if (off_host == nullptr) return fail(ABS_ERR_INVALID_ARG, "null output");
+    Plan p;
+    if (abs_status st = check_geometry(kv, map, &p)) return st;
+    for (int b = 0; b < kv->num_seqs; ++b)
+        if (capacity_tokens < kv->seq_lens_host[b])
+            return fail(ABS_ERR_INVALID_ARG, "capacity_tokens %d < seq_lens[%d] = %d", capacity_tokens, b,
+                        kv->seq_lens_host[b]);
+    int64_t run = 0;
+    for (int b = 0; b < kv->num_seqs; ++b)
+        for (int h = 0; h < kv->num_kv_heads; ++h) {
+            off_host[(int64_t)b * kv->num_kv_heads + h] = run;
+            run += ceil_div64(capacity_tokens, map->block_size_host[h]);
+        }
+    off_host[(int64_t)kv->num_seqs * kv->num_kv_heads] = run;
+    return ok();
+}
+
 abs_status abs_select_capacity(const abs_paged_kv* kv, const abs_block_map* map, int32_t token_budget,
                                int32_t* sel_cap) {
     if (sel_cap == nullptr) return fail(ABS_ERR_INVALID_ARG, "null output");
@@ -306,6 +325,23 @@ abs_status abs_build_centroids(const abs_paged_kv* kv, const abs_block_map* map,
     a.pmax = reinterpret_cast<float*>(ws_at(workspace, l.pmax));
     a.tiles = l.tiles;
     return hip_status(absk::launch_build(p.g, p.dt, a, static_cast<hipStream_t>(stream)), "build_centroids");
+}
+
+abs_status abs_update_centroids(const abs_paged_kv* kv, const abs_block_map* map, const abs_centroids* cents,
+                                int32_t appended, int32_t* out_of_range, void* stream) {
+    Plan p;
+    if (abs_status st = check_geometry(kv, map, &p)) return st;
+    if (abs_status st = require_device(p, false)) return st;
+    if (cents == nullptr || cents->codes == nullptr || cents->scale == nullptr || cents->lo == nullptr)
+        return fail(ABS_ERR_INVALID_ARG, "null centroid store");
+    if (appended < 0) return fail(ABS_ERR_INVALID_ARG, "appended %d < 0", appended);
+    absk::UpdateArgs a;
+    a.scale = cents->scale;
+    a.lo = cents->lo;
+    a.codes = cents->codes;
+    a.out_of_range = out_of_range;
+    a.appended = appended;
+    return hip_status(absk::launch_update(p.g, p.dt, a, static_cast<hipStream_t>(stream)), "update_centroids");
 }
 
 abs_status abs_score_select(const abs_paged_kv* kv, const abs_block_map* map, const abs_centroids* cents,

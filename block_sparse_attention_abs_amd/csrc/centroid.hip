@@ -2,7 +2,8 @@
 // Figure 1's block representation; Figure 8's INT4 asymmetric per-channel
 // centroids; the mapping figure after Figure 8 for pages -> blocks).
 //
-// Three launches per layer:
+// Three launches per layer (staging rows are (b*Hkv + h) * tiles*64 + j, so
+// they do not depend on the caller's centroid offsets):
 //   mean:     one workgroup per (tile of 64 blocks, b*Hkv + h).  16 lanes own a
 //             cache row (16 x head_dim/16 channels); 16 row-groups work on 16
 //             blocks at a time, streaming each page's 16 rows with 16
@@ -30,7 +31,6 @@ __global__ __launch_bounds__(256) void k_centroid_mean(Geom g, float* __restrict
     const int N = ceil_div(L, bs);
     const int j0 = blockIdx.x * kBuildTile;
     if (j0 >= N) return;                                  // uniform: whole workgroup leaves
-    const int64_t row0 = g.off[bh];
     const int lane = threadIdx.x & (kRowLanes - 1);
     const int grp = threadIdx.x / kRowLanes;
     const T* kbase = reinterpret_cast<const T*>(g.k);
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void k_centroid_mean(Geom g, float* __restrict
             mn[e] = fminf(mn[e], c[e]);
             mx[e] = fmaxf(mx[e], c[e]);
         }
-        float* dst = staging + (row0 + j) * D + lane * VEC;
+        float* dst = staging + ((int64_t)bh * tiles * kBuildTile + j) * D + lane * VEC;
 #pragma unroll
         for (int e = 0; e < VEC; e += 4)
             *reinterpret_cast<float4*>(dst + e) = make_float4(c[e], c[e + 1], c[e + 2], c[e + 3]);
@@ -126,7 +126,7 @@ template <int D>
 __global__ __launch_bounds__(256) void k_centroid_quantize(Geom g, const float* __restrict__ staging,
                                                            const float* __restrict__ scale,
                                                            const float* __restrict__ lo,
-                                                           uint8_t* __restrict__ codes) {
+                                                           uint8_t* __restrict__ codes, int tiles) {
     constexpr int TPB = D / 8;                 // threads per block row
     constexpr int ROWS = 256 / TPB;            // block rows per pass
     const int bh = blockIdx.y;
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) void k_centroid_quantize(Geom g, const float* 
     for (int jj = threadIdx.x / TPB; jj < kBuildTile; jj += ROWS) {
         const int j = j0 + jj;
         if (j >= N) break;
-        const float* src = staging + (row0 + j) * D + c8 * 8;
+        const float* src = staging + ((int64_t)bh * tiles * kBuildTile + j) * D + c8 * 8;
         const float4 u0 = reinterpret_cast<const float4*>(src)[0];
         const float4 u1 = reinterpret_cast<const float4*>(src)[1];
         const float c[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
@@ -171,7 +171,96 @@ hipError_t build_impl(const Geom& g, const BuildArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((k_centroid_mean<T, D>), grid, dim3(256), 0, s, g, a.staging, a.pmin, a.pmax, a.tiles);
     hipLaunchKernelGGL((k_centroid_range<D>), dim3(g.B * g.Hkv), dim3(D), 0, s, g, a.pmin, a.pmax, a.tiles,
                        a.scale, a.lo);
-    hipLaunchKernelGGL((k_centroid_quantize<D>), grid, dim3(256), 0, s, g, a.staging, a.scale, a.lo, a.codes);
+    hipLaunchKernelGGL((k_centroid_quantize<D>), grid, dim3(256), 0, s, g, a.staging, a.scale, a.lo, a.codes,
+                       a.tiles);
+    return hipGetLastError();
+}
+
+// Centroids kept current while decoding (the page fixes static per-head
+// block sizes, Figure 5's text, and INT4 per-channel centroids, Figure 8;
+// how they follow appended tokens is read as: recompute every block holding
+// one of the tokens [L - appended - 1, L) -- always at least the last,
+// possibly partial block -- and code it with the head's stored (scale, lo),
+// clamped to 0..15, counting the clamped codes).  One workgroup per (b, h);
+// each 16-lane row group sums one block's tokens in order, in fp64, as the
+// build does, so the fp32 centroid is the same correctly rounded mean.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_centroid_update(Geom g, int appended, const float* __restrict__ scale,
+                                                         const float* __restrict__ lo, uint8_t* __restrict__ codes,
+                                                         int32_t* __restrict__ out_of_range) {
+    constexpr int VEC = D / kRowLanes;                    // channels per lane
+    constexpr int NW = VEC * Elem<T>::kBytes / 4;
+    constexpr int GROUPS = 256 / kRowLanes;
+    const int bh = blockIdx.x;
+    const int b = bh / g.Hkv, h = bh - b * g.Hkv;
+    const int L = g.seq_lens[b];
+    const int bs = block_size_of(g, h);
+    const int N = ceil_div(L, bs);
+    const int prev = max(1, L - appended);
+    const int j_first = (prev - 1) / bs;
+    const int64_t row0 = g.off[bh];
+    const int lane = threadIdx.x & (kRowLanes - 1);
+    const int grp = threadIdx.x / kRowLanes;
+    const T* kbase = reinterpret_cast<const T*>(g.k);
+    float s[VEC], z[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        s[e] = scale[(int64_t)bh * D + lane * VEC + e];
+        z[e] = lo[(int64_t)bh * D + lane * VEC + e];
+    }
+    __shared__ int s_clamped;
+    if (threadIdx.x == 0) s_clamped = 0;
+    __syncthreads();
+    int clamped = 0;
+    for (int j = j_first + grp; j < N; j += GROUPS) {
+        const int t0 = j * bs;
+        const int t1 = min(t0 + bs, L);
+        double acc[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
+        for (int t = t0; t < t1; t += kPage) {
+            const int page = g.page_table[(int64_t)b * g.max_pages + t / kPage];
+            if (page < 0 || page >= g.num_pages) continue;
+            const T* src = kbase + ((int64_t)page * g.Hkv + h) * kPage * D + lane * VEC;
+            const int rows = min(kPage, t1 - t);
+            Words<NW> w[kPage];
+#pragma unroll
+            for (int r = 0; r < kPage; ++r) w[r] = r < rows ? load_words<NW>(src + r * D) : zero_words<NW>();
+#pragma unroll
+            for (int r = 0; r < kPage; ++r)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) acc[e] += (double)Elem<T>::get(w[r], e);
+        }
+        const double n = (double)(t1 - t0);
+        uint32_t packed = 0;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const float c = (float)(acc[e] / n);
+            uint32_t code = 0;
+            if (s[e] > 0.0f) {
+                const float diff = c - z[e];
+                const float quot = diff / s[e];           // IEEE fp32 division
+                const float r = rintf(quot);
+                clamped += (r < 0.0f || r > 15.0f) ? 1 : 0;
+                code = (uint32_t)fminf(fmaxf(r, 0.0f), 15.0f);
+            } else {
+                clamped += c != z[e] ? 1 : 0;
+            }
+            packed |= code << (4 * e);
+        }
+        uint8_t* dst = codes + (row0 + j) * (D / 2) + lane * (VEC / 2);
+        if constexpr (VEC == 8) *reinterpret_cast<uint32_t*>(dst) = packed;
+        else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
+    }
+    if (clamped != 0) atomicAdd(&s_clamped, clamped);
+    __syncthreads();
+    if (threadIdx.x == 0 && out_of_range != nullptr) out_of_range[bh] = s_clamped;
+}
+
+template <typename T, int D>
+hipError_t update_impl(const Geom& g, const UpdateArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((k_centroid_update<T, D>), dim3(g.B * g.Hkv), dim3(256), 0, s, g, a.appended, a.scale, a.lo,
+                       a.codes, a.out_of_range);
     return hipGetLastError();
 }
 
@@ -180,6 +269,12 @@ hipError_t build_impl(const Geom& g, const BuildArgs& a, hipStream_t s) {
 hipError_t launch_build(const Geom& g, DType dt, const BuildArgs& a, hipStream_t s) {
     if (dt == DType::BF16) return g.D == 128 ? build_impl<uint16_t, 128>(g, a, s) : build_impl<uint16_t, 64>(g, a, s);
     return g.D == 128 ? build_impl<float, 128>(g, a, s) : build_impl<float, 64>(g, a, s);
+}
+
+hipError_t launch_update(const Geom& g, DType dt, const UpdateArgs& a, hipStream_t s) {
+    if (dt == DType::BF16)
+        return g.D == 128 ? update_impl<uint16_t, 128>(g, a, s) : update_impl<uint16_t, 64>(g, a, s);
+    return g.D == 128 ? update_impl<float, 128>(g, a, s) : update_impl<float, 64>(g, a, s);
 }
 
 }  // namespace absk

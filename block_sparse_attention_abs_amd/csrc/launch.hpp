@@ -39,13 +39,25 @@ struct BuildArgs {
     uint8_t* codes;
     float* scale;
     float* lo;
-    float* staging;   // [total_blocks][D] fp32 centroids
+    float* staging;   // [B*Hkv][tiles * kBuildTile][D] fp32 centroids
     float* pmin;      // [B*Hkv][tiles][D]
     float* pmax;      // [B*Hkv][tiles][D]
     int tiles;        // ceil(max N / kBuildTile)
 };
 
 hipError_t launch_build(const Geom& g, DType dt, const BuildArgs& a, hipStream_t s);
+
+// Centroids of the blocks touched by the last `appended` tokens, coded with
+// the stored range.
+struct UpdateArgs {
+    const float* scale;
+    const float* lo;
+    uint8_t* codes;
+    int32_t* out_of_range;   // [B*Hkv] or null
+    int appended;
+};
+
+hipError_t launch_update(const Geom& g, DType dt, const UpdateArgs& a, hipStream_t s);
 
 // Score + select.
 constexpr int kMaxBlocksPerHead = 65536;   // top-K keeps N_{b,h} keys in registers: 1024 x 64

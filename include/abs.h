@@ -135,6 +135,14 @@ abs_status abs_total_blocks(const abs_paged_kv *kv, const abs_block_map *map, in
  * N_{b,h}, b-major then h (only map->block_size_host is read). */
 abs_status abs_centroid_offsets(const abs_paged_kv *kv, const abs_block_map *map, int64_t *off_host);
 
+/* Host: like abs_centroid_offsets, but every (b, h) gets room for
+ * ceil(capacity_tokens / bs_h) rows, so the rows of blocks that later
+ * appends create (abs_update_centroids) already exist; the centroid store
+ * then needs off_host[num_seqs * num_kv_heads] rows.  capacity_tokens must be
+ * at least every L_b, else ABS_ERR_INVALID_ARG. */
+abs_status abs_centroid_offsets_capacity(const abs_paged_kv *kv, const abs_block_map *map,
+                                         int32_t capacity_tokens, int64_t *off_host);
+
 /* Largest K_{b,h} = min(N_{b,h}, max(1, floor(token_budget / bs_h))) over all
  * (b, h): the smallest row length (sel_cap) a selection buffer may have. */
 abs_status abs_select_capacity(const abs_paged_kv *kv, const abs_block_map *map,
@@ -156,6 +164,32 @@ abs_status abs_workspace_bytes(const abs_paged_kv *kv, const abs_block_map *map,
 abs_status abs_build_centroids(const abs_paged_kv *kv, const abs_block_map *map,
                                const abs_centroids *out, void *workspace, size_t workspace_bytes,
                                void *stream);
+
+/*
+ * Keep the centroids current while decoding.  The page fixes static per-head
+ * block sizes (Figure 5's text) and INT4 per-channel centroids (Figure 8) but
+ * not how they follow appended tokens; this call reads it as: after the last
+ * `appended` tokens of every sequence were written to the cache (L_b counts
+ * them), every block holding one of the tokens [L_b - appended - 1, L_b) --
+ * always at least the last, possibly partial block -- gets its centroid
+ * recomputed (mean of its valid tokens, as abs_build_centroids) and coded
+ * with the (scale, lo) already in cents, clamped to 0..15.  The range is not
+ * widened: a caller rebuilds the layer (abs_build_centroids) when it wants a
+ * new one, e.g. when out_of_range grows.
+ *   cents: the store written by abs_build_centroids for this layer; block j
+ *       of (b, h) is row centroid_off[b * num_kv_heads + h] + j, so the
+ *       offsets must leave room for blocks that appends create (use
+ *       abs_centroid_offsets_capacity).
+ *   appended: >= 0, the same for every sequence (0 redoes the last block).
+ *   out_of_range: device int32 [num_seqs][num_kv_heads] or NULL; receives the
+ *       number of (block, channel) codes of this call that were clamped (the
+ *       rounded quotient outside 0..15, or, for a channel with scale 0, a
+ *       centroid other than lo).
+ * No workspace; one launch.
+ */
+abs_status abs_update_centroids(const abs_paged_kv *kv, const abs_block_map *map,
+                                const abs_centroids *cents, int32_t appended, int32_t *out_of_range,
+                                void *stream);
 
 /*
  * Dot-product estimation + top-K (Figure 1; the "Estimation" and "Top-K"

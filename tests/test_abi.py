@@ -25,7 +25,7 @@ def header_functions():
 
 def test_exports_every_declared_call():
     names = header_functions()
-    assert len(names) == 9
+    assert len(names) == 11
     assert sorted(A.EXPORTS) == names
     L = A.lib()
     for n in names:
@@ -91,6 +91,9 @@ def test_geometry_helpers_agree_with_oracle(oracle_mod):
         assert A.abs_select_capacity(h.kv, h.bmap, budget) == oracle_mod.sel_capacity(h.sl, h.bs, budget)
     for op in (A.ABS_OP_BUILD, A.ABS_OP_SELECT, A.ABS_OP_DECODE):
         assert A.abs_workspace_bytes(h.kv, h.bmap, 64, op) > 0
+    cap = A.abs_centroid_offsets_capacity(h.kv, h.bmap, 400)
+    np.testing.assert_array_equal(cap, oracle_mod.csr_offsets(h.sl, h.bs, capacity_tokens=400))
+    assert status_of(lambda: A.abs_centroid_offsets_capacity(h.kv, h.bmap, 299)) == A.ABS_ERR_INVALID_ARG
 
 
 def status_of(fn):
@@ -119,6 +122,7 @@ def test_descriptor_validation(field, value, want):
     setattr(h.kv, field, value)
     assert status_of(lambda: A.abs_total_blocks(h.kv, h.bmap)) == want
     assert status_of(lambda: A.abs_build_centroids(h.kv, h.bmap, h.cents, FAKE, 1 << 30, 0)) == want
+    assert status_of(lambda: A.abs_update_centroids(h.kv, h.bmap, h.cents, 1, None, 0)) == want
 
 
 @pytest.mark.parametrize("sizes,lens,want", [
@@ -153,6 +157,9 @@ def test_call_level_validation():
                                                 need_s, 0)) == I
     assert status_of(lambda: A.abs_sparse_decode(h.kv, h.bmap, FAKE, FAKE, cap, FAKE, 64, float("nan"), FAKE,
                                                  None, FAKE, need_d, 0)) == I
+    assert status_of(lambda: A.abs_update_centroids(h.kv, h.bmap, h.cents, -1, None, 0)) == I
+    assert status_of(lambda: A.abs_update_centroids(h.kv, h.bmap, A.abs_centroids(codes=FAKE, scale=None, lo=FAKE),
+                                                    1, None, 0)) == I
     h.kv.v_cache = None
     assert status_of(lambda: A.abs_sparse_decode(h.kv, h.bmap, FAKE, FAKE, cap, FAKE, 64, 0.125, FAKE, None,
                                                  FAKE, need_d, 0)) == I
