@@ -17,6 +17,9 @@ Prints ONE JSON line (see the "metric" field).  Options:
     --workload cfgN        0..4 (default 3: batch 4, 128K context, budget 4096)
     --replicas R           layer copies cycled through (default 8)
     --no-cpu-baseline      skip timing the CPU oracle
+    --context N            override the workload's context length (tokens)
+    --block-map M          "drawn" (the workload's seeded map) or 16, 32, 64
+                           for a uniform map (all heads one block size)
     --calibrate-copy MIB   before the timed region, copy MIB MiB device to
                            device three times (a plain copy kernel of known
                            size, the scale for hardware byte counters)
@@ -41,9 +44,10 @@ METRIC = "sparse decode attn queries/s per layer at 32K/128K ctx; achieved HBM G
 
 # HBM bytes per launch of the split kernel from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE, each scaled by the same counter's reading for a plain copy of
-# known size (see profiles/), keyed by workload and by a hash of the kernel
-# sources they were taken with; any other source reports null.
-TRAFFIC = {("llama8b-128k-b4-bf16", "e55c41b90776284b"): 68955197}
+# known size (see profiles/), keyed by (workload, context, block map) and by
+# a hash of the kernel sources they were taken with; any other source
+# reports null.
+TRAFFIC = {}
 KERNEL_SOURCES = ("decode.hip", "device.hpp", "launch.hpp")
 
 
@@ -66,6 +70,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", type=int, default=0)
+    ap.add_argument("--context", type=int, default=0)
+    ap.add_argument("--block-map", default="drawn", choices=["drawn", "16", "32", "64"])
     return ap.parse_args()
 
 
@@ -101,10 +107,12 @@ def main():
 
     cfg = int(args.workload.replace("cfg", ""))
     w = W.PRESETS[cfg]
+    if args.context:
+        w = w.scaled(context=args.context)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.time()
-    x = W.make_layer(w)
+    x = W.make_layer(w, block_sizes=None if args.block_map == "drawn" else [int(args.block_map)] * w.num_kv_heads)
     print(f"[bench] generated {w.name} in {time.time() - t0:.1f}s, block sizes {x.block_size.tolist()}",
           file=sys.stderr, flush=True)
     B, Hq, D = x.q.shape
@@ -236,7 +244,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x, budget, sm, args.cpu_seconds)
 
-    traffic = TRAFFIC.get((w.name, kernel_source_hash()))
+    traffic = TRAFFIC.get((w.name, int(w.context), args.block_map, kernel_source_hash()))
     rec = {
         "metric": METRIC,
         "value": round(queries_per_s, 1),
@@ -252,7 +260,7 @@ def main():
         "data": "synthetic (seeded Gaussian Q/K/V, 4 outlier key channels x10, 16 planted needles per head)",
         "config": {"workload": w.name, "batch": B, "context": int(w.context), "q_heads": Hq,
                    "kv_heads": w.num_kv_heads, "head_dim": D, "token_budget": budget, "page_size": 16,
-                   "block_sizes": x.block_size.tolist(), "kv_replicas": R},
+                   "block_sizes": x.block_size.tolist(), "block_map": args.block_map, "kv_replicas": R},
         "roofline": {"bound": "hbm", "kernel": "k_sparse_decode (abs_sparse_decode: split, merge in the same launch)",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
