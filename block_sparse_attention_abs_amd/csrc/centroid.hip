@@ -181,76 +181,87 @@ hipError_t build_impl(const Geom& g, const BuildArgs& a, hipStream_t s) {
 // how they follow appended tokens is read as: recompute every block holding
 // one of the tokens [L - appended - 1, L) -- always at least the last,
 // possibly partial block -- and code it with the head's stored (scale, lo),
-// clamped to 0..15, counting the clamped codes).  One workgroup per (b, h);
-// each 16-lane row group sums one block's tokens in order, in fp64, as the
-// build does, so the fp32 centroid is the same correctly rounded mean.
+// clamped to 0..15, counting the clamped codes).  One workgroup per (b, h).
+// Each 16-lane row group loads one 16-token page of a recomputed block (all
+// pages at once) and sums its rows in order in fp64; the page sums are then
+// added in page order (exact for bf16 keys, like the build's sums) and the
+// mean is coded by one thread per channel.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_centroid_update(Geom g, int appended, const float* __restrict__ scale,
                                                          const float* __restrict__ lo, uint8_t* __restrict__ codes,
                                                          int32_t* __restrict__ out_of_range) {
     constexpr int VEC = D / kRowLanes;                    // channels per lane
     constexpr int NW = VEC * Elem<T>::kBytes / 4;
-    constexpr int GROUPS = 256 / kRowLanes;
+    constexpr int GROUPS = 256 / kRowLanes;               // pages in flight
     const int bh = blockIdx.x;
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
     const int L = g.seq_lens[b];
     const int bs = block_size_of(g, h);
+    const int ppb = bs / kPage;                           // pages per block
     const int N = ceil_div(L, bs);
-    const int prev = max(1, L - appended);
-    const int j_first = (prev - 1) / bs;
+    const int j_first = (max(1, L - appended) - 1) / bs;
     const int64_t row0 = g.off[bh];
     const int lane = threadIdx.x & (kRowLanes - 1);
     const int grp = threadIdx.x / kRowLanes;
     const T* kbase = reinterpret_cast<const T*>(g.k);
-    float s[VEC], z[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-        s[e] = scale[(int64_t)bh * D + lane * VEC + e];
-        z[e] = lo[(int64_t)bh * D + lane * VEC + e];
-    }
+    __shared__ double s_part[GROUPS][D];                  // per page: sum of its valid rows
     __shared__ int s_clamped;
     if (threadIdx.x == 0) s_clamped = 0;
-    __syncthreads();
     int clamped = 0;
-    for (int j = j_first + grp; j < N; j += GROUPS) {
-        const int t0 = j * bs;
-        const int t1 = min(t0 + bs, L);
-        double acc[VEC];
+    // (block, page) items, GROUPS at a time; blocks of a pass are whole
+    const int bpp = max(1, GROUPS / ppb);                 // blocks per pass
+    for (int jb = j_first; jb < N; jb += bpp) {
+        const int nb = min(bpp, N - jb);
+        {
+            const int item = grp, j = jb + item / ppb, pg_in = item % ppb;
+            double acc[VEC];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
-        for (int t = t0; t < t1; t += kPage) {
-            const int page = g.page_table[(int64_t)b * g.max_pages + t / kPage];
-            if (page < 0 || page >= g.num_pages) continue;
-            const T* src = kbase + ((int64_t)page * g.Hkv + h) * kPage * D + lane * VEC;
-            const int rows = min(kPage, t1 - t);
-            Words<NW> w[kPage];
+            for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
+            if (item < nb * ppb) {
+                const int t = j * bs + pg_in * kPage;
+                const int rows = min(kPage, L - t);      // <= 0: page past the end of the sequence
+                if (rows > 0) {
+                    const int page = g.page_table[(int64_t)b * g.max_pages + t / kPage];
+                    if (page >= 0 && page < g.num_pages) {
+                        const T* src = kbase + ((int64_t)page * g.Hkv + h) * kPage * D + lane * VEC;
+                        Words<NW> w[kPage];
 #pragma unroll
-            for (int r = 0; r < kPage; ++r) w[r] = r < rows ? load_words<NW>(src + r * D) : zero_words<NW>();
+                        for (int r = 0; r < kPage; ++r)
+                            w[r] = r < rows ? load_words<NW>(src + r * D) : zero_words<NW>();
 #pragma unroll
-            for (int r = 0; r < kPage; ++r)
+                        for (int r = 0; r < kPage; ++r)
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) acc[e] += (double)Elem<T>::get(w[r], e);
+                            for (int e = 0; e < VEC; ++e) acc[e] += (double)Elem<T>::get(w[r], e);
+                    }
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) s_part[grp][lane * VEC + e] = acc[e];
         }
-        const double n = (double)(t1 - t0);
-        uint32_t packed = 0;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const float c = (float)(acc[e] / n);
+        __syncthreads();
+        // one thread per (block of this pass, channel): page sums in order, mean, code
+        for (int idx = threadIdx.x; idx < nb * D; idx += blockDim.x) {
+            const int k = idx / D, d = idx - k * D, j = jb + k;
+            double sum = 0.0;
+            for (int p = 0; p < ppb; ++p) sum += s_part[k * ppb + p][d];
+            const int n = min(bs, L - j * bs);
+            const float c = (float)(sum / (double)n);
+            const float sc = scale[(int64_t)bh * D + d], z = lo[(int64_t)bh * D + d];
             uint32_t code = 0;
-            if (s[e] > 0.0f) {
-                const float diff = c - z[e];
-                const float quot = diff / s[e];           // IEEE fp32 division
+            if (sc > 0.0f) {
+                const float diff = c - z;
+                const float quot = diff / sc;             // IEEE fp32 division
                 const float r = rintf(quot);
                 clamped += (r < 0.0f || r > 15.0f) ? 1 : 0;
                 code = (uint32_t)fminf(fmaxf(r, 0.0f), 15.0f);
             } else {
-                clamped += c != z[e] ? 1 : 0;
+                clamped += c != z ? 1 : 0;
             }
-            packed |= code << (4 * e);
+            // two channels per byte: the even channel's thread writes the pair
+            const uint32_t other = __shfl_xor(code, 1);
+            if ((d & 1) == 0) codes[(row0 + j) * (D / 2) + d / 2] = (uint8_t)(code | (other << 4));
         }
-        uint8_t* dst = codes + (row0 + j) * (D / 2) + lane * (VEC / 2);
-        if constexpr (VEC == 8) *reinterpret_cast<uint32_t*>(dst) = packed;
-        else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
+        __syncthreads();
     }
     if (clamped != 0) atomicAdd(&s_clamped, clamped);
     __syncthreads();
