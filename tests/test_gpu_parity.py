@@ -206,3 +206,29 @@ def test_decode_repeats_bit_identical():
     ref = outs[0].view(torch.int16)
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int16), ref)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_split_count_invariance(oracle_mod, dtype):
+    """One sequence alone (many small splits) and the same sequence repeated 8
+    times in a batch whose rows share its pages (few large, double-buffered
+    splits): every copy's output equals the single run within fp32 merge
+    rounding (bf16: one output ulp), and all 8 copies agree bit for bit."""
+    w = P[1].scaled(context=8192, token_budget=1024, dtype=dtype)
+    x = W.make_layer(w)
+    sm = default_scale(128)
+    r1 = GpuLayer(x).run(w.token_budget, sm)
+    rep = 8
+    xb = dataclasses.replace(x, q=np.repeat(x.q, rep, axis=0), page_table=np.repeat(x.page_table, rep, axis=0),
+                             seq_lens=np.repeat(x.seq_lens, rep))
+    r8 = GpuLayer(xb).run(w.token_budget, sm)
+    assert (r8.count == r1.count).all()
+    for b in range(rep):
+        np.testing.assert_array_equal(r8.sel[b], r1.sel[0])
+        np.testing.assert_array_equal(r8.out[b], r8.out[0])
+    d = np.abs(r8.out[0].astype(np.float64) - r1.out[0])
+    if dtype == "f32":
+        assert d.max() <= 2e-6, d.max()
+    else:
+        assert (d <= np.abs(r1.out[0]) * 2.0 ** -7 + 1e-6).all(), d.max()
+    assert np.abs(r8.lse[0] - r1.lse[0]).max() <= 1e-5
