@@ -425,23 +425,33 @@ __global__ __launch_bounds__(256 * RG, (DecodeOccupancy<T, D, GT, PIPE, MF>::val
         float mg = NEG, ls = 0.0f;
         float2 acc = make_float2(0.0f, 0.0f);
         for (int s0 = 0; s0 < nact; s0 += 8) {
-            float2 mlv[8], ov[8];   // 16 loads in flight, then the online fold
+            // 16 loads in flight (indices clamped, so no load waits on a
+            // branch), then one max and one weighted sum over the 8 splits
+            float2 mlv[8], ov[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                mlv[k] = s0 + k < nact ? load2_agent(ml + 2 * (s0 + k)) : make_float2(NEG, 0.0f);
-                ov[k] = s0 + k < nact ? load2_agent(po + (int64_t)(s0 + k) * D) : make_float2(0.0f, 0.0f);
+                const int sk = min(s0 + k, nact - 1);
+                mlv[k] = load2_agent(ml + 2 * sk);
+                ov[k] = load2_agent(po + (int64_t)sk * D);
             }
+            float bm = NEG;
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (s0 + k < nact) bm = fmaxf(bm, mlv[k].x);
+            const float mn = fmaxf(mg, bm);
+            if (mn == NEG) continue;                      // only empty partials so far
+            const float a = mg == NEG ? 0.0f : exp2f(mg - mn);
+            ls *= a;
+            acc.x *= a;
+            acc.y *= a;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                if (mlv[k].x == NEG) continue;
-                const float mn = fmaxf(mg, mlv[k].x);
-                const float a = mg == NEG ? 0.0f : exp2f(mg - mn);
-                const float w = exp2f(mlv[k].x - mn);
-                ls = ls * a + mlv[k].y * w;
-                acc.x = acc.x * a + ov[k].x * w;
-                acc.y = acc.y * a + ov[k].y * w;
-                mg = mn;
+                const float w = s0 + k < nact ? exp2f(mlv[k].x - mn) : 0.0f;   // empty partial: m = -inf, w = 0
+                ls = fmaf(mlv[k].y, w, ls);
+                acc.x = fmaf(ov[k].x, w, acc.x);
+                acc.y = fmaf(ov[k].y, w, acc.y);
             }
+            mg = mn;
         }
         write_output(out, lse, bi, d, acc, mg, ls, D);
     }
