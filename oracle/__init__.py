@@ -45,6 +45,8 @@ def lib():
         L.oracle_centroids.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P]
         L.oracle_quantize.argtypes = [i32, i32, i32, P, P, P, P, P, P]
         L.oracle_update.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
+        L.oracle_quantize_fmt.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P]
+        L.oracle_scores_dense.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P]
         L.oracle_scores.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, P]
         L.oracle_select.argtypes = [i32, i32, P, P, i32, P, P, i32, P]
         L.oracle_attend.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, i32, P,
@@ -159,6 +161,43 @@ def update(k_cache, page_table, seq_lens, prev_lens, block_size, row_off, quant:
     lib().oracle_update(B, Hkv, D, pt.shape[1], _is_bf16(dtype), _p(k), _p(pt), _p(sl), _p(pl), _p(bs), _p(off),
                         _p(sc), _p(lo), _p(codes), _p(oor))
     return codes, oor
+
+
+FORMATS = {"int4": 0, "int4_sym": 1, "int8": 2, "int4_tensor": 3, "bf16": 4}
+
+
+@dataclass
+class QuantizedFmt:
+    fmt: str
+    codes: np.ndarray   # uint16 [total_blocks][D]: code values (int4_sym: q + 8), bf16 bit patterns
+    scale: np.ndarray   # f32 [B][Hkv][D] (bf16: 0)
+    lo: np.ndarray      # f32 [B][Hkv][D] (int4_sym: -8*scale; bf16: 0)
+    deq: np.ndarray     # fp64 [total_blocks][D] dequantized centroids
+
+
+def quantize_fmt(cents: np.ndarray, seq_lens, block_size, fmt: str) -> QuantizedFmt:
+    """Centroids in one of the formats of oracle_quantize_fmt."""
+    c = np.ascontiguousarray(cents, dtype=np.float32)
+    sl, bs = _i32(seq_lens), _i32(block_size)
+    B, Hkv, D = len(sl), len(bs), c.shape[1]
+    codes = np.empty(c.shape, dtype=np.uint16)
+    scale = np.empty((B, Hkv, D), dtype=np.float32)
+    lo = np.empty((B, Hkv, D), dtype=np.float32)
+    deq = np.empty(c.shape, dtype=np.float64)
+    lib().oracle_quantize_fmt(FORMATS[fmt], B, Hkv, D, _p(sl), _p(bs), _p(c), _p(codes), _p(scale), _p(lo),
+                              _p(deq))
+    return QuantizedFmt(fmt, codes, scale, lo, deq)
+
+
+def scores_dense(q, deq: np.ndarray, seq_lens, block_size, dtype: str) -> np.ndarray:
+    """fp64 scores from dequantized centroids of any format."""
+    qq = _store(q, dtype)
+    sl, bs = _i32(seq_lens), _i32(block_size)
+    B, Hq, D = qq.shape
+    dq = np.ascontiguousarray(deq, dtype=np.float64)
+    out = np.empty(dq.shape[0], dtype=np.float64)
+    lib().oracle_scores_dense(B, Hq, len(bs), D, _is_bf16(dtype), _p(qq), _p(sl), _p(bs), _p(dq), _p(out))
+    return out
 
 
 def scores(q, quant: Quantized, seq_lens, block_size, dtype: str) -> np.ndarray:

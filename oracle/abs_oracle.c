@@ -242,6 +242,103 @@ void oracle_update(int B, int Hkv, int D, int max_pages, int is_bf16,
     }
 }
 
+/* ---- stage 1d: other centroid formats (precision variants) -------------- */
+
+/* Figure 8 compares centroid precisions; the library can store the centroids
+ * in five formats.  Per (b, h) over its blocks j and channels d:
+ *   0  INT4 asymmetric per channel (oracle_quantize): lo = min_j c, scale =
+ *      (max_j c - lo) / 15, code = clamp(rint((c - lo) / scale), 0, 15);
+ *   1  INT4 symmetric per channel: a = max_j |c|, scale = a / 7,
+ *      q = clamp(rint(c / scale), -7, 7), stored as q + 8; dequantized q*scale
+ *      (lo is reported as -8*scale, the same value in the asymmetric form);
+ *   2  INT8 asymmetric per channel: as 0 with 255 levels, code 0..255;
+ *   3  INT4 asymmetric per (sequence, head): one lo = min over j and d, one
+ *      scale = (max - lo) / 15 for every channel (reported per channel);
+ *   4  bf16: the fp32 centroid rounded to bf16 (nearest, ties to even).
+ * Each fp32 step that decides an integer code is an fp32 operation; a zero
+ * scale gives code 0 (format 1: q = 0).  codes: [total_blocks][D] values
+ * (format 4: bf16 bit patterns); deq: the dequantized centroids in fp64. */
+void oracle_quantize_fmt(int fmt, int B, int Hkv, int D, const int32_t *seq_lens, const int32_t *block_size,
+                         const float *centroids, uint16_t *codes, float *scale, float *lo, double *deq)
+{
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        for (int h = 0; h < Hkv; ++h) {
+            int64_t N = n_blocks(seq_lens[b], block_size[h]);
+            int64_t row0 = first_block(b, h, Hkv, seq_lens, block_size);
+            float *sc = scale + ((size_t)b * Hkv + h) * D;
+            float *zp = lo + ((size_t)b * Hkv + h) * D;
+            float tmn = centroids[row0 * D], tmx = tmn;          /* format 3: over the whole head */
+            for (int64_t j = 0; j < N; ++j)
+                for (int d = 0; d < D; ++d) {
+                    float c = centroids[(row0 + j) * D + d];
+                    if (c < tmn) tmn = c;
+                    if (c > tmx) tmx = c;
+                }
+            for (int d = 0; d < D; ++d) {
+                float mn = centroids[row0 * D + d], mx = mn;
+                for (int64_t j = 1; j < N; ++j) {
+                    float c = centroids[(row0 + j) * D + d];
+                    if (c < mn) mn = c;
+                    if (c > mx) mx = c;
+                }
+                if (fmt == 3) {
+                    mn = tmn;
+                    mx = tmx;
+                }
+                volatile float s = 0.0f;
+                float z = 0.0f;
+                if (fmt == 1) {
+                    float a = -mn > mx ? -mn : mx;              /* max |c| */
+                    s = a / 7.0f;
+                    z = -8.0f * s;
+                } else if (fmt != 4) {
+                    volatile float range = mx - mn;
+                    s = range / (fmt == 2 ? 255.0f : 15.0f);
+                    z = mn;
+                }
+                sc[d] = fmt == 4 ? 0.0f : s;
+                zp[d] = fmt == 4 ? 0.0f : z;
+                for (int64_t j = 0; j < N; ++j) {
+                    float c = centroids[(row0 + j) * D + d];
+                    size_t i = (size_t)(row0 + j) * D + d;
+                    if (fmt == 4) {
+                        uint32_t u;
+                        memcpy(&u, &c, 4);
+                        uint16_t hb = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+                        uint32_t back = (uint32_t)hb << 16;
+                        float f;
+                        memcpy(&f, &back, 4);
+                        codes[i] = hb;
+                        deq[i] = (double)f;
+                    } else if (fmt == 1) {
+                        float r = 0.0f;
+                        if (s > 0.0f) {
+                            volatile float quot = c / s;
+                            r = rintf(quot);
+                            if (r < -7.0f) r = -7.0f;
+                            if (r > 7.0f) r = 7.0f;
+                        }
+                        codes[i] = (uint16_t)(r + 8.0f);
+                        deq[i] = (double)r * (double)s;
+                    } else {
+                        float top = fmt == 2 ? 255.0f : 15.0f, r = 0.0f;
+                        if (s > 0.0f) {
+                            volatile float diff = c - mn;
+                            volatile float quot = diff / s;
+                            r = rintf(quot);
+                            if (r < 0.0f) r = 0.0f;
+                            if (r > top) r = top;
+                        }
+                        codes[i] = (uint16_t)r;
+                        deq[i] = (double)r * (double)s + (double)mn;
+                    }
+                }
+            }
+        }
+    }
+}
+
 /* ---- stage 2: dot-product estimation ------------------------------------ */
 
 /* Importance score of block j of (b, h): the group query qbar = sum of the
@@ -270,6 +367,31 @@ void oracle_scores(int B, int Hq, int Hkv, int D, int is_bf16, const void *q,
                     double chat = (double)codes[(row0 + j) * D + d] * (double)sc[d] + (double)zp[d];
                     s += qbar[d] * chat;
                 }
+                scores[row0 + j] = s;
+            }
+            free(qbar);
+        }
+    }
+}
+
+/* The same estimation from dequantized centroids of any format:
+ * score_j = qbar . chat_j in fp64; chat: [total_blocks][D]. */
+void oracle_scores_dense(int B, int Hq, int Hkv, int D, int is_bf16, const void *q,
+                         const int32_t *seq_lens, const int32_t *block_size, const double *chat, double *scores)
+{
+    int G = Hq / Hkv;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        for (int h = 0; h < Hkv; ++h) {
+            int64_t N = n_blocks(seq_lens[b], block_size[h]);
+            int64_t row0 = first_block(b, h, Hkv, seq_lens, block_size);
+            double *qbar = (double *)calloc((size_t)D, sizeof(double));
+            for (int g = 0; g < G; ++g)
+                for (int d = 0; d < D; ++d)
+                    qbar[d] += elem(q, is_bf16, ((size_t)b * Hq + (size_t)h * G + g) * D + d);
+            for (int64_t j = 0; j < N; ++j) {
+                double s = 0.0;
+                for (int d = 0; d < D; ++d) s += qbar[d] * chat[(row0 + j) * D + d];
                 scores[row0 + j] = s;
             }
             free(qbar);

@@ -134,6 +134,93 @@ def test_int4_constant_channel_is_exact(oracle_mod):
     assert (qz.scale[0, 0, np.arange(8) != 3] > 0).all()
 
 
+# ---------------------------------------------------------------- centroid precision variants
+
+@pytest.mark.parametrize("fmt", ["int4", "int4_sym", "int8", "int4_tensor", "bf16"])
+def test_precision_variant_error_bounds_and_end_codes(oracle_mod, fmt):
+    """Each format's error bound and end codes, from its definition:
+    asymmetric |c_hat - c| <= scale/2 with scale = range/levels (per channel,
+    or per head for int4_tensor), min -> 0 and max -> top code; symmetric
+    scale = max|c|/7, error <= scale/2, the largest |c| -> +-7; bf16: the
+    nearest bf16 (numpy round-to-nearest-even of the fp32 centroid)."""
+    x = W.make_layer(small("bf16", fixed_block_sizes=(16, 32)), seq_lens=[300, 211])
+    c = oracle_mod.centroids(x.k_cache, x.page_table, x.seq_lens, x.block_size, "bf16")
+    qf = oracle_mod.quantize_fmt(c, x.seq_lens, x.block_size, fmt)
+    for b, h, r0, n in oracle_mod.block_rows(x.seq_lens, x.block_size):
+        cb = c[r0:r0 + n].astype(np.float64)
+        dq = qf.deq[r0:r0 + n]
+        codes = qf.codes[r0:r0 + n].astype(np.int64)
+        cols = np.arange(c.shape[1])
+        if fmt == "bf16":
+            want = W.f32_to_bf16_bits(c[r0:r0 + n])
+            np.testing.assert_array_equal(qf.codes[r0:r0 + n], want)
+            np.testing.assert_array_equal(dq, W.bf16_bits_to_f32(want).astype(np.float64))
+            assert (np.abs(dq - cb) <= np.abs(cb) * 2.0 ** -8).all()
+            continue
+        sc = qf.scale[b, h].astype(np.float64)
+        assert (np.abs(dq - cb) <= sc / 2 * (1 + 1e-5) + 1e-7).all()
+        if fmt == "int4_sym":
+            a = np.abs(cb).max(axis=0)
+            np.testing.assert_allclose(sc * 7, a, rtol=1e-6)
+            assert codes.min() >= 1 and codes.max() <= 15
+            q = codes - 8
+            np.testing.assert_array_equal(dq, q * sc)
+            far = np.abs(cb).argmax(axis=0)
+            assert (np.abs(q[far, cols]) == 7).all()
+            np.testing.assert_array_equal(qf.lo[b, h], np.float32(-8) * qf.scale[b, h])
+        else:
+            top = 255 if fmt == "int8" else 15
+            assert codes.max() <= top
+            if fmt == "int4_tensor":
+                assert (qf.scale[b, h] == qf.scale[b, h, 0]).all() and (qf.lo[b, h] == cb.min()).all()
+                np.testing.assert_allclose(sc[0] * 15, cb.max() - cb.min(), rtol=1e-6)
+                assert codes.flat[cb.argmin()] == 0 and codes.flat[cb.argmax()] == 15
+            else:
+                np.testing.assert_array_equal(qf.lo[b, h], c[r0:r0 + n].min(axis=0))
+                np.testing.assert_allclose(sc * top, cb.max(axis=0) - cb.min(axis=0), rtol=1e-6)
+                assert (codes[cb.argmin(axis=0), cols] == 0).all()
+                assert (codes[cb.argmax(axis=0), cols] == top).all()
+            np.testing.assert_array_equal(dq, codes * sc + qf.lo[b, h].astype(np.float64))
+
+
+@pytest.mark.parametrize("fmt", ["int4_sym", "int8"])
+def test_precision_variant_code_is_the_nearest_level(oracle_mod, fmt):
+    """Brute force over the format's levels: the code is the nearest one."""
+    rng = np.random.default_rng(7)
+    c = (rng.standard_normal((200, 16)) * rng.uniform(0.1, 20, 16)).astype(np.float32)
+    qf = oracle_mod.quantize_fmt(c, [200 * 16], [16], fmt)
+    sc = qf.scale[0, 0].astype(np.float64)
+    if fmt == "int8":
+        lv = qf.lo[0, 0][None, :, None] + np.arange(256)[None, None, :] * sc[None, :, None]
+        code = qf.codes.astype(np.int64)
+    else:
+        lv = np.arange(-7, 8)[None, None, :] * sc[None, :, None]
+        code = qf.codes.astype(np.int64) - 1                  # q + 8 -> index into -7..7
+    dist = np.abs(lv - c.astype(np.float64)[:, :, None])
+    srt = np.sort(dist, axis=2)
+    clear = (srt[:, :, 1] - srt[:, :, 0]) > 1e-5 * sc
+    assert clear.mean() > 0.98
+    np.testing.assert_array_equal(code[clear], dist.argmin(axis=2)[clear])
+
+
+def test_dense_scores_agree_with_code_form(oracle_mod):
+    """The two estimation routes agree: qbar . (code*scale + lo) from codes,
+    and qbar . c_hat from the int4 format's dequantized centroids; and the
+    dense route is qbar . c_hat (numpy matmul)."""
+    x = W.make_layer(small("f32", fixed_block_sizes=(16, 64)), seq_lens=[300, 211])
+    c = oracle_mod.centroids(x.k_cache, x.page_table, x.seq_lens, x.block_size, "f32")
+    qz = oracle_mod.quantize(c, x.seq_lens, x.block_size)
+    qf = oracle_mod.quantize_fmt(c, x.seq_lens, x.block_size, "int4")
+    np.testing.assert_array_equal(qf.codes, qz.codes)
+    s1 = oracle_mod.scores(x.q, qz, x.seq_lens, x.block_size, "f32")
+    s2 = oracle_mod.scores_dense(x.q, qf.deq, x.seq_lens, x.block_size, "f32")
+    np.testing.assert_allclose(s1, s2, rtol=1e-13, atol=1e-12)
+    G = x.q.shape[1] // x.k_cache.shape[1]
+    for b, h, r0, n in oracle_mod.block_rows(x.seq_lens, x.block_size):
+        qbar = x.q[b, h * G:(h + 1) * G].astype(np.float64).sum(axis=0)
+        np.testing.assert_allclose(s2[r0:r0 + n], qf.deq[r0:r0 + n] @ qbar, rtol=1e-12, atol=1e-12)
+
+
 # ---------------------------------------------------------------- centroids during decode
 
 def _spread_rows(codes, seq_lens, block_size, off):
