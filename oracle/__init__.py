@@ -44,7 +44,7 @@ def lib():
         L.oracle_k.argtypes = [i64, i32, i32]
         L.oracle_centroids.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P]
         L.oracle_quantize.argtypes = [i32, i32, i32, P, P, P, P, P, P]
-        L.oracle_update.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
+        L.oracle_update.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
         L.oracle_quantize_fmt.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P]
         L.oracle_scores_dense.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P]
         L.oracle_scores.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, P]
@@ -144,26 +144,29 @@ def csr_offsets(seq_lens, block_size, capacity_tokens=None) -> np.ndarray:
     return np.asarray(out, dtype=np.int64)
 
 
-def update(k_cache, page_table, seq_lens, prev_lens, block_size, row_off, quant: Quantized, dtype: str):
+FORMATS = {"int4": 0, "int4_sym": 1, "int8": 2, "int4_tensor": 3, "bf16": 4}
+
+
+def update(k_cache, page_table, seq_lens, prev_lens, block_size, row_off, quant, dtype: str, fmt: str = "int4"):
     """Centroids kept current after appends (see oracle_update): returns a copy
-    of quant.codes ([rows][D], rows addressed through row_off) with the blocks
-    holding tokens [prev_b - 1, L_b) recomputed, and out_of_range [B][Hkv]."""
+    of quant.codes ([rows][D] code values in format fmt, rows addressed through
+    row_off) with the blocks holding tokens [prev_b - 1, L_b) recomputed, and
+    out_of_range [B][Hkv]."""
     k = _store(k_cache, dtype)
     pt, sl, pl, bs = _i32(page_table), _i32(seq_lens), _i32(prev_lens), _i32(block_size)
     off = np.ascontiguousarray(row_off, dtype=np.int64)
     B, Hkv, D = pt.shape[0], k.shape[1], k.shape[3]
-    codes = np.array(quant.codes, dtype=np.uint8, copy=True, order="C")
+    codes = np.array(quant.codes, dtype=np.uint16, copy=True, order="C")
     assert codes.shape[0] >= off[-1] and codes.shape[1] == D
     assert ((pl >= 1) & (pl <= sl)).all()
     sc = np.ascontiguousarray(quant.scale, dtype=np.float32)
     lo = np.ascontiguousarray(quant.lo, dtype=np.float32)
     oor = np.zeros((B, Hkv), dtype=np.int32)
-    lib().oracle_update(B, Hkv, D, pt.shape[1], _is_bf16(dtype), _p(k), _p(pt), _p(sl), _p(pl), _p(bs), _p(off),
-                        _p(sc), _p(lo), _p(codes), _p(oor))
-    return codes, oor
+    lib().oracle_update(FORMATS[fmt], B, Hkv, D, pt.shape[1], _is_bf16(dtype), _p(k), _p(pt), _p(sl), _p(pl),
+                        _p(bs), _p(off), _p(sc), _p(lo), _p(codes), _p(oor))
+    return codes.astype(np.asarray(quant.codes).dtype), oor
 
 
-FORMATS = {"int4": 0, "int4_sym": 1, "int8": 2, "int4_tensor": 3, "bf16": 4}
 
 
 @dataclass

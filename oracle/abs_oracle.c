@@ -187,18 +187,21 @@ void oracle_quantize(int B, int Hkv, int D, const int32_t *seq_lens, const int32
  * L_b), every block holding one of the tokens [prev_b - 1, L_b) -- blocks
  * j = (prev_b - 1) / bs .. N - 1, so the last, possibly partial block is
  * always redone -- gets its centroid recomputed exactly as in
- * oracle_centroids and coded with the head's stored (scale, lo) exactly as
- * in oracle_quantize, the code clamped to 0..15.  out_of_range[b][h] counts
- * the (block, channel) codes that were clamped: the rounded quotient fell
- * outside 0..15, or, in a constant channel (scale 0), the centroid differs
- * from lo.  A caller rebuilds the whole layer when it wants a new range.
- * Block j of (b, h) is row row_off[b*Hkv + h] + j of codes (one byte per
- * channel here), so the offsets may leave room for blocks still to come. */
-void oracle_update(int B, int Hkv, int D, int max_pages, int is_bf16,
+ * oracle_centroids and coded in format fmt (see oracle_quantize_fmt) with the
+ * head's stored (scale, lo), the code clamped to the format's range.
+ * out_of_range[b][h] counts the (block, channel) codes that were clamped: the
+ * rounded quotient fell outside the range (0..15, 0..255, or -7..7 for the
+ * symmetric form), or, in a constant channel (scale 0), the centroid differs
+ * from what code 0 stands for (lo; 0 for the symmetric form); for bf16, a
+ * finite centroid that rounds to an infinity.  A caller rebuilds the whole
+ * layer when it wants a new range.  Block j of (b, h) is row
+ * row_off[b*Hkv + h] + j of codes (one value per channel), so the offsets may
+ * leave room for blocks still to come. */
+void oracle_update(int fmt, int B, int Hkv, int D, int max_pages, int is_bf16,
                    const void *k_cache, const int32_t *page_table,
                    const int32_t *seq_lens, const int32_t *prev_lens, const int32_t *block_size,
                    const int64_t *row_off, const float *scale, const float *lo,
-                   uint8_t *codes /* [rows][D] */, int32_t *out_of_range /* [B][Hkv] */)
+                   uint16_t *codes /* [rows][D] */, int32_t *out_of_range /* [B][Hkv] */)
 {
 #pragma omp parallel for collapse(2) schedule(dynamic)
     for (int b = 0; b < B; ++b) {
@@ -221,17 +224,40 @@ void oracle_update(int B, int Hkv, int D, int max_pages, int is_bf16,
                         acc[d] += cache_at(k_cache, is_bf16, page_table, max_pages, Hkv, D, b, h, t, d);
                 for (int d = 0; d < D; ++d) {
                     float c = (float)(acc[d] / (double)(t1 - t0));
-                    uint8_t code = 0;
-                    if (sc[d] > 0.0f) {
-                        volatile float diff = c - zp[d];
-                        volatile float quot = diff / sc[d];
-                        float r = rintf(quot);
-                        if (r < 0.0f || r > 15.0f) ++clamped;
-                        if (r < 0.0f) r = 0.0f;
-                        if (r > 15.0f) r = 15.0f;
-                        code = (uint8_t)r;
-                    } else if (c != zp[d]) {
-                        ++clamped;
+                    uint16_t code = 0;
+                    if (fmt == 4) {
+                        uint32_t u;
+                        memcpy(&u, &c, 4);
+                        code = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+                        uint32_t back = (uint32_t)code << 16;
+                        float f;
+                        memcpy(&f, &back, 4);
+                        if (isinf(f) && !isinf(c)) ++clamped;
+                    } else if (fmt == 1) {
+                        float r = 0.0f;
+                        if (sc[d] > 0.0f) {
+                            volatile float quot = c / sc[d];
+                            r = rintf(quot);
+                            if (r < -7.0f || r > 7.0f) ++clamped;
+                            if (r < -7.0f) r = -7.0f;
+                            if (r > 7.0f) r = 7.0f;
+                        } else if (c != 0.0f) {
+                            ++clamped;
+                        }
+                        code = (uint16_t)(r + 8.0f);
+                    } else {
+                        float top = fmt == 2 ? 255.0f : 15.0f;
+                        if (sc[d] > 0.0f) {
+                            volatile float diff = c - zp[d];
+                            volatile float quot = diff / sc[d];
+                            float r = rintf(quot);
+                            if (r < 0.0f || r > top) ++clamped;
+                            if (r < 0.0f) r = 0.0f;
+                            if (r > top) r = top;
+                            code = (uint16_t)r;
+                        } else if (c != zp[d]) {
+                            ++clamped;
+                        }
                     }
                     codes[(row0 + j) * D + d] = code;
                 }

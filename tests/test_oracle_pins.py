@@ -225,7 +225,7 @@ def test_dense_scores_agree_with_code_form(oracle_mod):
 
 def _spread_rows(codes, seq_lens, block_size, off):
     """Compact CSR rows -> the same rows placed at the offsets `off`."""
-    out = np.zeros((int(off[-1]), codes.shape[1]), dtype=np.uint8)
+    out = np.zeros((int(off[-1]), codes.shape[1]), dtype=codes.dtype)
     r = 0
     for i, (L, bs) in enumerate([(L, bs) for L in seq_lens for bs in block_size]):
         n = (int(L) + int(bs) - 1) // int(bs)
@@ -319,6 +319,102 @@ def test_update_counts_clamped_channels(oracle_mod):
         for h in range(2):
             assert (got[off[b * 2 + h] + 9][1:] == 15).all() and got[off[b * 2 + h] + 9][0] == 0
             np.testing.assert_array_equal(got[off[b * 2 + h] + 8], start[off[b * 2 + h] + 8])
+
+
+def _code_fmt(c, s, lo, fmt):
+    """Code of fp32 centroid values `c` in format `fmt` with a stored range,
+    written from the format definitions (numpy fp32 steps; bf16 by torch's
+    round-to-nearest-even cast), and which codes were clamped."""
+    c, s, lo = np.float32(c), np.float32(s), np.float32(lo)
+    if fmt == "bf16":
+        code = torch.from_numpy(np.ascontiguousarray(c)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        back = (code.astype(np.uint32) << 16).view(np.float32)
+        return code, np.isinf(back) & ~np.isinf(c)
+    ok = s > 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        if fmt == "int4_sym":
+            q = np.rint(np.float32(c / s))
+            return (np.where(ok, np.clip(q, -7, 7), 0) + 8).astype(np.uint16), np.where(ok, np.abs(q) > 7, c != 0)
+        top = 255 if fmt == "int8" else 15
+        q = np.rint(np.float32(np.float32(c - lo) / s))
+        return np.where(ok, np.clip(q, 0, top), 0).astype(np.uint16), np.where(ok, (q < 0) | (q > top), c != lo)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "int4_sym", "int8", "int4_tensor", "bf16"])
+def test_update_formats_without_appends_reproduce_the_build(oracle_mod, fmt):
+    """Every format: nothing appended, the recomputed last blocks get the
+    build's codes and nothing is clamped."""
+    dtype = "bf16"
+    x = W.make_layer(small(dtype, fixed_block_sizes=(16, 32)), seq_lens=[300, 211])
+    c = oracle_mod.centroids(x.k_cache, x.page_table, x.seq_lens, x.block_size, dtype)
+    qf = oracle_mod.quantize_fmt(c, x.seq_lens, x.block_size, fmt)
+    off = oracle_mod.csr_offsets(x.seq_lens, x.block_size)
+    codes, oor = oracle_mod.update(x.k_cache, x.page_table, x.seq_lens, x.seq_lens, x.block_size, off, qf, dtype,
+                                   fmt)
+    np.testing.assert_array_equal(codes, qf.codes)
+    assert (oor == 0).all()
+
+
+@pytest.mark.parametrize("fmt", ["int4_sym", "int8", "int4_tensor", "bf16"])
+@pytest.mark.parametrize("grow,far", [(1, False), (17, False), (100, False), (16, True)])
+def test_update_formats_after_appends(oracle_mod, fmt, grow, far):
+    """Every other format: after `grow` appended tokens (far: keys of 1000,
+    outside every built range), the recomputed blocks hold the exact mean of
+    their valid tokens (fsum) coded from the format's definition with the
+    stored range; earlier rows are untouched; clamped codes are counted."""
+    dtype = "f32"
+    L = np.array([300, 211], dtype=np.int32)
+    L0 = L - grow
+    x = W.make_layer(small(dtype, fixed_block_sizes=(16, 64)), seq_lens=L.tolist())
+    if far:
+        for b in range(2):
+            for t in range(int(L0[b]), int(L[b])):
+                x.k_cache[x.page_table[b, t // 16], :, t % 16, :] = np.float32(1e3)
+    c0 = oracle_mod.centroids(x.k_cache, x.page_table, L0, x.block_size, dtype)
+    qf = oracle_mod.quantize_fmt(c0, L0, x.block_size, fmt)
+    off = oracle_mod.csr_offsets(L0, x.block_size, capacity_tokens=int(L.max()))
+    start = _spread_rows(qf.codes, L0, x.block_size, off)
+    got, oor = oracle_mod.update(x.k_cache, x.page_table, L, L0, x.block_size, off,
+                                 oracle_mod.QuantizedFmt(fmt, start, qf.scale, qf.lo, None), dtype, fmt)
+    want = start.copy()
+    total = 0
+    for b in range(2):
+        keys = W.contiguous_kv(x, "k", b).astype(np.float64)
+        for h, bs in enumerate(x.block_size.tolist()):
+            n = (int(L[b]) + bs - 1) // bs
+            clamped = 0
+            for j in range((int(L0[b]) - 1) // bs, n):
+                blk = keys[h, j * bs:min((j + 1) * bs, int(L[b]))]
+                cj = np.float32([math.fsum(blk[:, d]) / len(blk) for d in range(blk.shape[1])])
+                code, cl = _code_fmt(cj, qf.scale[b, h], qf.lo[b, h], fmt)
+                want[off[b * 2 + h] + j] = code
+                clamped += int(cl.sum())
+            assert oor[b, h] == clamped
+            total += clamped
+    np.testing.assert_array_equal(got, want)
+    if far:   # the far block clamps in every range-coded format; bf16 holds 1000 exactly
+        assert (total == 0) if fmt == "bf16" else (total > 0)
+
+
+def test_update_bf16_counts_overflow_to_infinity(oracle_mod):
+    """bf16 centroids: a finite fp32 mean above bf16's largest finite value
+    rounds to an infinity and is counted."""
+    dtype = "f32"
+    x = W.make_layer(small(dtype, fixed_block_sizes=(16, 16), needles_per_head=0), seq_lens=[160, 160])
+    L0 = np.array([144, 144], dtype=np.int32)
+    c0 = oracle_mod.centroids(x.k_cache, x.page_table, L0, x.block_size, dtype)
+    qf = oracle_mod.quantize_fmt(c0, L0, x.block_size, "bf16")
+    for b in range(2):
+        for t in range(144, 160):
+            x.k_cache[x.page_table[b, t // 16], :, t % 16, :3] = np.float32(3.4e38)
+    off = oracle_mod.csr_offsets(L0, x.block_size, capacity_tokens=160)
+    start = _spread_rows(qf.codes, L0, x.block_size, off)
+    got, oor = oracle_mod.update(x.k_cache, x.page_table, [160, 160], L0, x.block_size, off,
+                                 oracle_mod.QuantizedFmt("bf16", start, qf.scale, qf.lo, None), dtype, "bf16")
+    assert (oor == 3).all()
+    for b in range(2):
+        for h in range(2):
+            assert (got[off[b * 2 + h] + 9][:3] == 0x7F80).all()
 
 
 # ---------------------------------------------------------------- estimation
