@@ -72,20 +72,23 @@ def parse():
     ap.add_argument("--calibrate-copy", type=int, default=0)
     ap.add_argument("--context", type=int, default=0)
     ap.add_argument("--block-map", default="drawn", choices=["drawn", "16", "32", "64"])
+    ap.add_argument("--centroid-format", default="int4",
+                    choices=["int4", "int4_sym", "int8", "int4_tensor", "bf16"])
     return ap.parse_args()
 
 
-def algorithmic_bytes(x, budget, cap_tokens):
+def algorithmic_bytes(x, budget, cap_tokens, code_bits=4):
     """Bytes the method itself must move per decode step (one layer):
-    selected K and V, the INT4 codes and per-channel (scale, lo), q in, out."""
+    selected K and V, the centroid codes (code_bits per channel) and
+    per-channel (scale, lo), q in, out."""
     B, Hq, D = x.q.shape
     Hkv = x.k_cache.shape[1]
     esz = 2 if x.dtype == "bf16" else 4
     sel_tokens = sum(cap_tokens(int(L), int(bs)) for L in x.seq_lens for bs in x.block_size)
     kv = sel_tokens * D * esz * 2
     blocks = sum((int(L) + int(bs) - 1) // int(bs) for L in x.seq_lens for bs in x.block_size)
-    codes = blocks * D // 2
-    params = B * Hkv * D * 4 * 2
+    codes = blocks * D * code_bits // 8
+    params = B * Hkv * D * 4 * 2 if code_bits != 16 else 0
     qo = B * Hq * D * esz * 2
     return {"kv": kv, "codes": codes, "params": params, "q_out": qo,
             "decode": kv + qo, "step": kv + codes + params + qo, "sel_tokens": sel_tokens}
@@ -127,7 +130,9 @@ def main():
         layers.append(A.PagedKV(base.k_cache.clone(), base.v_cache.clone(), base.page_table, base.seq_lens,
                                 base.seq_lens_host, base.block_size, base.block_size_host, base.centroid_off,
                                 Hq, x.dtype))
-    cents = [A.Centroids.empty(base) for _ in range(R)]
+    fmt = args.centroid_format
+    code_bits = {"int8": 8, "bf16": 16}.get(fmt, 4)
+    cents = [A.Centroids.empty(base, fmt) for _ in range(R)]
     stream = torch.cuda.current_stream()
     sh = int(stream.cuda_stream)
     ws_b = A.workspace(base.workspace_bytes(budget, A.ABS_OP_BUILD), dev)
@@ -149,7 +154,7 @@ def main():
     build_ms = sorted(ev[2 * r].elapsed_time(ev[2 * r + 1]) for r in range(R))
     build_med = build_ms[len(build_ms) // 2]
     k_bytes = int(x.seq_lens.sum()) * w.num_kv_heads * D * (2 if x.dtype == "bf16" else 4)
-    build_bytes = k_bytes + A.abs_total_blocks(base.kv, base.bmap) * D // 2
+    build_bytes = k_bytes + A.abs_total_blocks(base.kv, base.bmap) * A.abs_centroid_row_bytes(D, A.CENTROID_FORMATS[fmt])
 
     def select_call(i, st):
         r = i % R
@@ -235,7 +240,7 @@ def main():
     g_upd = capture(update_call)
     upd_us = float(np.median([timed(g_upd, sreps) / (sreps * R) * 1e3 for _ in range(5)]))
 
-    ab = algorithmic_bytes(x, budget, lambda L, bs: min(L, max(1, budget // bs) * bs))
+    ab = algorithmic_bytes(x, budget, lambda L, bs: min(L, max(1, budget // bs) * bs), code_bits)
     dec_avg = float(np.median(dec_us))
     achieved = ab["decode"] / (dec_avg * 1e-6) / 1e9
     queries_per_s = B / (ms_per_step * 1e-3)
@@ -260,7 +265,8 @@ def main():
         "data": "synthetic (seeded Gaussian Q/K/V, 4 outlier key channels x10, 16 planted needles per head)",
         "config": {"workload": w.name, "batch": B, "context": int(w.context), "q_heads": Hq,
                    "kv_heads": w.num_kv_heads, "head_dim": D, "token_budget": budget, "page_size": 16,
-                   "block_sizes": x.block_size.tolist(), "block_map": args.block_map, "kv_replicas": R},
+                   "block_sizes": x.block_size.tolist(), "block_map": args.block_map, "centroid_format": fmt,
+                   "kv_replicas": R},
         "roofline": {"bound": "hbm", "kernel": "k_sparse_decode (abs_sparse_decode: split, merge in the same launch)",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,

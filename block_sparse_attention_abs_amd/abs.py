@@ -24,9 +24,11 @@ LIB_PATH = os.path.join(_PKG, "libabs.so")
 ABS_OK, ABS_ERR_INVALID_ARG, ABS_ERR_UNSUPPORTED, ABS_ERR_WORKSPACE, ABS_ERR_HIP = range(5)
 ABS_F32, ABS_BF16 = 0, 1
 ABS_OP_BUILD, ABS_OP_SELECT, ABS_OP_DECODE = 0, 1, 2
+# abs_centroid_format, by name
+CENTROID_FORMATS = {"int4": 0, "int4_sym": 1, "int8": 2, "int4_tensor": 3, "bf16": 4}
 
 EXPORTS = ("abs_status_str", "abs_last_error", "abs_total_blocks", "abs_centroid_offsets",
-           "abs_centroid_offsets_capacity", "abs_select_capacity", "abs_workspace_bytes", "abs_build_centroids",
+           "abs_centroid_offsets_capacity", "abs_centroid_row_bytes", "abs_select_capacity", "abs_workspace_bytes", "abs_build_centroids",
            "abs_update_centroids", "abs_score_select", "abs_sparse_decode")
 
 
@@ -43,7 +45,8 @@ class abs_block_map(C.Structure):
 
 
 class abs_centroids(C.Structure):
-    _fields_ = [("codes", C.c_void_p), ("scale", C.c_void_p), ("lo", C.c_void_p)]
+    _fields_ = [("codes", C.c_void_p), ("scale", C.c_void_p), ("lo", C.c_void_p), ("format", C.c_int32),
+                ("reserved0", C.c_int32)]
 
 
 class AbsError(RuntimeError):
@@ -74,6 +77,8 @@ def lib():
         L.abs_centroid_offsets.argtypes = [KV, MAP, P]
         L.abs_centroid_offsets_capacity.restype = st
         L.abs_centroid_offsets_capacity.argtypes = [KV, MAP, i32, P]
+        L.abs_centroid_row_bytes.restype = st
+        L.abs_centroid_row_bytes.argtypes = [i32, i32, C.POINTER(C.c_int64)]
         L.abs_select_capacity.restype = st
         L.abs_select_capacity.argtypes = [KV, MAP, i32, C.POINTER(C.c_int32)]
         L.abs_workspace_bytes.restype = st
@@ -123,6 +128,12 @@ def abs_centroid_offsets_capacity(kv: abs_paged_kv, bmap: abs_block_map, capacit
     _check(lib().abs_centroid_offsets_capacity(C.byref(kv), C.byref(bmap), capacity_tokens, off.ctypes.data),
            "abs_centroid_offsets_capacity")
     return off
+
+
+def abs_centroid_row_bytes(head_dim: int, fmt: int) -> int:
+    n = C.c_int64()
+    _check(lib().abs_centroid_row_bytes(head_dim, fmt, C.byref(n)), "abs_centroid_row_bytes")
+    return n.value
 
 
 def abs_select_capacity(kv: abs_paged_kv, bmap: abs_block_map, token_budget: int) -> int:
@@ -254,23 +265,26 @@ class PagedKV:
 
 @dataclass
 class Centroids:
-    codes: object      # uint8 [total_blocks][D/2]
+    codes: object      # uint8 [total_blocks][row bytes]
     scale: object      # f32 [B][Hkv][D]
     lo: object         # f32 [B][Hkv][D]
+    fmt: str = "int4"  # a CENTROID_FORMATS name
     desc: abs_centroids = field(init=False)
 
     def __post_init__(self):
-        self.desc = abs_centroids(codes=_ptr(self.codes), scale=_ptr(self.scale), lo=_ptr(self.lo))
+        self.desc = abs_centroids(codes=_ptr(self.codes), scale=_ptr(self.scale), lo=_ptr(self.lo),
+                                  format=CENTROID_FORMATS[self.fmt], reserved0=0)
 
     @classmethod
-    def empty(cls, kv: PagedKV) -> "Centroids":
+    def empty(cls, kv: PagedKV, fmt: str = "int4") -> "Centroids":
         import torch
         dev = kv.k_cache.device
         B, Hkv, D = kv.kv.num_seqs, kv.kv.num_kv_heads, kv.kv.head_dim
         rows = getattr(kv, "centroid_rows", None) or kv.total_blocks()
-        return cls(torch.zeros(rows, D // 2, dtype=torch.uint8, device=dev),
+        rb = abs_centroid_row_bytes(D, CENTROID_FORMATS[fmt])
+        return cls(torch.zeros(rows, rb, dtype=torch.uint8, device=dev),
                    torch.empty(B, Hkv, D, dtype=torch.float32, device=dev),
-                   torch.empty(B, Hkv, D, dtype=torch.float32, device=dev))
+                   torch.empty(B, Hkv, D, dtype=torch.float32, device=dev), fmt)
 
 
 def current_stream() -> int:

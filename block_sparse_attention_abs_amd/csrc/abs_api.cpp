@@ -215,6 +215,17 @@ DecodeLayout decode_layout(const Plan& p) {
     return l;
 }
 
+abs_status check_centroids(const abs_centroids* c) {
+    if (c == nullptr || c->codes == nullptr || c->scale == nullptr || c->lo == nullptr)
+        return fail(ABS_ERR_INVALID_ARG, "null centroid store");
+    if (c->format < ABS_CENT_INT4 || c->format > ABS_CENT_BF16)
+        return fail(ABS_ERR_INVALID_ARG, "unknown centroid format %d", c->format);
+    if (c->reserved0 != 0) return fail(ABS_ERR_INVALID_ARG, "abs_centroids.reserved0 must be 0");
+    if (reinterpret_cast<uintptr_t>(c->codes) % 16 != 0)
+        return fail(ABS_ERR_INVALID_ARG, "centroid codes are not 16-byte aligned");
+    return ok();
+}
+
 char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
 abs_status hip_status(hipError_t e, const char* what) {
@@ -280,6 +291,15 @@ abs_status abs_centroid_offsets_capacity(const abs_paged_kv* kv, const abs_block
     return ok();
 }
 
+abs_status abs_centroid_row_bytes(int32_t head_dim, int32_t format, int64_t* bytes) {
+    if (bytes == nullptr) return fail(ABS_ERR_INVALID_ARG, "null output");
+    if (head_dim < 1) return fail(ABS_ERR_INVALID_ARG, "head_dim %d < 1", head_dim);
+    if (format < ABS_CENT_INT4 || format > ABS_CENT_BF16)
+        return fail(ABS_ERR_INVALID_ARG, "unknown centroid format %d", format);
+    *bytes = absk::row_bytes(head_dim, format);
+    return ok();
+}
+
 abs_status abs_select_capacity(const abs_paged_kv* kv, const abs_block_map* map, int32_t token_budget,
                                int32_t* sel_cap) {
     if (sel_cap == nullptr) return fail(ABS_ERR_INVALID_ARG, "null output");
@@ -311,8 +331,7 @@ abs_status abs_build_centroids(const abs_paged_kv* kv, const abs_block_map* map,
     Plan p;
     if (abs_status st = check_geometry(kv, map, &p)) return st;
     if (abs_status st = require_device(p, false)) return st;
-    if (out == nullptr || out->codes == nullptr || out->scale == nullptr || out->lo == nullptr)
-        return fail(ABS_ERR_INVALID_ARG, "null centroid output");
+    if (abs_status st = check_centroids(out)) return st;
     const BuildLayout l = build_layout(p);
     if (workspace == nullptr || workspace_bytes < l.bytes)
         return fail(ABS_ERR_WORKSPACE, "build needs %zu workspace bytes, got %zu", l.bytes, workspace_bytes);
@@ -324,6 +343,7 @@ abs_status abs_build_centroids(const abs_paged_kv* kv, const abs_block_map* map,
     a.pmin = reinterpret_cast<float*>(ws_at(workspace, l.pmin));
     a.pmax = reinterpret_cast<float*>(ws_at(workspace, l.pmax));
     a.tiles = l.tiles;
+    a.fmt = out->format;
     return hip_status(absk::launch_build(p.g, p.dt, a, static_cast<hipStream_t>(stream)), "build_centroids");
 }
 
@@ -332,8 +352,7 @@ abs_status abs_update_centroids(const abs_paged_kv* kv, const abs_block_map* map
     Plan p;
     if (abs_status st = check_geometry(kv, map, &p)) return st;
     if (abs_status st = require_device(p, false)) return st;
-    if (cents == nullptr || cents->codes == nullptr || cents->scale == nullptr || cents->lo == nullptr)
-        return fail(ABS_ERR_INVALID_ARG, "null centroid store");
+    if (abs_status st = check_centroids(cents)) return st;
     if (appended < 0) return fail(ABS_ERR_INVALID_ARG, "appended %d < 0", appended);
     absk::UpdateArgs a;
     a.scale = cents->scale;
@@ -341,6 +360,7 @@ abs_status abs_update_centroids(const abs_paged_kv* kv, const abs_block_map* map
     a.codes = cents->codes;
     a.out_of_range = out_of_range;
     a.appended = appended;
+    a.fmt = cents->format;
     return hip_status(absk::launch_update(p.g, p.dt, a, static_cast<hipStream_t>(stream)), "update_centroids");
 }
 
@@ -351,8 +371,7 @@ abs_status abs_score_select(const abs_paged_kv* kv, const abs_block_map* map, co
     if (abs_status st = check_geometry(kv, map, &p)) return st;
     if (abs_status st = require_device(p, false)) return st;
     if (abs_status st = plan_budget(kv, map, token_budget, &p)) return st;
-    if (cents == nullptr || cents->codes == nullptr || cents->scale == nullptr || cents->lo == nullptr)
-        return fail(ABS_ERR_INVALID_ARG, "null centroid store");
+    if (abs_status st = check_centroids(cents)) return st;
     if (q == nullptr || sel == nullptr || sel_count == nullptr)
         return fail(ABS_ERR_INVALID_ARG, "null q, sel or sel_count");
     if (sel_cap < p.sel_cap) return fail(ABS_ERR_INVALID_ARG, "sel_cap %d < required %d", sel_cap, p.sel_cap);
@@ -365,6 +384,7 @@ abs_status abs_score_select(const abs_paged_kv* kv, const abs_block_map* map, co
     a.codes = cents->codes;
     a.scale = cents->scale;
     a.lo = cents->lo;
+    a.fmt = cents->format;
     a.q = q;
     a.scores = reinterpret_cast<float*>(workspace);
     a.stride = score_stride(p);

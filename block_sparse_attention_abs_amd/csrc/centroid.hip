@@ -12,6 +12,12 @@
 //             min/max of the tile is reduced with shuffles + LDS.
 //   range:    per (b, h, channel): min/max over tiles -> lo, scale (fp32).
 //   quantize: code = clamp(rint((c - lo) / scale), 0, 15), two per byte.
+// The other storage formats (Figure 8's precision comparison) change only
+// range and quantize: INT4 symmetric (scale = max|c| / 7, q = clamp(rint(c /
+// scale), -7, 7) stored as q + 8, lo reported as -8 * scale), INT8 (255
+// levels, one byte per channel), INT4 with one range per (sequence, head)
+// (min/max over every block and channel), and bf16 (the fp32 mean rounded to
+// nearest even; scale and lo are 0).
 #include "device.hpp"
 
 namespace absk {
@@ -103,7 +109,7 @@ __global__ __launch_bounds__(256) void k_centroid_mean(Geom g, float* __restrict
 
 template <int D>
 __global__ __launch_bounds__(D) void k_centroid_range(Geom g, const float* __restrict__ pmin,
-                                                      const float* __restrict__ pmax, int tiles,
+                                                      const float* __restrict__ pmax, int tiles, int fmt,
                                                       float* __restrict__ scale, float* __restrict__ lo) {
     const int bh = blockIdx.x;
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
@@ -115,20 +121,86 @@ __global__ __launch_bounds__(D) void k_centroid_range(Geom g, const float* __res
         a = fminf(a, pmin[((int64_t)bh * tiles + t) * D + d]);
         z = fmaxf(z, pmax[((int64_t)bh * tiles + t) * D + d]);
     }
-    const float range = z - a;        // fp32
-    const float s = range / 15.0f;    // IEEE fp32 division
+    if (fmt == kInt4Tensor) {   // one range for the whole head: min/max over the channels too
+        __shared__ float s_mn[D / 64], s_mx[D / 64];
+        for (int o = 32; o > 0; o >>= 1) {
+            a = fminf(a, __shfl_xor(a, o));
+            z = fmaxf(z, __shfl_xor(z, o));
+        }
+        if ((d & 63) == 0) {
+            s_mn[d / 64] = a;
+            s_mx[d / 64] = z;
+        }
+        __syncthreads();
+        a = s_mn[0];
+        z = s_mx[0];
+#pragma unroll
+        for (int w = 1; w < D / 64; ++w) {
+            a = fminf(a, s_mn[w]);
+            z = fmaxf(z, s_mx[w]);
+        }
+    }
+    float s = 0.0f, zp = 0.0f;
+    if (fmt == kInt4Sym) {
+        const float amax = -a > z ? -a : z;   // max |c|
+        s = amax / 7.0f;                      // IEEE fp32 division
+        zp = -8.0f * s;
+    } else if (fmt != kBf16) {
+        const float range = z - a;            // fp32
+        s = range / (fmt == kInt8 ? 255.0f : 15.0f);
+        zp = a;
+    }
     scale[(int64_t)bh * D + d] = s;
-    lo[(int64_t)bh * D + d] = a;
+    lo[(int64_t)bh * D + d] = zp;
 }
 
-// One thread per (block, 8 channels): reads 32 B of fp32 centroid, writes 4 B of codes.
-template <int D>
+// Code of one fp32 centroid value under format FMT with the head's (s, z).
+// `clamped` is set when the value lies outside what the code can express.
+template <int FMT>
+__device__ __forceinline__ uint32_t code_of(float c, float s, float z, bool* clamped) {
+    if constexpr (FMT == kBf16) {
+        const uint32_t u = __float_as_uint(c);
+        const uint32_t hb = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;   // round to nearest even
+        *clamped = ((hb & 0x7FFFu) == 0x7F80u) && ((u & 0x7FFFFFFFu) < 0x7F800000u);   // finite -> inf
+        return hb;
+    } else if constexpr (FMT == kInt4Sym) {
+        float r = 0.0f;
+        if (s > 0.0f) {
+            const float quot = c / s;            // IEEE fp32 division
+            r = rintf(quot);
+            *clamped = r < -7.0f || r > 7.0f;
+            r = fminf(fmaxf(r, -7.0f), 7.0f);
+        } else {
+            *clamped = c != 0.0f;
+        }
+        return (uint32_t)(r + 8.0f);
+    } else {
+        constexpr float top = FMT == kInt8 ? 255.0f : 15.0f;
+        float r = 0.0f;
+        if (s > 0.0f) {
+            const float diff = c - z;
+            const float quot = diff / s;         // IEEE fp32 division
+            r = rintf(quot);
+            *clamped = r < 0.0f || r > top;
+            r = fminf(fmaxf(r, 0.0f), top);
+        } else {
+            *clamped = c != z;
+        }
+        return (uint32_t)r;
+    }
+}
+
+// One thread per (block, 8 channels): reads 32 B of fp32 centroid, writes
+// the 8 codes (4, 8 or 16 B).
+template <int D, int FMT>
 __global__ __launch_bounds__(256) void k_centroid_quantize(Geom g, const float* __restrict__ staging,
                                                            const float* __restrict__ scale,
                                                            const float* __restrict__ lo,
                                                            uint8_t* __restrict__ codes, int tiles) {
     constexpr int TPB = D / 8;                 // threads per block row
     constexpr int ROWS = 256 / TPB;            // block rows per pass
+    constexpr int BITS = fmt_bits(FMT);
+    constexpr int64_t RB = row_bytes(D, FMT);
     const int bh = blockIdx.y;
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
     const int N = ceil_div(g.seq_lens[b], block_size_of(g, h));
@@ -149,19 +221,24 @@ __global__ __launch_bounds__(256) void k_centroid_quantize(Geom g, const float* 
         const float4 u0 = reinterpret_cast<const float4*>(src)[0];
         const float4 u1 = reinterpret_cast<const float4*>(src)[1];
         const float c[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-        uint32_t packed = 0;
+        uint32_t code[8];
+        bool unused;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            uint32_t code = 0;
-            if (s[e] > 0.0f) {
-                const float diff = c[e] - z[e];
-                const float quot = diff / s[e];          // IEEE fp32 division
-                const float r = fminf(fmaxf(rintf(quot), 0.0f), 15.0f);
-                code = (uint32_t)r;
-            }
-            packed |= code << (4 * e);
+        for (int e = 0; e < 8; ++e) code[e] = code_of<FMT>(c[e], s[e], z[e], &unused);
+        uint8_t* dst = codes + (row0 + j) * RB + c8 * BITS;   // 8 channels = BITS bytes
+        if constexpr (BITS == 4) {
+            uint32_t packed = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) packed |= code[e] << (4 * e);
+            *reinterpret_cast<uint32_t*>(dst) = packed;
+        } else if constexpr (BITS == 8) {
+            *reinterpret_cast<uint2*>(dst) =
+                make_uint2(code[0] | code[1] << 8 | code[2] << 16 | code[3] << 24,
+                           code[4] | code[5] << 8 | code[6] << 16 | code[7] << 24);
+        } else {
+            *reinterpret_cast<uint4*>(dst) = make_uint4(code[0] | code[1] << 16, code[2] | code[3] << 16,
+                                                        code[4] | code[5] << 16, code[6] | code[7] << 16);
         }
-        *reinterpret_cast<uint32_t*>(codes + (row0 + j) * (D / 2) + c8 * 4) = packed;
     }
 }
 
@@ -169,10 +246,18 @@ template <typename T, int D>
 hipError_t build_impl(const Geom& g, const BuildArgs& a, hipStream_t s) {
     const dim3 grid(a.tiles, g.B * g.Hkv);
     hipLaunchKernelGGL((k_centroid_mean<T, D>), grid, dim3(256), 0, s, g, a.staging, a.pmin, a.pmax, a.tiles);
-    hipLaunchKernelGGL((k_centroid_range<D>), dim3(g.B * g.Hkv), dim3(D), 0, s, g, a.pmin, a.pmax, a.tiles,
+    hipLaunchKernelGGL((k_centroid_range<D>), dim3(g.B * g.Hkv), dim3(D), 0, s, g, a.pmin, a.pmax, a.tiles, a.fmt,
                        a.scale, a.lo);
-    hipLaunchKernelGGL((k_centroid_quantize<D>), grid, dim3(256), 0, s, g, a.staging, a.scale, a.lo, a.codes,
-                       a.tiles);
+#define ABS_QUANT(F_)                                                                                         \
+    hipLaunchKernelGGL((k_centroid_quantize<D, F_>), grid, dim3(256), 0, s, g, a.staging, a.scale, a.lo, a.codes, \
+                       a.tiles)
+    switch (a.fmt) {
+        case kInt4Sym: ABS_QUANT(kInt4Sym); break;
+        case kInt8: ABS_QUANT(kInt8); break;
+        case kBf16: ABS_QUANT(kBf16); break;
+        default: ABS_QUANT(kInt4); break;   // kInt4 and kInt4Tensor: the same coding, per-channel (s, lo)
+    }
+#undef ABS_QUANT
     return hipGetLastError();
 }
 
@@ -181,18 +266,20 @@ hipError_t build_impl(const Geom& g, const BuildArgs& a, hipStream_t s) {
 // how they follow appended tokens is read as: recompute every block holding
 // one of the tokens [L - appended - 1, L) -- always at least the last,
 // possibly partial block -- and code it with the head's stored (scale, lo),
-// clamped to 0..15, counting the clamped codes).  One workgroup per (b, h).
+// clamped to the format's code range, counting the clamped codes).  One workgroup per (b, h).
 // Each 16-lane row group loads one 16-token page of a recomputed block (all
 // pages at once) and sums its rows in order in fp64; the page sums are then
 // added in page order (exact for bf16 keys, like the build's sums) and the
 // mean is coded by one thread per channel.
-template <typename T, int D>
+template <typename T, int D, int FMT>
 __global__ __launch_bounds__(256) void k_centroid_update(Geom g, int appended, const float* __restrict__ scale,
                                                          const float* __restrict__ lo, uint8_t* __restrict__ codes,
                                                          int32_t* __restrict__ out_of_range) {
     constexpr int VEC = D / kRowLanes;                    // channels per lane
     constexpr int NW = VEC * Elem<T>::kBytes / 4;
     constexpr int GROUPS = 256 / kRowLanes;               // pages in flight
+    constexpr int BITS = fmt_bits(FMT);
+    constexpr int64_t RB = row_bytes(D, FMT);
     const int bh = blockIdx.x;
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
     const int L = g.seq_lens[b];
@@ -247,19 +334,18 @@ __global__ __launch_bounds__(256) void k_centroid_update(Geom g, int appended, c
             const int n = min(bs, L - j * bs);
             const float c = (float)(sum / (double)n);
             const float sc = scale[(int64_t)bh * D + d], z = lo[(int64_t)bh * D + d];
-            uint32_t code = 0;
-            if (sc > 0.0f) {
-                const float diff = c - z;
-                const float quot = diff / sc;             // IEEE fp32 division
-                const float r = rintf(quot);
-                clamped += (r < 0.0f || r > 15.0f) ? 1 : 0;
-                code = (uint32_t)fminf(fmaxf(r, 0.0f), 15.0f);
+            bool out;
+            const uint32_t code = code_of<FMT>(c, sc, z, &out);
+            clamped += out ? 1 : 0;
+            if constexpr (BITS == 4) {
+                // two channels per byte: the even channel's thread writes the pair
+                const uint32_t other = __shfl_xor(code, 1);
+                if ((d & 1) == 0) codes[(row0 + j) * RB + d / 2] = (uint8_t)(code | (other << 4));
+            } else if constexpr (BITS == 8) {
+                codes[(row0 + j) * RB + d] = (uint8_t)code;
             } else {
-                clamped += c != z ? 1 : 0;
+                reinterpret_cast<uint16_t*>(codes + (row0 + j) * RB)[d] = (uint16_t)code;
             }
-            // two channels per byte: the even channel's thread writes the pair
-            const uint32_t other = __shfl_xor(code, 1);
-            if ((d & 1) == 0) codes[(row0 + j) * (D / 2) + d / 2] = (uint8_t)(code | (other << 4));
         }
         __syncthreads();
     }
@@ -270,8 +356,16 @@ __global__ __launch_bounds__(256) void k_centroid_update(Geom g, int appended, c
 
 template <typename T, int D>
 hipError_t update_impl(const Geom& g, const UpdateArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((k_centroid_update<T, D>), dim3(g.B * g.Hkv), dim3(256), 0, s, g, a.appended, a.scale, a.lo,
-                       a.codes, a.out_of_range);
+#define ABS_UPDATE(F_)                                                                                         \
+    hipLaunchKernelGGL((k_centroid_update<T, D, F_>), dim3(g.B * g.Hkv), dim3(256), 0, s, g, a.appended, a.scale, \
+                       a.lo, a.codes, a.out_of_range)
+    switch (a.fmt) {
+        case kInt4Sym: ABS_UPDATE(kInt4Sym); break;
+        case kInt8: ABS_UPDATE(kInt8); break;
+        case kBf16: ABS_UPDATE(kBf16); break;
+        default: ABS_UPDATE(kInt4); break;   // kInt4 and kInt4Tensor
+    }
+#undef ABS_UPDATE
     return hipGetLastError();
 }
 

@@ -214,19 +214,31 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
     return x + (row == 1 ? t0 : row == 2 ? t1 : row == 3 ? t2 : 0u);
 }
 
-// Sum over aligned groups of N lanes (N = 2 or 4), fp64: both halves of the
-// double move with quad_perm DPP ([1,0,3,2], then [2,3,0,1] for N = 4).
+// Sum over aligned groups of N lanes (N = 2, 4, 8 or 16), fp64: both halves
+// of the double move with DPP -- quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror, row_mirror -- each step adding the partner group's sum.
 template <int N>
 __device__ __forceinline__ double lanes_sum_f64(double v) {
-    static_assert(N == 2 || N == 4, "pairs or quads");
+    static_assert(N == 2 || N == 4 || N == 8 || N == 16, "2, 4, 8 or 16 lanes");
+    constexpr int kSteps = N == 2 ? 1 : N == 4 ? 2 : N == 8 ? 3 : 4;
 #pragma unroll
-    for (int step = 0; step < (N == 4 ? 2 : 1); ++step) {
+    for (int step = 0; step < kSteps; ++step) {
         const uint64_t u = __double_as_longlong(v);
         const int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
-        const int lo2 = step == 0 ? __builtin_amdgcn_mov_dpp(lo, 0xB1, 0xF, 0xF, true)
-                                  : __builtin_amdgcn_mov_dpp(lo, 0x4E, 0xF, 0xF, true);
-        const int hi2 = step == 0 ? __builtin_amdgcn_mov_dpp(hi, 0xB1, 0xF, 0xF, true)
-                                  : __builtin_amdgcn_mov_dpp(hi, 0x4E, 0xF, 0xF, true);
+        int lo2, hi2;
+        if (step == 0) {
+            lo2 = __builtin_amdgcn_mov_dpp(lo, 0xB1, 0xF, 0xF, true);
+            hi2 = __builtin_amdgcn_mov_dpp(hi, 0xB1, 0xF, 0xF, true);
+        } else if (step == 1) {
+            lo2 = __builtin_amdgcn_mov_dpp(lo, 0x4E, 0xF, 0xF, true);
+            hi2 = __builtin_amdgcn_mov_dpp(hi, 0x4E, 0xF, 0xF, true);
+        } else if (step == 2) {
+            lo2 = __builtin_amdgcn_mov_dpp(lo, 0x141, 0xF, 0xF, true);
+            hi2 = __builtin_amdgcn_mov_dpp(hi, 0x141, 0xF, 0xF, true);
+        } else {
+            lo2 = __builtin_amdgcn_mov_dpp(lo, 0x140, 0xF, 0xF, true);
+            hi2 = __builtin_amdgcn_mov_dpp(hi, 0x140, 0xF, 0xF, true);
+        }
         v += __longlong_as_double((int64_t)(((uint64_t)(uint32_t)hi2 << 32) | (uint32_t)lo2));
     }
     return v;

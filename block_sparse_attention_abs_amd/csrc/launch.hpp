@@ -31,6 +31,12 @@ __device__ __forceinline__ int block_size_of(const Geom& g, int h) {
 
 enum class DType { F32 = 0, BF16 = 1 };
 
+// Centroid storage formats (values of abs_centroid_format): bits per channel
+// and bytes per centroid row.
+enum CentFmt { kInt4 = 0, kInt4Sym = 1, kInt8 = 2, kInt4Tensor = 3, kBf16 = 4 };
+__host__ __device__ constexpr int fmt_bits(int fmt) { return fmt == kInt8 ? 8 : fmt == kBf16 ? 16 : 4; }
+__host__ __device__ constexpr int64_t row_bytes(int D, int fmt) { return (int64_t)D * fmt_bits(fmt) / 8; }
+
 // Centroid build: blocks per workgroup tile, and the tile count the host
 // derives from the largest N_{b,h}.
 constexpr int kBuildTile = 64;
@@ -43,6 +49,7 @@ struct BuildArgs {
     float* pmin;      // [B*Hkv][tiles][D]
     float* pmax;      // [B*Hkv][tiles][D]
     int tiles;        // ceil(max N / kBuildTile)
+    int fmt;          // CentFmt
 };
 
 hipError_t launch_build(const Geom& g, DType dt, const BuildArgs& a, hipStream_t s);
@@ -55,6 +62,7 @@ struct UpdateArgs {
     uint8_t* codes;
     int32_t* out_of_range;   // [B*Hkv] or null
     int appended;
+    int fmt;                 // CentFmt
 };
 
 hipError_t launch_update(const Geom& g, DType dt, const UpdateArgs& a, hipStream_t s);
@@ -76,6 +84,7 @@ struct SelectArgs {
     const uint8_t* codes;
     const float* scale;
     const float* lo;
+    int fmt;          // CentFmt
     const void* q;
     float* scores;    // [B*Hkv][stride]
     int stride;       // max N_{b,h} rounded up to a multiple of 4

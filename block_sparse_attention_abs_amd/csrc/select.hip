@@ -10,10 +10,12 @@
 //             w_d = qbar_d * scale_d,   c0 = sum_d qbar_d * lo_d,
 //             score_j = c0 + sum_d w_d * code_{j,d}
 //         (fp64 inside, stored as fp32 in a [b*Hkv+h][stride] scratch with
-//         16-byte aligned rows).  head_dim/32 lanes share one block row of
-//         INT4 codes, 16 bytes each, so one load instruction reads a
-//         contiguous 1 KiB run per wavefront; all of a lane's code loads
-//         are issued before the workgroup's query prologue.
+//         16-byte aligned rows).  The lanes of one block row load 16 bytes
+//         of codes each (head_dim/32 lanes for INT4, head_dim/16 for INT8,
+//         head_dim/8 for bf16 centroids, whose w_d is qbar_d and c0 = 0),
+//         so one load instruction reads a contiguous 1 KiB run per
+//         wavefront; all of a lane's code loads are issued before the
+//         workgroup's query prologue.
 // top-K:  one workgroup per (b, h); thread t owns block indices
 //         [t*KPT, (t+1)*KPT) as order-preserving 32-bit keys in registers.
 //         1. min/max of the scores; a 2048-bin histogram of the scores'
@@ -39,16 +41,20 @@ namespace {
 #define ABS_SCORE_NT 256
 #endif
 
-// One tile of 256 blocks of (b, h) = bh, by an ABS_SCORE_NT-thread workgroup.
-template <typename T, int D, int GT>
+// One tile of 256 blocks of (b, h) = bh, by an ABS_SCORE_NT-thread
+// workgroup; BITS = 4 (INT4 codes), 8 (INT8 codes) or 16 (bf16 centroids).
+template <typename T, int D, int GT, int BITS>
 __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restrict__ codes,
                                            const float* __restrict__ scale, const float* __restrict__ lo,
                                            const T* __restrict__ q, float* __restrict__ scores, int stride, int bh,
                                            int tile) {
     constexpr int NT = ABS_SCORE_NT;
-    constexpr int LPB = D / 32;               // lanes per block row (16 B of codes each)
+    constexpr int CPL = 128 / BITS;           // channels per lane (16 B of codes)
+    constexpr int LPB = D / CPL;              // lanes per block row
     constexpr int GPW = NT / LPB;             // lane groups per workgroup
     constexpr int RPL = kScoreBlocksPerWg / GPW;   // block rows per lane group
+    constexpr int RB = D * BITS / 8;          // bytes per row
+    constexpr int PER = 32 / BITS;            // channels per 32-bit word
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
     const int N = ceil_div(g.seq_lens[b], block_size_of(g, h));
     const int j0 = tile * kScoreBlocksPerWg;
@@ -63,10 +69,11 @@ __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restr
     for (int r = 0; r < RPL; ++r) {
         const int j = j0 + r * GPW + grp;
         v[r] = make_uint4(0u, 0u, 0u, 0u);
-        if (j < N) v[r] = *reinterpret_cast<const uint4*>(codes + (row0 + j) * (D / 2) + sub * 16);
+        if (j < N) v[r] = *reinterpret_cast<const uint4*>(codes + (row0 + j) * RB + sub * 16);
     }
 
-    // per channel: w_d = qbar_d * scale_d and z_d = qbar_d * lo_d (fp64, LDS)
+    // per channel: w_d = qbar_d * scale_d and z_d = qbar_d * lo_d (fp64, LDS);
+    // bf16 centroids are values already: w_d = qbar_d, z_d = 0
     __shared__ double w[D], z[D];
     if (threadIdx.x < D) {
         const int d = threadIdx.x;
@@ -74,22 +81,28 @@ __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restr
 #pragma unroll
         for (int gg = 0; gg < GT; ++gg)
             qv[gg] = Elem<T>::load1(q + ((int64_t)b * g.Hq + h * g.G + min(gg, g.G - 1)) * D + d);
-        const float sc = scale[(int64_t)bh * D + d], zp = lo[(int64_t)bh * D + d];
         double qbar = 0.0;
 #pragma unroll
         for (int gg = 0; gg < GT; ++gg) qbar += gg < g.G ? (double)qv[gg] : 0.0;
-        w[d] = qbar * (double)sc;
-        z[d] = qbar * (double)zp;
+        if constexpr (BITS == 16) {
+            w[d] = qbar;
+            z[d] = 0.0;
+        } else {
+            const float sc = scale[(int64_t)bh * D + d], zp = lo[(int64_t)bh * D + d];
+            w[d] = qbar * (double)sc;
+            z[d] = qbar * (double)zp;
+        }
     }
     __syncthreads();
 
-    // this lane's 32 channels: its share of sum_d z_d once, then sum_d w_d * code_d
-    // per row (two accumulators per row); the LPB lanes of a row then add up
-    double wr[32], c0 = 0.0;
+    // this lane's CPL channels: its share of sum_d z_d once, then sum_d w_d *
+    // value_d per row (two accumulators per row); the LPB lanes of a row then
+    // add up
+    double wr[CPL], c0 = 0.0;
 #pragma unroll
-    for (int n = 0; n < 32; ++n) {
-        wr[n] = w[sub * 32 + n];
-        c0 += z[sub * 32 + n];
+    for (int n = 0; n < CPL; ++n) {
+        wr[n] = w[sub * CPL + n];
+        if constexpr (BITS != 16) c0 += z[sub * CPL + n];
     }
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
@@ -98,28 +111,34 @@ __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restr
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int n = 0; n < 8; ++n)
-                acc[i >> 1] = fma(wr[i * 8 + n], (double)((wd[i] >> (4 * n)) & 15u), acc[i >> 1]);
+            for (int n = 0; n < PER; ++n) {
+                double x;
+                if constexpr (BITS == 16)
+                    x = (double)__uint_as_float(n == 0 ? wd[i] << 16 : wd[i] & 0xFFFF0000u);
+                else
+                    x = (double)((wd[i] >> (BITS * n)) & ((1u << BITS) - 1u));
+                acc[i >> 1] = fma(wr[i * PER + n], x, acc[i >> 1]);
+            }
         const double sum = lanes_sum_f64<LPB>(acc[0] + acc[1]);
         const int j = j0 + r * GPW + grp;
         if (j < N && sub == 0) scores[(int64_t)bh * stride + j] = (float)sum;
     }
 }
 
-template <typename T, int D, int GT>
+template <typename T, int D, int GT, int BITS>
 __global__ __launch_bounds__(ABS_SCORE_NT) void k_score_grid(Geom g, const uint8_t* __restrict__ codes,
                                                     const float* __restrict__ scale, const float* __restrict__ lo,
                                                     const T* __restrict__ q, float* __restrict__ scores, int stride) {
-    score_tile<T, D, GT>(g, codes, scale, lo, q, scores, stride, blockIdx.y, blockIdx.x);
+    score_tile<T, D, GT, BITS>(g, codes, scale, lo, q, scores, stride, blockIdx.y, blockIdx.x);
 }
 
-template <typename T, int D, int GT>
+template <typename T, int D, int GT, int BITS>
 __global__ __launch_bounds__(ABS_SCORE_NT) void k_score_list(Geom g, const uint8_t* __restrict__ codes,
                                                     const float* __restrict__ scale, const float* __restrict__ lo,
                                                     const T* __restrict__ q, float* __restrict__ scores, int stride,
                                                     const ScoreTiles tl) {
     const uint32_t e = tl.t[blockIdx.x];
-    score_tile<T, D, GT>(g, codes, scale, lo, q, scores, stride, (int)(e >> 8), (int)(e & 255u));
+    score_tile<T, D, GT, BITS>(g, codes, scale, lo, q, scores, stride, (int)(e >> 8), (int)(e & 255u));
 }
 
 // Order-preserving map of a float to uint32 (larger float -> larger key);
@@ -406,15 +425,15 @@ __global__ __launch_bounds__(NT) void k_topk(Geom g, const float* __restrict__ s
     }
 }
 
-template <typename T, int D>
-hipError_t select_impl(const Geom& g, const SelectArgs& a, hipStream_t s) {
+template <typename T, int D, int BITS>
+void launch_score(const Geom& g, const SelectArgs& a, hipStream_t s) {
     const T* q = reinterpret_cast<const T*>(a.q);
     if (a.tiles_host != nullptr && a.ntiles <= kMaxScoreTiles) {
         ScoreTiles tl;
         for (int i = 0; i < a.ntiles; ++i) tl.t[i] = a.tiles_host[i];
-#define ABS_SCORE(GT_)                                                                                       \
-    hipLaunchKernelGGL((k_score_list<T, D, GT_>), dim3(a.ntiles), dim3(ABS_SCORE_NT), 0, s, g, a.codes, a.scale, a.lo, q, \
-                       a.scores, a.stride, tl)
+#define ABS_SCORE(GT_)                                                                                    \
+    hipLaunchKernelGGL((k_score_list<T, D, GT_, BITS>), dim3(a.ntiles), dim3(ABS_SCORE_NT), 0, s, g, a.codes, \
+                       a.scale, a.lo, q, a.scores, a.stride, tl)
         if (g.G <= 1) ABS_SCORE(1);
         else if (g.G <= 2) ABS_SCORE(2);
         else if (g.G <= 4) ABS_SCORE(4);
@@ -423,14 +442,22 @@ hipError_t select_impl(const Geom& g, const SelectArgs& a, hipStream_t s) {
     } else {
         const dim3 sgrid(ceil_div(a.max_n, kScoreBlocksPerWg), g.B * g.Hkv);
 #define ABS_SCORE(GT_)                                                                                       \
-    hipLaunchKernelGGL((k_score_grid<T, D, GT_>), sgrid, dim3(ABS_SCORE_NT), 0, s, g, a.codes, a.scale, a.lo, q, a.scores, \
-                       a.stride)
+    hipLaunchKernelGGL((k_score_grid<T, D, GT_, BITS>), sgrid, dim3(ABS_SCORE_NT), 0, s, g, a.codes, a.scale, a.lo, \
+                       q, a.scores, a.stride)
         if (g.G <= 1) ABS_SCORE(1);
         else if (g.G <= 2) ABS_SCORE(2);
         else if (g.G <= 4) ABS_SCORE(4);
         else ABS_SCORE(8);
 #undef ABS_SCORE
     }
+}
+
+template <typename T, int D>
+hipError_t select_impl(const Geom& g, const SelectArgs& a, hipStream_t s) {
+    const int bits = fmt_bits(a.fmt);
+    if (bits == 8) launch_score<T, D, 8>(g, a, s);
+    else if (bits == 16) launch_score<T, D, 16>(g, a, s);
+    else launch_score<T, D, 4>(g, a, s);
     const dim3 tgrid(g.B * g.Hkv);
 #define ABS_TOPK(NT_, KPT_)                                                                                  \
     hipLaunchKernelGGL((k_topk<NT_, KPT_>), tgrid, dim3(NT_), 0, s, g, a.scores, a.stride, a.budget, a.sel, \

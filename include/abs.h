@@ -110,16 +110,49 @@ typedef struct abs_block_map {
 } abs_block_map;
 
 /*
- * INT4 centroid store (Figure 8: asymmetric, per channel).
- *   codes: device uint8 [total_blocks][head_dim / 2]; channel 2i in the low
- *       nibble of byte i, channel 2i+1 in the high nibble.
+ * Centroid storage formats.  Figure 8 of the page compares centroid
+ * precisions and keeps INT4 asymmetric per channel (ABS_CENT_INT4, the
+ * default); the others are there to measure that trade-off.  Per (b, h) over
+ * its blocks j, per channel d, with c the fp32 mean key:
+ *   ABS_CENT_INT4: lo = min_j c, scale = (max_j c - lo) / 15,
+ *       code = clamp(rint((c - lo) / scale), 0, 15); 4 bits per channel.
+ *   ABS_CENT_INT4_SYM: scale = max_j |c| / 7, q = clamp(rint(c / scale),
+ *       -7, 7), code = q + 8; lo = -8 * scale, so code * scale + lo = q * scale.
+ *   ABS_CENT_INT8: as ABS_CENT_INT4 with 255 levels; 8 bits per channel.
+ *   ABS_CENT_INT4_TENSOR: as ABS_CENT_INT4 with one range for the whole
+ *       (b, h): lo and scale from the min/max over every block and channel
+ *       (stored per channel, all equal).
+ *   ABS_CENT_BF16: code = the bf16 bit pattern of c (round to nearest, ties
+ *       to even); scale and lo are written as 0 and not used.
+ * Every step that decides a code is an fp32 operation; a scale of 0 gives
+ * code 0 (ABS_CENT_INT4_SYM: q = 0).
+ */
+typedef enum abs_centroid_format {
+    ABS_CENT_INT4 = 0,
+    ABS_CENT_INT4_SYM = 1,
+    ABS_CENT_INT8 = 2,
+    ABS_CENT_INT4_TENSOR = 3,
+    ABS_CENT_BF16 = 4
+} abs_centroid_format;
+
+/*
+ * Centroid store.
+ *   codes: device [total_blocks][row bytes] (abs_centroid_row_bytes), 16-byte
+ *       aligned.  4-bit formats: channel 2i in the low nibble of byte i,
+ *       channel 2i+1 in the high nibble; ABS_CENT_INT8: one byte per channel;
+ *       ABS_CENT_BF16: one little-endian uint16 per channel.
  *   scale, lo: device f32 [num_seqs][num_kv_heads][head_dim]; the
- *       dequantized centroid is code * scale + lo.
+ *       dequantized centroid is code * scale + lo (ABS_CENT_BF16: the bf16
+ *       value itself).
+ *   format: abs_centroid_format; a zero-filled struct means ABS_CENT_INT4.
+ *   reserved0: must be 0.
  */
 typedef struct abs_centroids {
     uint8_t *codes;
     float *scale;
     float *lo;
+    int32_t format;
+    int32_t reserved0;
 } abs_centroids;
 
 /* Static text for a status code. */
@@ -143,6 +176,11 @@ abs_status abs_centroid_offsets(const abs_paged_kv *kv, const abs_block_map *map
 abs_status abs_centroid_offsets_capacity(const abs_paged_kv *kv, const abs_block_map *map,
                                          int32_t capacity_tokens, int64_t *off_host);
 
+/* Bytes of one centroid row: head_dim / 2 (4-bit formats), head_dim
+ * (ABS_CENT_INT8) or 2 * head_dim (ABS_CENT_BF16).  ABS_ERR_INVALID_ARG for
+ * an unknown format or head_dim < 1. */
+abs_status abs_centroid_row_bytes(int32_t head_dim, int32_t format, int64_t *bytes);
+
 /* Largest K_{b,h} = min(N_{b,h}, max(1, floor(token_budget / bs_h))) over all
  * (b, h): the smallest row length (sel_cap) a selection buffer may have. */
 abs_status abs_select_capacity(const abs_paged_kv *kv, const abs_block_map *map,
@@ -154,11 +192,12 @@ abs_status abs_workspace_bytes(const abs_paged_kv *kv, const abs_block_map *map,
                                int32_t token_budget, abs_op op, size_t *bytes);
 
 /*
- * Centroid build + INT4 quantization, for every (b, h) of the layer.
+ * Centroid build + quantization, for every (b, h) of the layer.
  * Centroid of block j of (b, h) = mean of the keys of its valid tokens
- * [j*bs_h, min((j+1)*bs_h, L_b)) (Figure 1's block representation; mean key).
- * Per (b, h, channel d): lo = min_j c_j[d], scale = (max_j c_j[d] - lo) / 15
- * (fp32), code = clamp(rint((c - lo) / scale), 0, 15) in fp32, 0 if scale == 0.
+ * [j*bs_h, min((j+1)*bs_h, L_b)) (Figure 1's block representation; mean key),
+ * rounded once to fp32, then coded in out->format (ABS_CENT_INT4: per (b, h,
+ * channel d): lo = min_j c_j[d], scale = (max_j c_j[d] - lo) / 15 (fp32),
+ * code = clamp(rint((c - lo) / scale), 0, 15) in fp32, 0 if scale == 0).
  * Writes out->codes (all total_blocks rows), out->scale, out->lo.
  */
 abs_status abs_build_centroids(const abs_paged_kv *kv, const abs_block_map *map,
@@ -173,7 +212,8 @@ abs_status abs_build_centroids(const abs_paged_kv *kv, const abs_block_map *map,
  * them), every block holding one of the tokens [L_b - appended - 1, L_b) --
  * always at least the last, possibly partial block -- gets its centroid
  * recomputed (mean of its valid tokens, as abs_build_centroids) and coded
- * with the (scale, lo) already in cents, clamped to 0..15.  The range is not
+ * with the (scale, lo) already in cents, clamped to the format's code range
+ * (cents->format must be the format the store was built in).  The range is not
  * widened: a caller rebuilds the layer (abs_build_centroids) when it wants a
  * new one, e.g. when out_of_range grows.
  *   cents: the store written by abs_build_centroids for this layer; block j
@@ -183,8 +223,9 @@ abs_status abs_build_centroids(const abs_paged_kv *kv, const abs_block_map *map,
  *   appended: >= 0, the same for every sequence (0 redoes the last block).
  *   out_of_range: device int32 [num_seqs][num_kv_heads] or NULL; receives the
  *       number of (block, channel) codes of this call that were clamped (the
- *       rounded quotient outside 0..15, or, for a channel with scale 0, a
- *       centroid other than lo).
+ *       rounded quotient outside the code range, or, for a channel with
+ *       scale 0, a centroid other than lo; ABS_CENT_BF16: a finite centroid
+ *       that rounds to an infinity).
  * No workspace; one launch.
  */
 abs_status abs_update_centroids(const abs_paged_kv *kv, const abs_block_map *map,
@@ -195,7 +236,8 @@ abs_status abs_update_centroids(const abs_paged_kv *kv, const abs_block_map *map
  * Dot-product estimation + top-K (Figure 1; the "Estimation" and "Top-K"
  * stages of the per-stage latency figure after Figure 13).  For each (b, h):
  * qbar = sum of the query heads h*G .. h*G+G-1 (G = num_q_heads /
- * num_kv_heads), score_j = qbar . (code_j * scale + lo); keep the K_{b,h}
+ * num_kv_heads), score_j = qbar . (code_j * scale + lo) (ABS_CENT_BF16:
+ * qbar . centroid_j), evaluated in fp64 and rounded to fp32; keep the K_{b,h}
  * best blocks ranked by (score desc, index asc).
  *   q: device [num_seqs][num_q_heads][head_dim] in kv_dtype.
  *   sel: device int32 [num_seqs][num_kv_heads][sel_cap]; row (b, h) gets its

@@ -2,13 +2,14 @@
 results back to the host, plus the comparison rules the parity tests use.
 
 Comparison rules (how the tolerances are applied):
-  * centroid build: INT4 codes, scale and lo are compared bit for bit (the
+  * centroid build: codes (every format), scale and lo are compared bit for bit (the
     kernel sums keys in fp64, so its fp32 centroid is the same correctly
     rounded mean as the oracle's, and the quantizer's fp32 steps are the same
     IEEE operations);
   * selection: per (b, h) the selected index sets must be equal, except for
     blocks whose oracle score lies within the tie band of the K-th score tau:
     band = max(1e-4 |tau|, 1e-6 M), M = sum_d |qbar_d| max(|lo_d|, |hi_d|)
+    (or, for any centroid format, sum_d |qbar_d| max_j |c_hat_{j,d}|)
     bounds every |score| of the head; indices ascending, K entries;
   * attention: element-wise against the oracle run on the GPU's own
     selection; bf16 max-abs <= 2e-2 and mean-abs <= 2e-3, fp32 max-abs <= 1e-4
@@ -44,6 +45,17 @@ def unpack_codes(packed: np.ndarray) -> np.ndarray:
     out[:, 0::2] = p & 15
     out[:, 1::2] = p >> 4
     return out
+
+
+def codes_of_format(raw: np.ndarray, fmt: str) -> np.ndarray:
+    """Device code rows (uint8 [rows][row bytes]) -> uint16 [rows][D] code
+    values in the layout of abs_centroids."""
+    raw = np.ascontiguousarray(raw, dtype=np.uint8)
+    if fmt == "bf16":
+        return raw.view("<u2").astype(np.uint16)
+    if fmt == "int8":
+        return raw.astype(np.uint16)
+    return unpack_codes(raw).astype(np.uint16)
 
 
 def pack_codes(codes: np.ndarray) -> np.ndarray:
@@ -116,8 +128,11 @@ def check_selection(oracle_mod, x, quant, scores, gpu_sel, gpu_cnt, budget):
             continue
         tau = s[order[k - 1]]
         qbar = qf[b, h * G:(h + 1) * G].sum(0)
-        hi = quant.lo[b, h].astype(np.float64) + 15 * quant.scale[b, h].astype(np.float64)
-        M = np.sum(np.abs(qbar) * np.maximum(np.abs(quant.lo[b, h]), np.abs(hi)))
+        if getattr(quant, "deq", None) is not None:   # any centroid format: bound from the dequantized rows
+            M = np.sum(np.abs(qbar) * np.abs(quant.deq[r0:r0 + n]).max(axis=0))
+        else:
+            hi = quant.lo[b, h].astype(np.float64) + 15 * quant.scale[b, h].astype(np.float64)
+            M = np.sum(np.abs(qbar) * np.maximum(np.abs(quant.lo[b, h]), np.abs(hi)))
         band = max(1e-4 * abs(tau), 1e-6 * M)
         diff = np.setxor1d(got, want)
         assert (np.abs(s[diff] - tau) <= band).all(), (b, h, diff, s[diff], tau, band)

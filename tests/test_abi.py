@@ -25,7 +25,7 @@ def header_functions():
 
 def test_exports_every_declared_call():
     names = header_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     assert sorted(A.EXPORTS) == names
     L = A.lib()
     for n in names:
@@ -47,6 +47,7 @@ int main(void) {
          sizeof(abs_paged_kv), sizeof(abs_block_map), sizeof(abs_centroids));
   F(abs_paged_kv, num_pages); F(abs_paged_kv, kv_dtype); F(abs_paged_kv, k_cache);
   F(abs_paged_kv, seq_lens_host); F(abs_block_map, centroid_off); F(abs_centroids, lo);
+  F(abs_centroids, format); F(abs_centroids, reserved0);
   return 0;
 }""")
     exe = tmp_path / "layout"
@@ -60,7 +61,9 @@ int main(void) {
                          "abs_paged_kv.k_cache": (A.abs_paged_kv, "k_cache"),
                          "abs_paged_kv.seq_lens_host": (A.abs_paged_kv, "seq_lens_host"),
                          "abs_block_map.centroid_off": (A.abs_block_map, "centroid_off"),
-                         "abs_centroids.lo": (A.abs_centroids, "lo")}.items():
+                         "abs_centroids.lo": (A.abs_centroids, "lo"),
+                         "abs_centroids.format": (A.abs_centroids, "format"),
+                         "abs_centroids.reserved0": (A.abs_centroids, "reserved0")}.items():
         assert int(got[key]) == getattr(st, f).offset
 
 
@@ -163,6 +166,34 @@ def test_call_level_validation():
     h.kv.v_cache = None
     assert status_of(lambda: A.abs_sparse_decode(h.kv, h.bmap, FAKE, FAKE, cap, FAKE, 64, 0.125, FAKE, None,
                                                  FAKE, need_d, 0)) == I
+
+
+@pytest.mark.parametrize("fmt,D,want", [(0, 128, 64), (1, 128, 64), (2, 128, 128), (3, 64, 32), (4, 64, 128),
+                                        (4, 128, 256)])
+def test_centroid_row_bytes(fmt, D, want):
+    assert A.abs_centroid_row_bytes(D, fmt) == want
+    assert A.CENTROID_FORMATS[["int4", "int4_sym", "int8", "int4_tensor", "bf16"][fmt]] == fmt
+
+
+def test_centroid_format_validation():
+    """Unknown formats, a non-zero reserved field and misaligned codes are
+    rejected by every call that takes a centroid store."""
+    assert status_of(lambda: A.abs_centroid_row_bytes(64, 5)) == A.ABS_ERR_INVALID_ARG
+    assert status_of(lambda: A.abs_centroid_row_bytes(0, 0)) == A.ABS_ERR_INVALID_ARG
+    h = Host()
+    need_b = A.abs_workspace_bytes(h.kv, h.bmap, 64, A.ABS_OP_BUILD)
+    need_s = A.abs_workspace_bytes(h.kv, h.bmap, 64, A.ABS_OP_SELECT)
+    cap = A.abs_select_capacity(h.kv, h.bmap, 64)
+    bad = [A.abs_centroids(codes=FAKE, scale=FAKE, lo=FAKE, format=5),
+           A.abs_centroids(codes=FAKE, scale=FAKE, lo=FAKE, format=-1),
+           A.abs_centroids(codes=FAKE, scale=FAKE, lo=FAKE, format=0, reserved0=1),
+           A.abs_centroids(codes=FAKE + 8, scale=FAKE, lo=FAKE, format=2)]
+    I = A.ABS_ERR_INVALID_ARG
+    for c in bad:
+        assert status_of(lambda: A.abs_build_centroids(h.kv, h.bmap, c, FAKE, need_b, 0)) == I
+        assert status_of(lambda: A.abs_update_centroids(h.kv, h.bmap, c, 1, None, 0)) == I
+        assert status_of(lambda: A.abs_score_select(h.kv, h.bmap, c, FAKE, 64, FAKE, cap, FAKE, FAKE, need_s,
+                                                    0)) == I
 
 
 def test_too_many_blocks_per_head_is_unsupported():
