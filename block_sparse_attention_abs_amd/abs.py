@@ -29,7 +29,8 @@ CENTROID_FORMATS = {"int4": 0, "int4_sym": 1, "int8": 2, "int4_tensor": 3, "bf16
 
 EXPORTS = ("abs_status_str", "abs_last_error", "abs_total_blocks", "abs_centroid_offsets",
            "abs_centroid_offsets_capacity", "abs_centroid_row_bytes", "abs_select_capacity", "abs_workspace_bytes", "abs_build_centroids",
-           "abs_update_centroids", "abs_score_select", "abs_sparse_decode")
+           "abs_update_centroids", "abs_score_select", "abs_sparse_decode", "abs_head_recall",
+           "abs_assign_block_sizes")
 
 
 class abs_paged_kv(C.Structure):
@@ -91,6 +92,10 @@ def lib():
         L.abs_score_select.argtypes = [KV, MAP, CEN, P, i32, P, i32, P, P, C.c_size_t, P]
         L.abs_sparse_decode.restype = st
         L.abs_sparse_decode.argtypes = [KV, MAP, P, P, i32, P, i32, C.c_float, P, P, P, C.c_size_t, P]
+        L.abs_head_recall.restype = st
+        L.abs_head_recall.argtypes = [KV, P, P, P, P]
+        L.abs_assign_block_sizes.restype = st
+        L.abs_assign_block_sizes.argtypes = [i32, P, C.c_float, P]
         _lib = L
     return _lib
 
@@ -173,6 +178,20 @@ def abs_sparse_decode(kv, bmap, q_ptr: int, sel_ptr: int, sel_cap: int, count_pt
                                    sm_scale, out_ptr, lse_ptr, ws_ptr, ws_bytes, stream), "abs_sparse_decode")
 
 
+def abs_head_recall(kv, lse_sel_ptr: int, lse_full_ptr: int, recall_ptr: int, stream: int) -> None:
+    _check(lib().abs_head_recall(C.byref(kv), lse_sel_ptr, lse_full_ptr, recall_ptr, stream), "abs_head_recall")
+
+
+def abs_assign_block_sizes(recall_host: np.ndarray, threshold: float) -> np.ndarray:
+    """recall_host: [3][num_kv_heads] (block sizes 16, 32, 64) -> int32 [num_kv_heads]."""
+    r = np.ascontiguousarray(recall_host, dtype=np.float32)
+    assert r.ndim == 2 and r.shape[0] == 3
+    out = np.zeros(r.shape[1], dtype=np.int32)
+    _check(lib().abs_assign_block_sizes(r.shape[1], r.ctypes.data, threshold, out.ctypes.data),
+           "abs_assign_block_sizes")
+    return out
+
+
 # ---- torch-side holder ------------------------------------------------------
 
 def _ptr(t) -> int:
@@ -247,6 +266,20 @@ class PagedKV:
         out = PagedKV(self.k_cache, self.v_cache, self.page_table, upload(sl, self.k_cache.device), sl,
                       self.block_size, self.block_size_host, self.centroid_off, self.num_q_heads, self.kv_dtype)
         out.centroid_rows = self.centroid_rows
+        return out
+
+    def with_block_sizes(self, block_size: np.ndarray) -> "PagedKV":
+        """The same cache, page table and lengths under another block-size map
+        (its own compact centroid offsets)."""
+        import torch
+        bs = np.ascontiguousarray(block_size, dtype=np.int32)
+        dev = self.k_cache.device
+        out = PagedKV(self.k_cache, self.v_cache, self.page_table, self.seq_lens, self.seq_lens_host, upload(bs, dev),
+                      bs, torch.zeros(len(self.seq_lens_host) * len(bs) + 1, dtype=torch.int64, device=dev),
+                      self.num_q_heads, self.kv_dtype)
+        off = abs_centroid_offsets(out.kv, out.bmap)
+        out.centroid_off.copy_(torch.from_numpy(off))
+        out.centroid_rows = int(off[-1])
         return out
 
     @property
@@ -328,3 +361,44 @@ def sparse_decode(kv: PagedKV, q, sel, count, budget: int, sm_scale: float, out,
     abs_sparse_decode(kv.kv, kv.bmap, _ptr(q), _ptr(sel), int(sel.shape[-1]), _ptr(count), budget, sm_scale,
                       _ptr(out), _ptr(lse) if lse is not None else None, _ptr(ws), ws.numel(),
                       current_stream() if stream is None else stream)
+
+
+CALIBRATION_SIZES = (16, 32, 64)
+
+
+def calibrate_block_sizes(kv: PagedKV, q, budget: int, sm_scale: float, threshold: float = 0.95,
+                          fmt: str = "int4", stream: Optional[int] = None):
+    """Offline calibration of the per-head block-size map on one layer (see
+    abs_head_recall / abs_assign_block_sizes): for each block size, the
+    layer with that size everywhere is built, selected and decoded; the
+    decode with every block selected gives the full normalizers.  Returns
+    (block sizes int32 [Hkv], recall fp32 [3][Hkv]).  Synchronizes once, to
+    read the recalls."""
+    import torch
+    dev = kv.k_cache.device
+    st = current_stream() if stream is None else stream
+    B, Hq, Hkv = kv.kv.num_seqs, kv.kv.num_q_heads, kv.kv.num_kv_heads
+    D = kv.kv.head_dim
+    out = torch.empty((B, Hq, D), dtype=torch_dtype(kv.kv_dtype), device=dev)
+    lse_full = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    lse_sel = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    recall = torch.empty((3, Hkv), dtype=torch.float32, device=dev)
+    everything = int(kv.seq_lens_host.max())
+
+    def select_and_decode(layer, cents, bud, lse):
+        cap = layer.select_capacity(bud)
+        sel = torch.empty((B, Hkv, cap), dtype=torch.int32, device=dev)
+        cnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+        score_select(layer, cents, q, bud, sel, cnt, stream=st)
+        sparse_decode(layer, q, sel, cnt, bud, sm_scale, out, lse, stream=st)
+
+    for k, bs in enumerate(CALIBRATION_SIZES):
+        layer = kv.with_block_sizes(np.full(Hkv, bs, dtype=np.int32))
+        cents = build_centroids(layer, Centroids.empty(layer, fmt), stream=st)
+        if k == 0:
+            select_and_decode(layer, cents, everything, lse_full)
+        select_and_decode(layer, cents, budget, lse_sel)
+        abs_head_recall(layer.kv, _ptr(lse_sel), _ptr(lse_full), _ptr(recall[k]), st)
+    torch.cuda.synchronize(dev)
+    r = recall.cpu().numpy()
+    return abs_assign_block_sizes(r, threshold), r

@@ -439,4 +439,45 @@ abs_status abs_sparse_decode(const abs_paged_kv* kv, const abs_block_map* map, c
     return hip_status(absk::launch_decode(p.g, p.dt, a, static_cast<hipStream_t>(stream)), "sparse_decode");
 }
 
+abs_status abs_head_recall(const abs_paged_kv* kv, const float* lse_sel, const float* lse_full, float* recall,
+                           void* stream) {
+    if (kv == nullptr) return fail(ABS_ERR_INVALID_ARG, "null descriptor");
+    if (kv->num_seqs < 1 || kv->num_q_heads < 1 || kv->num_kv_heads < 1)
+        return fail(ABS_ERR_INVALID_ARG, "num_seqs, num_q_heads, num_kv_heads must be >= 1");
+    if (kv->num_q_heads % kv->num_kv_heads != 0)
+        return fail(ABS_ERR_INVALID_ARG, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                    kv->num_q_heads, kv->num_kv_heads);
+    if (lse_sel == nullptr || lse_full == nullptr || recall == nullptr)
+        return fail(ABS_ERR_INVALID_ARG, "null lse_sel, lse_full or recall");
+    return hip_status(absk::launch_head_recall(kv->num_seqs, kv->num_q_heads, kv->num_kv_heads, lse_sel, lse_full,
+                                               recall, static_cast<hipStream_t>(stream)),
+                      "head_recall");
+}
+
+abs_status abs_assign_block_sizes(int32_t num_kv_heads, const float* recall_host, float threshold,
+                                  int32_t* block_size_host) {
+    if (num_kv_heads < 1) return fail(ABS_ERR_INVALID_ARG, "num_kv_heads %d < 1", num_kv_heads);
+    if (recall_host == nullptr || block_size_host == nullptr)
+        return fail(ABS_ERR_INVALID_ARG, "null recall or block size array");
+    if (!std::isfinite(threshold) || threshold <= 0.0f)
+        return fail(ABS_ERR_INVALID_ARG, "threshold must be finite and > 0");
+    for (int i = 0; i < 3 * num_kv_heads; ++i)
+        if (!(recall_host[i] >= 0.0f && recall_host[i] <= 1.0f))
+            return fail(ABS_ERR_INVALID_ARG, "recall[%d] = %g outside [0, 1]", i, (double)recall_host[i]);
+    static constexpr int kSizes[3] = {16, 32, 64};
+    for (int h = 0; h < num_kv_heads; ++h) {
+        const double base = recall_host[h];
+        int bs = kSizes[0];
+        for (int k = 2; k >= 1; --k) {
+            const double ratio = base > 0.0 ? (double)recall_host[k * num_kv_heads + h] / base : 1.0;
+            if (ratio >= (double)threshold) {
+                bs = kSizes[k];
+                break;
+            }
+        }
+        block_size_host[h] = bs;
+    }
+    return ok();
+}
+
 }  // extern "C"

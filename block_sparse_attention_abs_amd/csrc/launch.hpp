@@ -121,4 +121,8 @@ constexpr int kMaxPagesPerWg = 64;
 
 hipError_t launch_decode(const Geom& g, DType dt, const DecodeArgs& a, hipStream_t s);
 
+// Calibration: recall[h] = mean over (b, query heads of h) of exp(lse_sel - lse_full).
+hipError_t launch_head_recall(int B, int Hq, int Hkv, const float* lse_sel, const float* lse_full, float* recall,
+                              hipStream_t s);
+
 }  // namespace absk

@@ -132,8 +132,10 @@ class LayerInputs:
         return int(self.page_table.shape[1])
 
 
-def _head_keys(w, layer, b, h, L, D, qbar):
-    """Keys of one (sequence, KV head) as fp32 [L][D], plus needle positions."""
+def _head_keys(w, layer, b, h, L, D, qbar, run=1):
+    """Keys of one (sequence, KV head) as fp32 [L][D], plus needle positions.
+    run > 1 plants the needles as runs of `run` consecutive tokens starting
+    at multiples of `run` (clustered); run = 1 scatters them."""
     k = _rng(w, layer, b, h, S_K).standard_normal((L, D), dtype=np.float32)
     chans = _rng(w, layer, 0, h, S_OUTLIER).permutation(D)[:OUTLIER_CHANNELS]
     k[:, chans] *= np.float32(OUTLIER_SCALE)
@@ -141,7 +143,12 @@ def _head_keys(w, layer, b, h, L, D, qbar):
     pos = np.zeros(0, dtype=np.int64)
     if n > 0:
         r = _rng(w, layer, b, h, S_NEEDLE)
-        pos = np.sort(r.choice(L, size=n, replace=False)).astype(np.int64)
+        if run > 1:
+            nr = max(1, min(n // run, L // run))
+            starts = r.choice(L // run, size=nr, replace=False).astype(np.int64) * run
+            pos = np.sort((starts[:, None] + np.arange(run, dtype=np.int64)[None, :]).ravel())
+        else:
+            pos = np.sort(r.choice(L, size=n, replace=False)).astype(np.int64)
         rho = float(np.median(np.linalg.norm(k.astype(np.float64), axis=1)))
         nrm = float(np.linalg.norm(qbar))
         u = qbar / nrm if nrm > 0 else np.eye(D)[0]
@@ -155,12 +162,15 @@ def _head_keys(w, layer, b, h, L, D, qbar):
 
 def make_layer(w: Workload, layer: int = 0, *, seq_lens: Optional[Sequence[int]] = None,
                block_sizes: Optional[Sequence[int]] = None, shuffle_pages: bool = True,
-               needles: bool = True, extra_pages: int = 0) -> LayerInputs:
+               needles: bool = True, extra_pages: int = 0,
+               needle_runs: Optional[Sequence[int]] = None) -> LayerInputs:
     """Generate one layer's decode inputs.
 
     ``seq_lens`` overrides the context per sequence (ragged batches);
     ``block_sizes`` overrides the drawn map; ``shuffle_pages=False`` gives the
-    identity page table; ``extra_pages`` adds unused physical pages to the pool.
+    identity page table; ``extra_pages`` adds unused physical pages to the pool;
+    ``needle_runs`` (per KV head) plants that head's needles in aligned runs
+    of that many tokens instead of scattering them (1).
     """
     B, Hq, Hkv, D, G = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.group
     lens = np.asarray(seq_lens if seq_lens is not None else [w.context] * B, dtype=np.int32)
@@ -168,6 +178,8 @@ def make_layer(w: Workload, layer: int = 0, *, seq_lens: Optional[Sequence[int]]
     bsz = (np.asarray(block_sizes, dtype=np.int32) if block_sizes is not None
            else block_sizes_for(w, layer))
     assert bsz.shape == (Hkv,)
+    runs = [1] * Hkv if needle_runs is None else [int(r) for r in needle_runs]
+    assert len(runs) == Hkv and min(runs) >= 1
 
     q32 = np.stack([_rng(w, layer, b, 0, S_Q).standard_normal((Hq, D), dtype=np.float32)
                     for b in range(B)])
@@ -191,7 +203,7 @@ def make_layer(w: Workload, layer: int = 0, *, seq_lens: Optional[Sequence[int]]
     pad = to_storage(np.float32([PAD_SENTINEL]), w.dtype)[0]
     k_cache = np.full((total, Hkv, PAGE_SIZE, D), pad, dtype=sdt)
     v_cache = np.full((total, Hkv, PAGE_SIZE, D), pad, dtype=sdt)
-    nmax = min(w.needles_per_head, int(lens.max())) if needles else 0
+    nmax = min(max(w.needles_per_head, max(runs)), int(lens.max())) if needles else 0
     needle_pos = np.full((B, Hkv, nmax), -1, dtype=np.int64)
     wn = w if needles else dataclasses.replace(w, needles_per_head=0)
 
@@ -199,7 +211,7 @@ def make_layer(w: Workload, layer: int = 0, *, seq_lens: Optional[Sequence[int]]
         L, P = int(lens[b]), int(npages[b])
         phys = page_table[b, :P]
         qbar = qf[b, h * G:(h + 1) * G].sum(axis=0)
-        k, pos = _head_keys(wn, layer, b, h, L, D, qbar)
+        k, pos = _head_keys(wn, layer, b, h, L, D, qbar, runs[h])
         needle_pos[b, h, :len(pos)] = pos
         v = _rng(w, layer, b, h, S_V).standard_normal((L, D), dtype=np.float32)
         kp = np.full((P * PAGE_SIZE, D), PAD_SENTINEL, dtype=np.float32)

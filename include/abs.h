@@ -275,6 +275,39 @@ abs_status abs_sparse_decode(const abs_paged_kv *kv, const abs_block_map *map, c
                              int32_t token_budget, float sm_scale, void *out, float *lse,
                              void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Offline block-size calibration (Figure 3 of the page: per-head recall at
+ * block sizes 16, 32 and 64, normalized by the recall at 16; the heatmap
+ * after it: the resulting per-head map).  The page does not define its
+ * sensitivity metric; these two calls implement this reading of it:
+ *   recall of a selection for query head i = the share of i's exact
+ *   attention over all L_b tokens that falls on the kept tokens; a KV head's
+ *   recall at block size s = the mean of that share over the sequences and
+ *   the head's query group, when every head uses block size s;
+ *   a head gets the largest block size whose recall divided by its recall
+ *   at 16 is at least a threshold, else 16.
+ * A caller measures the recall with the calls above: for each s, a layer
+ * descriptor with every block size = s, abs_build_centroids,
+ * abs_score_select and abs_sparse_decode (lse -> lse_sel); once, the decode
+ * with every block selected (token_budget >= every L_b, lse -> lse_full).
+ */
+
+/* recall: device f32 [num_kv_heads] = mean over b and g < G of
+ * exp(lse_sel[b][h*G + g] - lse_full[b][h*G + g]) (fp64 inside).
+ * lse_sel, lse_full: device f32 [num_seqs][num_q_heads] as abs_sparse_decode
+ * writes them.  Only kv's num_seqs, num_q_heads and num_kv_heads are read.
+ * One launch, no workspace. */
+abs_status abs_head_recall(const abs_paged_kv *kv, const float *lse_sel, const float *lse_full, float *recall,
+                           void *stream);
+
+/* Host: block_size_host[h] = the largest s in {32, 64} with
+ * recall_host[k(s)][h] / recall_host[0][h] >= threshold (a ratio of 1 when
+ * the recall at 16 is 0), else 16; k(16) = 0, k(32) = 1, k(64) = 2.
+ * recall_host: [3][num_kv_heads], each in [0, 1] (else
+ * ABS_ERR_INVALID_ARG); threshold: finite, > 0. */
+abs_status abs_assign_block_sizes(int32_t num_kv_heads, const float *recall_host, float threshold,
+                                  int32_t *block_size_host);
+
 #ifdef __cplusplus
 }
 #endif

@@ -47,6 +47,7 @@ def lib():
         L.oracle_update.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
         L.oracle_quantize_fmt.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P]
         L.oracle_scores_dense.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P]
+        L.oracle_attention_mass.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, i32, P, C.c_double, P]
         L.oracle_scores.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, P]
         L.oracle_select.argtypes = [i32, i32, P, P, i32, P, P, i32, P]
         L.oracle_attend.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, i32, P,
@@ -240,6 +241,59 @@ def attend(q, k_cache, v_cache, page_table, seq_lens, block_size, sel, count, sm
     lib().oracle_attend(B, Hq, k.shape[1], D, pt.shape[1], _is_bf16(dtype), _p(qq), _p(k), _p(v), _p(pt),
                         _p(sl), _p(bs), _p(se), se.shape[-1], _p(cn), float(sm_scale), _p(out), _p(lse))
     return out, lse
+
+
+def attention_mass(q, k_cache, page_table, seq_lens, block_size, sel, count, sm_scale: float,
+                   dtype: str) -> np.ndarray:
+    """Share of each query head's exact attention over all its tokens that
+    the selection keeps (see oracle_attention_mass): fp64 [B][Hq]."""
+    qq, k = _store(q, dtype), _store(k_cache, dtype)
+    pt, sl, bs = _i32(page_table), _i32(seq_lens), _i32(block_size)
+    se, cn = _i32(sel), _i32(count)
+    B, Hq, D = qq.shape
+    mass = np.empty((B, Hq), dtype=np.float64)
+    lib().oracle_attention_mass(B, Hq, k.shape[1], D, pt.shape[1], _is_bf16(dtype), _p(qq), _p(k), _p(pt), _p(sl),
+                                _p(bs), _p(se), se.shape[-1], _p(cn), float(sm_scale), _p(mass))
+    return mass
+
+
+CALIBRATION_SIZES = (16, 32, 64)
+
+
+def head_recall(x, block_size: int, budget: int, sm_scale: float, fmt: str = "int4") -> np.ndarray:
+    """Recall of every KV head when all heads use `block_size` (Figure 3's
+    x axis): run centroids, quantization (format fmt), estimation and top-K
+    at that block size, then average the attention mass kept over the
+    sequences and the head's query group.  fp64 [Hkv]."""
+    Hkv = x.k_cache.shape[1]
+    bs = np.full(Hkv, int(block_size), dtype=np.int32)
+    c = centroids(x.k_cache, x.page_table, x.seq_lens, bs, x.dtype)
+    qf = quantize_fmt(c, x.seq_lens, bs, fmt)
+    s = scores_dense(x.q, qf.deq, x.seq_lens, bs, x.dtype)
+    cap = sel_capacity(x.seq_lens, bs, budget)
+    sel, cnt = select(s, x.seq_lens, bs, budget, cap)
+    mass = attention_mass(x.q, x.k_cache, x.page_table, x.seq_lens, bs, sel, cnt, sm_scale, x.dtype)
+    B, Hq = mass.shape
+    G = Hq // Hkv
+    return mass.reshape(B, Hkv, G).mean(axis=(0, 2))
+
+
+def assign_block_sizes(recall: np.ndarray, threshold: float) -> np.ndarray:
+    """The allocation rule (reading of Figure 3 and the heatmap after it):
+    recall[k][h] is head h's recall at block size CALIBRATION_SIZES[k]; its
+    normalized recall is recall / recall at 16 (1 when that is 0); the head
+    gets the largest block size whose normalized recall is >= threshold,
+    else 16.  int32 [Hkv]."""
+    r = np.asarray(recall, dtype=np.float64)
+    out = np.full(r.shape[1], CALIBRATION_SIZES[0], dtype=np.int32)
+    for h in range(r.shape[1]):
+        base = r[0, h]
+        for k in range(len(CALIBRATION_SIZES) - 1, 0, -1):
+            norm = r[k, h] / base if base > 0 else 1.0
+            if norm >= threshold:
+                out[h] = CALIBRATION_SIZES[k]
+                break
+    return out
 
 
 def sel_capacity(seq_lens, block_size, budget: int) -> int:

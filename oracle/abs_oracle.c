@@ -526,6 +526,60 @@ void oracle_attend(int B, int Hq, int Hkv, int D, int max_pages, int is_bf16,
     }
 }
 
+/* ---- calibration: attention mass kept by a selection -------------------- */
+
+/* Figure 3 of the page plots, per head, recall against block size,
+ * normalized by the recall at block size 16.  Reading: the recall of a
+ * selection for query head i is the share of i's exact attention over all
+ * L_b tokens that falls on the kept tokens,
+ *     mass_i = sum_{t kept} exp(z_t) / sum_{t < L_b} exp(z_t),
+ * z_t = sm_scale * q_i . k_t, in fp64 (both sums taken with the maximum
+ * over all tokens subtracted).  mass: [B][Hq]. */
+void oracle_attention_mass(int B, int Hq, int Hkv, int D, int max_pages, int is_bf16,
+                           const void *q, const void *k_cache, const int32_t *page_table,
+                           const int32_t *seq_lens, const int32_t *block_size,
+                           const int32_t *sel, int sel_cap, const int32_t *count, double sm_scale,
+                           double *mass)
+{
+    int G = Hq / Hkv;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        for (int h = 0; h < Hkv; ++h) {
+            int64_t L = seq_lens[b];
+            int bs = block_size[h];
+            const int32_t *blk = sel + ((size_t)b * Hkv + h) * sel_cap;
+            int64_t K = count[(size_t)b * Hkv + h];
+            unsigned char *kept = (unsigned char *)calloc((size_t)L, 1);
+            for (int64_t i = 0; i < K; ++i)
+                for (int64_t t = (int64_t)blk[i] * bs; t < (int64_t)(blk[i] + 1) * bs && t < L; ++t)
+                    kept[t] = 1;
+            double *z = (double *)malloc(sizeof(double) * (size_t)L);
+            for (int g = 0; g < G; ++g) {
+                int i = h * G + g;
+                size_t qrow = ((size_t)b * Hq + i) * D;
+                double m = -INFINITY;
+                for (int64_t t = 0; t < L; ++t) {
+                    double s = 0.0;
+                    for (int d = 0; d < D; ++d)
+                        s += elem(q, is_bf16, qrow + d) *
+                             cache_at(k_cache, is_bf16, page_table, max_pages, Hkv, D, b, h, t, d);
+                    z[t] = sm_scale * s;
+                    if (z[t] > m) m = z[t];
+                }
+                double all = 0.0, in = 0.0;
+                for (int64_t t = 0; t < L; ++t) {
+                    double e = exp(z[t] - m);
+                    all += e;
+                    if (kept[t]) in += e;
+                }
+                mass[(size_t)b * Hq + i] = in / all;
+            }
+            free(z);
+            free(kept);
+        }
+    }
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP

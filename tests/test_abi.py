@@ -25,7 +25,7 @@ def header_functions():
 
 def test_exports_every_declared_call():
     names = header_functions()
-    assert len(names) == 12
+    assert len(names) == 14
     assert sorted(A.EXPORTS) == names
     L = A.lib()
     for n in names:
@@ -194,6 +194,35 @@ def test_centroid_format_validation():
         assert status_of(lambda: A.abs_update_centroids(h.kv, h.bmap, c, 1, None, 0)) == I
         assert status_of(lambda: A.abs_score_select(h.kv, h.bmap, c, FAKE, 64, FAKE, cap, FAKE, FAKE, need_s,
                                                     0)) == I
+
+
+def test_assign_block_sizes_follows_the_oracle_rule(oracle_mod):
+    """The C host rule and the oracle's agree on random tables (fp32 recalls,
+    a threshold exact in fp32) and on hand-made edge cases."""
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        r = rng.uniform(0, 1, (3, 16)).astype(np.float32)
+        r[1:] = np.minimum(1, r[0] * rng.uniform(0.8, 1.1, (2, 16))).astype(np.float32)
+        r[:, 0] = 0.0
+        np.testing.assert_array_equal(A.abs_assign_block_sizes(r, 0.9375),
+                                      oracle_mod.assign_block_sizes(r.astype(np.float64), 0.9375))
+    edge = np.array([[0.5, 0.5, 0.0], [0.46875, 0.25, 0.0], [0.25, 0.5, 0.0]], dtype=np.float32)
+    np.testing.assert_array_equal(A.abs_assign_block_sizes(edge, 0.9375), [32, 64, 64])
+
+
+def test_calibration_call_validation():
+    I = A.ABS_ERR_INVALID_ARG
+    ok = np.full((3, 4), 0.5, dtype=np.float32)
+    assert status_of(lambda: A.abs_assign_block_sizes(ok, 0.0)) == I
+    assert status_of(lambda: A.abs_assign_block_sizes(ok, float("nan"))) == I
+    for bad in (1.5, -0.1, float("nan")):
+        r = ok.copy()
+        r[2, 1] = bad
+        assert status_of(lambda: A.abs_assign_block_sizes(r, 0.95)) == I
+    h = Host()
+    assert status_of(lambda: A.abs_head_recall(h.kv, FAKE, None, FAKE, 0)) == I
+    h.kv.num_q_heads = 3
+    assert status_of(lambda: A.abs_head_recall(h.kv, FAKE, FAKE, FAKE, 0)) == I
 
 
 def test_too_many_blocks_per_head_is_unsupported():

@@ -1,0 +1,105 @@
+"""Pins of the oracle's block-size calibration (Figure 3 of the AB-Sparse
+page: per-head recall against block size, normalized by the recall at 16;
+the heatmap after it: the per-head map).  Recall = the share of each query
+head's exact attention that the selection keeps; the rule = the largest block
+size whose normalized recall reaches the threshold.
+
+Pins: a selection of every block keeps everything; with identical keys the
+attention is uniform, so the kept share is (kept tokens) / L exactly; the
+share equals exp(lse_kept - lse_all) from the oracle's own attention (two
+different computations); the rule on hand-made tables; and on a synthetic
+layer whose heads hold their needles scattered or in aligned runs, the
+scattered head gets 16, clustered heads 64, and a head with few short runs
+32 (the structure the inputs plant)."""
+import numpy as np
+import pytest
+
+from block_sparse_attention_abs_amd import workload as W
+
+
+def layer(dtype="f32", context=8192, runs=(1, 2, 4, 64), budget=1536):
+    w = W.PRESETS[1].scaled(batch=2, context=context, token_budget=budget, needles_per_head=64, num_q_heads=4 * len(runs),
+                            num_kv_heads=len(runs), dtype=dtype)
+    return W.make_layer(w, needle_runs=list(runs))
+
+
+def sm(D):
+    return float(np.float32(1.0 / np.sqrt(D)))
+
+
+def _select(oracle_mod, x, bs_val, budget):
+    bs = np.full(x.k_cache.shape[1], bs_val, dtype=np.int32)
+    c = oracle_mod.centroids(x.k_cache, x.page_table, x.seq_lens, bs, x.dtype)
+    qz = oracle_mod.quantize(c, x.seq_lens, bs)
+    s = oracle_mod.scores(x.q, qz, x.seq_lens, bs, x.dtype)
+    cap = oracle_mod.sel_capacity(x.seq_lens, bs, budget)
+    sel, cnt = oracle_mod.select(s, x.seq_lens, bs, budget, cap)
+    return bs, sel, cnt
+
+
+def test_every_block_kept_is_all_the_mass(oracle_mod):
+    x = layer(context=1000, runs=(1, 64))
+    x = W.make_layer(x.workload, seq_lens=[1000, 777], needle_runs=[1, 64])
+    bs, sel, cnt = _select(oracle_mod, x, 32, 1 << 20)
+    m = oracle_mod.attention_mass(x.q, x.k_cache, x.page_table, x.seq_lens, bs, sel, cnt, sm(128), x.dtype)
+    np.testing.assert_allclose(m, 1.0, rtol=0, atol=1e-15)
+    r = oracle_mod.head_recall(x, 64, 1 << 20, sm(128))
+    np.testing.assert_allclose(r, 1.0, rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("bs_val", [16, 32, 64])
+def test_identical_keys_give_uniform_attention(oracle_mod, bs_val):
+    """Every key equal: every z_t is equal, so the kept share is the kept
+    token count over L (ragged L: the last block is clipped)."""
+    x = layer(context=1000, runs=(1, 1))
+    x = W.make_layer(x.workload, seq_lens=[1000, 517], needle_runs=[1, 1], needles=False)
+    x.k_cache[:] = x.k_cache[x.page_table[0, 0], :, 3:4, :]
+    budget = 160
+    bs, sel, cnt = _select(oracle_mod, x, bs_val, budget)
+    m = oracle_mod.attention_mass(x.q, x.k_cache, x.page_table, x.seq_lens, bs, sel, cnt, sm(128), x.dtype)
+    G = x.q.shape[1] // x.k_cache.shape[1]
+    for b, L in enumerate(x.seq_lens.tolist()):
+        for h in range(x.k_cache.shape[1]):
+            kept = sum(min(bs_val, L - j * bs_val) for j in sel[b, h, :cnt[b, h]])
+            assert kept == min(L, (budget // bs_val) * bs_val) or kept < (budget // bs_val) * bs_val
+            np.testing.assert_allclose(m[b, h * G:(h + 1) * G], kept / L, rtol=1e-14)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mass_is_the_ratio_of_normalizers(oracle_mod, dtype):
+    """The kept share equals exp(lse over the kept tokens - lse over all
+    tokens), the latter two from the oracle's attention."""
+    x = layer(dtype=dtype, context=3000, runs=(1, 16, 64))
+    x = W.make_layer(x.workload, seq_lens=[3000, 2049], needle_runs=[1, 16, 64])
+    bs, sel, cnt = _select(oracle_mod, x, 32, 512)
+    m = oracle_mod.attention_mass(x.q, x.k_cache, x.page_table, x.seq_lens, bs, sel, cnt, sm(128), x.dtype)
+    _, lse_k = oracle_mod.attend(x.q, x.k_cache, x.v_cache, x.page_table, x.seq_lens, bs, sel, cnt, sm(128), x.dtype)
+    bs_a, sel_a, cnt_a = _select(oracle_mod, x, 32, 1 << 20)
+    _, lse_a = oracle_mod.attend(x.q, x.k_cache, x.v_cache, x.page_table, x.seq_lens, bs_a, sel_a, cnt_a, sm(128),
+                                 x.dtype)
+    np.testing.assert_allclose(m, np.exp(lse_k - lse_a), rtol=1e-12)
+    assert (m > 0).all() and (m < 1).all()
+
+
+def test_rule_on_hand_made_tables(oracle_mod):
+    r = np.array([[0.80, 0.80, 0.50, 0.0, 0.6, 0.9],
+                  [0.79, 0.50, 0.50, 0.0, 0.3, 0.9],
+                  [0.50, 0.40, 0.475, 0.0, 0.6, 0.9]])
+    # head 0: 32 only; head 1: neither; head 2: 64 at exactly the threshold;
+    # head 3: no recall at 16 (ratio 1) -> 64; head 4: 64 although 32 fails;
+    # head 5: flat -> 64
+    np.testing.assert_array_equal(oracle_mod.assign_block_sizes(r, 0.95), [32, 16, 64, 64, 64, 64])
+    np.testing.assert_array_equal(oracle_mod.assign_block_sizes(r, 1.01), [16, 16, 16, 16, 16, 16])
+
+
+def test_planted_sensitivity_is_recovered(oracle_mod):
+    """Heads with 64 scattered needles lose recall at 32 and 64 (fewer
+    blocks than needles), 2-token runs (32 sites) only at 64, and 4- and
+    64-token runs at neither."""
+    x = layer()
+    R = np.array([oracle_mod.head_recall(x, bs, 1536, sm(128)) for bs in (16, 32, 64)])
+    norm = R / R[0]
+    assert norm[1, 0] < 0.9 and norm[2, 0] < 0.9
+    assert norm[1, 1] > 0.97 and norm[2, 1] < 0.9
+    assert (norm[1:, 2:] > 0.99).all()
+    np.testing.assert_array_equal(oracle_mod.assign_block_sizes(R, 0.95), [16, 32, 64, 64])
