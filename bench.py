@@ -20,6 +20,13 @@ Prints ONE JSON line (see the "metric" field).  Options:
     --context N            override the workload's context length (tokens)
     --block-map M          "drawn" (the workload's seeded map) or 16, 32, 64
                            for a uniform map (all heads one block size)
+    --centroid-format F    int4 (default), int4_sym, int8, int4_tensor, bf16
+    --warm-cache           also time R steps on one layer copy (Infinity
+                           Cache warm), reported as warm_cache_step_us
+    --naive-per-size       also time the per-block-size variant: the heads of
+                           each block size as a layer of their own (cache
+                           copied per group before timing), one select and
+                           one decode call per group and step
     --calibrate-copy MIB   before the timed region, copy MIB MiB device to
                            device three times (a plain copy kernel of known
                            size, the scale for hardware byte counters)
@@ -48,7 +55,7 @@ METRIC = "sparse decode attn queries/s per layer at 32K/128K ctx; achieved HBM G
 # a hash of the kernel sources they were taken with; any other source
 # reports null.
 TRAFFIC = {}
-KERNEL_SOURCES = ("decode.hip", "device.hpp", "launch.hpp")
+KERNEL_SOURCES = ("decode.hip", "device.hpp", "launch.hpp", "abs_api.cpp")   # kernel + its launch layout
 
 
 def kernel_source_hash():
@@ -72,6 +79,8 @@ def parse():
     ap.add_argument("--calibrate-copy", type=int, default=0)
     ap.add_argument("--context", type=int, default=0)
     ap.add_argument("--block-map", default="drawn", choices=["drawn", "16", "32", "64"])
+    ap.add_argument("--warm-cache", action="store_true")
+    ap.add_argument("--naive-per-size", action="store_true")
     ap.add_argument("--centroid-format", default="int4",
                     choices=["int4", "int4_sym", "int8", "int4_tensor", "bf16"])
     return ap.parse_args()
@@ -227,8 +236,10 @@ def main():
     sel_us = np.array([timed(g_sel, sreps) / (sreps * R) * 1e3 for _ in range(5)])
     dec_us = np.array([timed(g_dec, sreps) / (sreps * R) * 1e3 for _ in range(5)])
     # warm Infinity Cache, for reference: R steps on the same layer copy
-    g_warm = capture(lambda i, st: step(0, st))
-    warm_us = float(np.median([timed(g_warm, sreps) / (sreps * R) * 1e3 for _ in range(5)]))
+    warm_us = None
+    if args.warm_cache:
+        g_warm = capture(lambda i, st: step(0, st))
+        warm_us = round(float(np.median([timed(g_warm, sreps) / (sreps * R) * 1e3 for _ in range(5)])), 3)
     # keeping the centroids current after one appended token per sequence
     # (abs_update_centroids; the last block of every head is recomputed)
     oor = torch.zeros((B, w.num_kv_heads), dtype=torch.int32, device=dev)
@@ -239,6 +250,10 @@ def main():
 
     g_upd = capture(update_call)
     upd_us = float(np.median([timed(g_upd, sreps) / (sreps * R) * 1e3 for _ in range(5)]))
+
+    naive = None
+    if args.naive_per_size:
+        naive = naive_per_size(A, torch, x, layers, q, budget, sm, fmt, R, capture, timed, sreps)
 
     ab = algorithmic_bytes(x, budget, lambda L, bs: min(L, max(1, budget // bs) * bs), code_bits)
     dec_avg = float(np.median(dec_us))
@@ -277,7 +292,7 @@ def main():
                  "score_select_us": round(float(np.median(sel_us)), 3), "sparse_decode_us": round(dec_avg, 3),
                  "sparse_decode_us_min_max": [round(float(dec_us.min()), 3), round(float(dec_us.max()), 3)],
                  "step_us_p10_p50_p90": [round(float(np.percentile(per_rep, q)), 3) for q in (10, 50, 90)],
-                 "warm_cache_step_us": round(warm_us, 3),
+                 "warm_cache_step_us": warm_us,
                  "update_centroids_us": round(upd_us, 3),
                  "build_plus_step_us": round(build_med * 1e3 + ms_per_step * 1e3, 3),
                  "wall_s": round(wall, 4)},
@@ -285,7 +300,75 @@ def main():
                   "hbm_gbs": round(build_bytes / (build_med * 1e-3) / 1e9, 1)},
         "needle_recall": recall,
     }
+    if naive is not None:
+        rec["naive_per_size"] = naive
     print(json.dumps(rec), flush=True)
+
+
+def naive_per_size(A, torch, x, layers, q, budget, sm, fmt, R, capture, timed, sreps):
+    """The per-block-size variant: for each block size present, the heads of
+    that size become a layer of their own (K/V copied per group and layer
+    copy, outside the timing); a step calls abs_score_select and
+    abs_sparse_decode once per group."""
+    B, Hq, D = x.q.shape
+    Hkv = x.k_cache.shape[1]
+    G = Hq // Hkv
+    dev = q.device
+    groups = []
+    for bs in sorted(set(int(b) for b in x.block_size)):
+        heads = [h for h in range(Hkv) if int(x.block_size[h]) == bs]
+        hidx = torch.tensor(heads, dtype=torch.long, device=dev)
+        qidx = torch.tensor([h * G + g for h in heads for g in range(G)], dtype=torch.long, device=dev)
+        bs_np = np.full(len(heads), bs, dtype=np.int32)
+        gl = []
+        for L in layers:
+            t = A.PagedKV(L.k_cache[:, hidx].contiguous(), L.v_cache[:, hidx].contiguous(), L.page_table, L.seq_lens,
+                          L.seq_lens_host, L.block_size, L.block_size_host, L.centroid_off, len(heads) * G, x.dtype)
+            gl.append(t.with_block_sizes(bs_np))
+        cents = [A.build_centroids(g, A.Centroids.empty(g, fmt)) for g in gl]
+        qg = q[:, qidx].contiguous()
+        cap = gl[0].select_capacity(budget)
+        grp = dict(bs=bs, heads=heads, layers=gl, cents=cents, q=qg, cap=cap,
+                   sel=torch.zeros((B, len(heads), cap), dtype=torch.int32, device=dev),
+                   cnt=torch.zeros((B, len(heads)), dtype=torch.int32, device=dev),
+                   out=torch.empty((B, len(heads) * G, D), dtype=A.torch_dtype(x.dtype), device=dev),
+                   lse=torch.empty((B, len(heads) * G), dtype=torch.float32, device=dev),
+                   ws_s=A.workspace(gl[0].workspace_bytes(budget, A.ABS_OP_SELECT), dev),
+                   ws_d=A.workspace(gl[0].workspace_bytes(budget, A.ABS_OP_DECODE), dev))
+        groups.append(grp)
+    torch.cuda.synchronize()
+
+    def sel_g(i, st):
+        for g in groups:
+            L, c = g["layers"][i % R], g["cents"][i % R]
+            A.abs_score_select(L.kv, L.bmap, c.desc, int(g["q"].data_ptr()), budget, int(g["sel"].data_ptr()),
+                               g["cap"], int(g["cnt"].data_ptr()), int(g["ws_s"].data_ptr()), g["ws_s"].numel(), st)
+
+    def dec_g(i, st):
+        for g in groups:
+            L = g["layers"][i % R]
+            A.abs_sparse_decode(L.kv, L.bmap, int(g["q"].data_ptr()), int(g["sel"].data_ptr()), g["cap"],
+                                int(g["cnt"].data_ptr()), budget, sm, int(g["out"].data_ptr()),
+                                int(g["lse"].data_ptr()), int(g["ws_d"].data_ptr()), g["ws_d"].numel(), st)
+
+    def step_g(i, st):
+        sel_g(i, st)
+        dec_g(i, st)
+
+    st0 = int(torch.cuda.current_stream().cuda_stream)
+    for i in range(R):
+        step_g(i, st0)
+    torch.cuda.synchronize()
+    g_step, g_sel, g_dec = capture(step_g), capture(sel_g), capture(dec_g)
+
+    def us(g):
+        return round(float(np.median([timed(g, sreps) / (sreps * R) * 1e3 for _ in range(5)])), 3)
+
+    res = {"step_us": us(g_step), "score_select_us": us(g_sel), "sparse_decode_us": us(g_dec),
+           "groups": {str(g["bs"]): len(g["heads"]) for g in groups}}
+    del groups
+    torch.cuda.empty_cache()
+    return res
 
 
 def needle_recall(x, sel, cnt):

@@ -180,6 +180,13 @@ struct DecodeLayout {
 #ifndef ABS_DECODE_PIPE_WGS
 #define ABS_DECODE_PIPE_WGS 256
 #endif
+// At most this many splits per (b, h) outside the double-buffered layout:
+// the merging workgroup reads the splits' partials 8 at a time, so a
+// small layer does better with more pages per workgroup than with a long
+// merge.
+#ifndef ABS_DECODE_MAX_SPLITS
+#define ABS_DECODE_MAX_SPLITS 32
+#endif
 // 1: the last split workgroup of each (b, h) merges (one launch); 0: a merge launch.
 #ifndef ABS_DECODE_FUSED_MERGE
 #define ABS_DECODE_FUSED_MERGE 1
@@ -197,6 +204,12 @@ DecodeLayout decode_layout(const Plan& p) {
     l.chunk = (int)std::min<int64_t>(cmax, ideal >= 8 ? 8 : ideal >= 4 ? 4 : ideal >= 2 ? 2 : 1);
     l.ppw = (int)std::min<int64_t>(absk::kMaxPagesPerWg, ceil_div64(ideal, l.chunk) * l.chunk);
     l.splits = (int)ceil_div64(maxp, l.ppw);
+    if (l.splits > ABS_DECODE_MAX_SPLITS) {
+        const int64_t need = ceil_div64(maxp, ABS_DECODE_MAX_SPLITS);
+        l.chunk = (int)std::min<int64_t>(cmax, need >= 8 ? 8 : need >= 4 ? 4 : need >= 2 ? 2 : 1);
+        l.ppw = (int)std::min<int64_t>(absk::kMaxPagesPerWg, ceil_div64(need, l.chunk) * l.chunk);
+        l.splits = (int)ceil_div64(maxp, l.ppw);
+    }
     // Enough pages for two chunks of 8 per workgroup at about
     // ABS_DECODE_PIPE_WGS workgroups (two per compute unit): stream them
     // double-buffered instead.
