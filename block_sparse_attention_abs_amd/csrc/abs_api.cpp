@@ -185,7 +185,7 @@ struct DecodeLayout {
 // small layer does better with more pages per workgroup than with a long
 // merge.
 #ifndef ABS_DECODE_MAX_SPLITS
-#define ABS_DECODE_MAX_SPLITS 32
+#define ABS_DECODE_MAX_SPLITS 16
 #endif
 // 1: the last split workgroup of each (b, h) merges (one launch); 0: a merge launch.
 #ifndef ABS_DECODE_FUSED_MERGE

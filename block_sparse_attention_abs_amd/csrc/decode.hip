@@ -24,6 +24,11 @@
 //         per (b, query head).
 #include "device.hpp"
 
+// Build-time tuning: partials the merging workgroup loads per pass.
+#ifndef ABS_DECODE_MERGE_BATCH
+#define ABS_DECODE_MERGE_BATCH 8
+#endif
+
 namespace absk {
 namespace {
 
@@ -416,6 +421,7 @@ __global__ __launch_bounds__(256 * RG, (DecodeOccupancy<T, D, GT, PIPE, MF>::val
     }
     __syncthreads();
     if (!s_last) return;
+    constexpr int MB = ABS_DECODE_MERGE_BATCH;   // partials per merge pass
     for (int idx = 2 * (int)threadIdx.x; idx < GT * D; idx += 2 * (int)blockDim.x) {
         const int gg = idx / D, d = idx - gg * D;
         if (gg >= g.G) continue;
@@ -424,19 +430,19 @@ __global__ __launch_bounds__(256 * RG, (DecodeOccupancy<T, D, GT, PIPE, MF>::val
         const float* po = part_o + bi * splits * D + d;
         float mg = NEG, ls = 0.0f;
         float2 acc = make_float2(0.0f, 0.0f);
-        for (int s0 = 0; s0 < nact; s0 += 8) {
-            // 16 loads in flight (indices clamped, so no load waits on a
-            // branch), then one max and one weighted sum over the 8 splits
-            float2 mlv[8], ov[8];
+        for (int s0 = 0; s0 < nact; s0 += MB) {
+            // 2 MB loads in flight (indices clamped, so no load waits on a
+            // branch), then one max and one weighted sum over the MB splits
+            float2 mlv[MB], ov[MB];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
+            for (int k = 0; k < MB; ++k) {
                 const int sk = min(s0 + k, nact - 1);
                 mlv[k] = load2_agent(ml + 2 * sk);
                 ov[k] = load2_agent(po + (int64_t)sk * D);
             }
             float bm = NEG;
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
+            for (int k = 0; k < MB; ++k)
                 if (s0 + k < nact) bm = fmaxf(bm, mlv[k].x);
             const float mn = fmaxf(mg, bm);
             if (mn == NEG) continue;                      // only empty partials so far
@@ -445,7 +451,7 @@ __global__ __launch_bounds__(256 * RG, (DecodeOccupancy<T, D, GT, PIPE, MF>::val
             acc.x *= a;
             acc.y *= a;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
+            for (int k = 0; k < MB; ++k) {
                 const float w = s0 + k < nact ? exp2f(mlv[k].x - mn) : 0.0f;   // empty partial: m = -inf, w = 0
                 ls = fmaf(mlv[k].y, w, ls);
                 acc.x = fmaf(ov[k].x, w, acc.x);
