@@ -18,6 +18,7 @@ Prints ONE JSON line (see the "metric" field).  Options:
     --replicas R           layer copies cycled through (default 8)
     --no-cpu-baseline      skip timing the CPU oracle
     --context N            override the workload's context length (tokens)
+    --batch B              override the workload's batch (sequences)
     --block-map M          "drawn" (the workload's seeded map) or 16, 32, 64
                            for a uniform map (all heads one block size)
     --centroid-format F    int4 (default), int4_sym, int8, int4_tensor, bf16
@@ -78,6 +79,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", type=int, default=0)
     ap.add_argument("--context", type=int, default=0)
+    ap.add_argument("--batch", type=int, default=0)
     ap.add_argument("--block-map", default="drawn", choices=["drawn", "16", "32", "64"])
     ap.add_argument("--warm-cache", action="store_true")
     ap.add_argument("--naive-per-size", action="store_true")
@@ -121,6 +123,8 @@ def main():
     w = W.PRESETS[cfg]
     if args.context:
         w = w.scaled(context=args.context)
+    if args.batch:
+        w = w.scaled(batch=args.batch)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.time()

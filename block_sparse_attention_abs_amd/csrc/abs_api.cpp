@@ -417,6 +417,14 @@ abs_status abs_score_select(const abs_paged_kv* kv, const abs_block_map* map, co
                 if (a.ntiles < absk::kMaxScoreTiles) tiles[a.ntiles] = (uint32_t)(b * p.g.Hkv + h) << 8 | (uint32_t)t;
         }
     a.tiles_host = a.ntiles <= absk::kMaxScoreTiles ? tiles : nullptr;
+    // per-head cumulative tiles of the longest sequence (the grid when the list does not fit)
+    int max_len = 0;
+    for (int b = 0; b < p.g.B; ++b) max_len = std::max(max_len, kv->seq_lens_host[b]);
+    a.head_tiles.cum[0] = 0;
+    for (int h = 0; h < p.g.Hkv; ++h)
+        a.head_tiles.cum[h + 1] =
+            a.head_tiles.cum[h] +
+            (uint32_t)ceil_div64(ceil_div64(max_len, map->block_size_host[h]), absk::kScoreBlocksPerWg);
     return hip_status(absk::launch_select(p.g, p.dt, a, static_cast<hipStream_t>(stream)), "score_select");
 }
 

@@ -73,11 +73,17 @@ constexpr int kMaxBlocksPerHead = 65536;   // top-K keeps N_{b,h} keys in regist
 // The score launch: 256 blocks per workgroup.
 // When the tiles of all heads fit kMaxScoreTiles, they are listed in the
 // kernel arguments ((b*Hkv + h) << 8 | tile) and the grid has exactly that
-// many workgroups; otherwise the grid is (max tiles per head, B*Hkv).
+// many workgroups.  Otherwise the grid is (sum over heads of the tiles that
+// head needs for the longest sequence, B): x is mapped to (head, tile)
+// through the per-head cumulative tile counts in HeadTiles, and only the
+// workgroups past a shorter sequence's blocks have nothing to do.
 constexpr int kScoreBlocksPerWg = 256;
 constexpr int kMaxScoreTiles = 512;
 struct ScoreTiles {
     uint32_t t[kMaxScoreTiles];
+};
+struct HeadTiles {
+    uint32_t cum[kMaxKvHeads + 1];   // cum[0] = 0, cum[h + 1] - cum[h] = tiles of head h
 };
 
 struct SelectArgs {
@@ -95,6 +101,7 @@ struct SelectArgs {
     int max_n;        // largest N_{b,h}
     int ntiles;       // score tiles over all heads
     const uint32_t* tiles_host;   // their list (host, valid during the call) or null
+    HeadTiles head_tiles;         // per-head cumulative tiles for the longest sequence
 };
 
 hipError_t launch_select(const Geom& g, DType dt, const SelectArgs& a, hipStream_t s);

@@ -125,11 +125,22 @@ __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restr
     }
 }
 
+// Grid (tiles per sequence, B): x -> (head, tile) by a binary search of the
+// per-head cumulative tile counts (uniform, kernel-argument reads only).
 template <typename T, int D, int GT, int BITS>
-__global__ __launch_bounds__(ABS_SCORE_NT) void k_score_grid(Geom g, const uint8_t* __restrict__ codes,
-                                                    const float* __restrict__ scale, const float* __restrict__ lo,
-                                                    const T* __restrict__ q, float* __restrict__ scores, int stride) {
-    score_tile<T, D, GT, BITS>(g, codes, scale, lo, q, scores, stride, blockIdx.y, blockIdx.x);
+__global__ __launch_bounds__(ABS_SCORE_NT) void k_score_seq(Geom g, const uint8_t* __restrict__ codes,
+                                                   const float* __restrict__ scale, const float* __restrict__ lo,
+                                                   const T* __restrict__ q, float* __restrict__ scores, int stride,
+                                                   const HeadTiles ht) {
+    const uint32_t x = blockIdx.x;
+    int hl = 0, hh = g.Hkv;                          // ht.cum[hl] <= x < ht.cum[hh]
+    while (hh - hl > 1) {
+        const int mid = (hl + hh) >> 1;
+        if (ht.cum[mid] <= x) hl = mid;
+        else hh = mid;
+    }
+    score_tile<T, D, GT, BITS>(g, codes, scale, lo, q, scores, stride, (int)blockIdx.y * g.Hkv + hl,
+                               (int)(x - ht.cum[hl]));
 }
 
 template <typename T, int D, int GT, int BITS>
@@ -440,10 +451,10 @@ void launch_score(const Geom& g, const SelectArgs& a, hipStream_t s) {
         else ABS_SCORE(8);
 #undef ABS_SCORE
     } else {
-        const dim3 sgrid(ceil_div(a.max_n, kScoreBlocksPerWg), g.B * g.Hkv);
+        const dim3 sgrid(a.head_tiles.cum[g.Hkv], g.B);
 #define ABS_SCORE(GT_)                                                                                       \
-    hipLaunchKernelGGL((k_score_grid<T, D, GT_, BITS>), sgrid, dim3(ABS_SCORE_NT), 0, s, g, a.codes, a.scale, a.lo, \
-                       q, a.scores, a.stride)
+    hipLaunchKernelGGL((k_score_seq<T, D, GT_, BITS>), sgrid, dim3(ABS_SCORE_NT), 0, s, g, a.codes, a.scale, a.lo, \
+                       q, a.scores, a.stride, a.head_tiles)
         if (g.G <= 1) ABS_SCORE(1);
         else if (g.G <= 2) ABS_SCORE(2);
         else if (g.G <= 4) ABS_SCORE(4);

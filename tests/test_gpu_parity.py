@@ -115,6 +115,21 @@ def test_budget_covering_context_is_dense_attention(oracle_mod, dtype):
     check_attention(r.out, r.lse, ref.out, ref.lse, dtype)
 
 
+@pytest.mark.parametrize("bs", [(16,) * 8, (16, 64, 32, 64, 16, 32, 64, 64)])
+def test_many_score_tiles_ragged(oracle_mod, bs):
+    """More score tiles than the launch can list (the per-sequence grid):
+    40 ragged sequences, some far shorter than the longest, so workgroups
+    past their blocks must leave without writing."""
+    rng = np.random.default_rng(11)
+    lens = [32768, 1, 17, 4096, 255, 256, 257] + rng.integers(1, 32769, 33).tolist()
+    x = W.make_layer(P[1].scaled(batch=len(lens), context=32768, token_budget=1024, needles_per_head=8,
+                                 fixed_block_sizes=bs), seq_lens=lens)
+    tiles = sum(-(-(-(-L // b)) // 256) for L in lens for b in bs)
+    print(f"[gpu parity] many score tiles: {tiles} tiles, bs={bs}", flush=True)
+    assert tiles > 512
+    _run_and_compare(oracle_mod, x, budget=1024)
+
+
 def test_tiny_lengths_partial_pages_and_blocks(oracle_mod):
     lens = [1, 15, 16, 17, 33, 63, 64, 65, 100]
     x = W.make_layer(P[1].scaled(batch=len(lens), context=100, needles_per_head=2), seq_lens=lens)
