@@ -97,7 +97,7 @@ typedef struct abs_paged_kv {
  * Figure 3; static per Figure 5's text).
  *   block_size_host / block_size: host / device int32 [num_kv_heads], each in
  *       {16, 32, 64}; bs_h / 16 is the head's page stride.  The two must hold
- *       the same values; this build's kernels take them from the host copy
+ *       the same values; the kernels take them from the host copy
  *       (passed in the launch), the device copy must still be non-null.
  *   centroid_off: device int64 [num_seqs * num_kv_heads + 1]; the first
  *       centroid row of (b, h) is centroid_off[b * num_kv_heads + h], with
