@@ -107,39 +107,79 @@ __global__ __launch_bounds__(256) void k_centroid_mean(Geom g, float* __restrict
     }
 }
 
+// One workgroup of kRangeThreads per (b, h): S = kRangeThreads / D stripes
+// of tiles per channel, four tiles' loads in flight per thread, then LDS.
+constexpr int kRangeThreads = 1024;
+
 template <int D>
-__global__ __launch_bounds__(D) void k_centroid_range(Geom g, const float* __restrict__ pmin,
-                                                      const float* __restrict__ pmax, int tiles, int fmt,
-                                                      float* __restrict__ scale, float* __restrict__ lo) {
+__global__ __launch_bounds__(kRangeThreads) void k_centroid_range(Geom g, const float* __restrict__ pmin,
+                                                                  const float* __restrict__ pmax, int tiles, int fmt,
+                                                                  float* __restrict__ scale, float* __restrict__ lo) {
+    constexpr int S = kRangeThreads / D;
     const int bh = blockIdx.x;
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
     const int N = ceil_div(g.seq_lens[b], block_size_of(g, h));
     const int nt = ceil_div(N, kBuildTile);
-    const int d = threadIdx.x;
+    const int d = threadIdx.x % D, stripe = threadIdx.x / D;
+    const float* pn = pmin + (int64_t)bh * tiles * D + d;
+    const float* px = pmax + (int64_t)bh * tiles * D + d;
     float a = __builtin_inff(), z = -__builtin_inff();
-    for (int t = 0; t < nt; ++t) {
-        a = fminf(a, pmin[((int64_t)bh * tiles + t) * D + d]);
-        z = fmaxf(z, pmax[((int64_t)bh * tiles + t) * D + d]);
+    int t = stripe;
+    for (; t + 3 * S < nt; t += 4 * S) {
+        float an[4], zx[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            an[k] = pn[(int64_t)(t + k * S) * D];
+            zx[k] = px[(int64_t)(t + k * S) * D];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            a = fminf(a, an[k]);
+            z = fmaxf(z, zx[k]);
+        }
+    }
+    for (; t < nt; t += S) {
+        a = fminf(a, pn[(int64_t)t * D]);
+        z = fmaxf(z, px[(int64_t)t * D]);
+    }
+    __shared__ float s_mn[S][D], s_mx[S][D];
+    __shared__ float s_hmn[D / 64], s_hmx[D / 64];
+    s_mn[stripe][d] = a;
+    s_mx[stripe][d] = z;
+    __syncthreads();
+    // stripe 0 (the first D threads: whole wavefronts) finishes; every thread
+    // still reaches each barrier
+    const bool mine = stripe == 0;
+    if (mine) {
+#pragma unroll
+        for (int k = 1; k < S; ++k) {
+            a = fminf(a, s_mn[k][d]);
+            z = fmaxf(z, s_mx[k][d]);
+        }
     }
     if (fmt == kInt4Tensor) {   // one range for the whole head: min/max over the channels too
-        __shared__ float s_mn[D / 64], s_mx[D / 64];
-        for (int o = 32; o > 0; o >>= 1) {
-            a = fminf(a, __shfl_xor(a, o));
-            z = fmaxf(z, __shfl_xor(z, o));
-        }
-        if ((d & 63) == 0) {
-            s_mn[d / 64] = a;
-            s_mx[d / 64] = z;
+        if (mine) {
+            for (int o = 32; o > 0; o >>= 1) {
+                a = fminf(a, __shfl_xor(a, o));
+                z = fmaxf(z, __shfl_xor(z, o));
+            }
+            if ((d & 63) == 0) {
+                s_hmn[d / 64] = a;
+                s_hmx[d / 64] = z;
+            }
         }
         __syncthreads();
-        a = s_mn[0];
-        z = s_mx[0];
+        if (mine) {
+            a = s_hmn[0];
+            z = s_hmx[0];
 #pragma unroll
-        for (int w = 1; w < D / 64; ++w) {
-            a = fminf(a, s_mn[w]);
-            z = fmaxf(z, s_mx[w]);
+            for (int w = 1; w < D / 64; ++w) {
+                a = fminf(a, s_hmn[w]);
+                z = fmaxf(z, s_hmx[w]);
+            }
         }
     }
+    if (!mine) return;
     float s = 0.0f, zp = 0.0f;
     if (fmt == kInt4Sym) {
         const float amax = -a > z ? -a : z;   // max |c|
@@ -246,8 +286,8 @@ template <typename T, int D>
 hipError_t build_impl(const Geom& g, const BuildArgs& a, hipStream_t s) {
     const dim3 grid(a.tiles, g.B * g.Hkv);
     hipLaunchKernelGGL((k_centroid_mean<T, D>), grid, dim3(256), 0, s, g, a.staging, a.pmin, a.pmax, a.tiles);
-    hipLaunchKernelGGL((k_centroid_range<D>), dim3(g.B * g.Hkv), dim3(D), 0, s, g, a.pmin, a.pmax, a.tiles, a.fmt,
-                       a.scale, a.lo);
+    hipLaunchKernelGGL((k_centroid_range<D>), dim3(g.B * g.Hkv), dim3(kRangeThreads), 0, s, g, a.pmin, a.pmax,
+                       a.tiles, a.fmt, a.scale, a.lo);
 #define ABS_QUANT(F_)                                                                                         \
     hipLaunchKernelGGL((k_centroid_quantize<D, F_>), grid, dim3(256), 0, s, g, a.staging, a.scale, a.lo, a.codes, \
                        a.tiles)
