@@ -46,6 +46,7 @@ struct Plan {
     absk::DType dt{};
     int64_t total_blocks = 0;
     int max_n = 0;            // largest N_{b,h}
+    int max_len = 0;          // largest L_b
     int sel_cap = 0;          // largest K_{b,h}
     int max_pages_read = 0;   // largest K_{b,h} * (bs_h / 16)
     const int32_t* block_size_dev = nullptr;   // the descriptor's device copy (kernels use the host values)
@@ -106,6 +107,8 @@ abs_status check_geometry(const abs_paged_kv* kv, const abs_block_map* map, Plan
     }
     p->total_blocks = 0;
     p->max_n = 0;
+    p->max_len = 0;
+    for (int b = 0; b < g.B; ++b) p->max_len = std::max(p->max_len, kv->seq_lens_host[b]);
     for (int b = 0; b < g.B; ++b)
         for (int h = 0; h < g.Hkv; ++h) {
             const int64_t n = ceil_div64(kv->seq_lens_host[b], map->block_size_host[h]);
@@ -149,10 +152,10 @@ struct BuildLayout {
 
 BuildLayout build_layout(const Plan& p) {
     BuildLayout l;
-    l.tiles = (int)ceil_div64(p.max_n, absk::kBuildTile);
+    l.tiles = (int)ceil_div64(p.max_len, absk::kBuildTileTokens);
     const size_t part = align_up((size_t)p.g.B * p.g.Hkv * l.tiles * p.g.D * sizeof(float));
-    l.staging = 0;   // per (b, h): tiles * kBuildTile rows, whatever the centroid offsets
-    l.pmin = align_up((size_t)p.g.B * p.g.Hkv * l.tiles * absk::kBuildTile * p.g.D * sizeof(float));
+    l.staging = 0;   // per (b, h): max N rows, whatever the centroid offsets
+    l.pmin = align_up((size_t)p.g.B * p.g.Hkv * p.max_n * p.g.D * sizeof(float));
     l.pmax = l.pmin + part;
     l.bytes = l.pmax + part;
     return l;
@@ -356,6 +359,7 @@ abs_status abs_build_centroids(const abs_paged_kv* kv, const abs_block_map* map,
     a.pmin = reinterpret_cast<float*>(ws_at(workspace, l.pmin));
     a.pmax = reinterpret_cast<float*>(ws_at(workspace, l.pmax));
     a.tiles = l.tiles;
+    a.stage_rows = p.max_n;
     a.fmt = out->format;
     return hip_status(absk::launch_build(p.g, p.dt, a, static_cast<hipStream_t>(stream)), "build_centroids");
 }

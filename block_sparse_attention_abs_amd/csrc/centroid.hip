@@ -2,12 +2,12 @@
 // Figure 1's block representation; Figure 8's INT4 asymmetric per-channel
 // centroids; the mapping figure after Figure 8 for pages -> blocks).
 //
-// Three launches per layer (staging rows are (b*Hkv + h) * tiles*64 + j, so
+// Three launches per layer (staging rows are (b*Hkv + h) * max N + j, so
 // they do not depend on the caller's centroid offsets):
-//   mean:     one workgroup per (tile of 64 blocks, b*Hkv + h).  16 lanes own a
-//             cache row (16 x head_dim/16 channels); 16 row-groups work on 16
-//             blocks at a time, streaming each page's 16 rows with 16
-//             independent wide loads.  Sums are fp64 (exact for bf16 keys), so
+//   mean:     one workgroup per (tile of 1024 tokens, b*Hkv + h), i.e. 64,
+//             32 or 16 blocks.  16 lanes own a cache row (16 x head_dim/16
+//             channels); 16 row-groups work on 16 blocks at a time,
+//             streaming each page's 16 rows with 16 independent wide loads.  Sums are fp64 (exact for bf16 keys), so
 //             the fp32 centroid is the correctly rounded mean.  Per-channel
 //             min/max of the tile is reduced with shuffles + LDS.
 //   range:    per (b, h, channel): min/max over tiles -> lo, scale (fp32).
@@ -26,7 +26,7 @@ namespace {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_centroid_mean(Geom g, float* __restrict__ staging,
                                                         float* __restrict__ pmin, float* __restrict__ pmax,
-                                                        int tiles) {
+                                                        int tiles, int stage_rows) {
     constexpr int VEC = D / kRowLanes;                    // channels per lane
     constexpr int NW = VEC * Elem<T>::kBytes / 4;         // 32-bit words per lane per row
     constexpr int GROUPS = 256 / kRowLanes;               // 16 blocks in flight
@@ -35,7 +35,8 @@ __global__ __launch_bounds__(256) void k_centroid_mean(Geom g, float* __restrict
     const int L = g.seq_lens[b];
     const int bs = block_size_of(g, h);
     const int N = ceil_div(L, bs);
-    const int j0 = blockIdx.x * kBuildTile;
+    const int bpt = kBuildTileTokens / bs;                // blocks per tile
+    const int j0 = blockIdx.x * bpt;
     if (j0 >= N) return;                                  // uniform: whole workgroup leaves
     const int lane = threadIdx.x & (kRowLanes - 1);
     const int grp = threadIdx.x / kRowLanes;
@@ -48,7 +49,7 @@ __global__ __launch_bounds__(256) void k_centroid_mean(Geom g, float* __restrict
         mx[e] = -__builtin_inff();
     }
 
-    for (int jj = grp; jj < kBuildTile; jj += GROUPS) {
+    for (int jj = grp; jj < bpt; jj += GROUPS) {
         const int j = j0 + jj;
         if (j >= N) break;
         const int t0 = j * bs;
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(256) void k_centroid_mean(Geom g, float* __restrict
             mn[e] = fminf(mn[e], c[e]);
             mx[e] = fmaxf(mx[e], c[e]);
         }
-        float* dst = staging + ((int64_t)bh * tiles * kBuildTile + j) * D + lane * VEC;
+        float* dst = staging + ((int64_t)bh * stage_rows + j) * D + lane * VEC;
 #pragma unroll
         for (int e = 0; e < VEC; e += 4)
             *reinterpret_cast<float4*>(dst + e) = make_float4(c[e], c[e + 1], c[e + 2], c[e + 3]);
@@ -118,8 +119,8 @@ __global__ __launch_bounds__(kRangeThreads) void k_centroid_range(Geom g, const 
     constexpr int S = kRangeThreads / D;
     const int bh = blockIdx.x;
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
-    const int N = ceil_div(g.seq_lens[b], block_size_of(g, h));
-    const int nt = ceil_div(N, kBuildTile);
+    const int bs = block_size_of(g, h);
+    const int nt = ceil_div(ceil_div(g.seq_lens[b], bs), kBuildTileTokens / bs);
     const int d = threadIdx.x % D, stripe = threadIdx.x / D;
     const float* pn = pmin + (int64_t)bh * tiles * D + d;
     const float* px = pmax + (int64_t)bh * tiles * D + d;
@@ -236,15 +237,17 @@ template <int D, int FMT>
 __global__ __launch_bounds__(256) void k_centroid_quantize(Geom g, const float* __restrict__ staging,
                                                            const float* __restrict__ scale,
                                                            const float* __restrict__ lo,
-                                                           uint8_t* __restrict__ codes, int tiles) {
+                                                           uint8_t* __restrict__ codes, int stage_rows) {
     constexpr int TPB = D / 8;                 // threads per block row
     constexpr int ROWS = 256 / TPB;            // block rows per pass
     constexpr int BITS = fmt_bits(FMT);
     constexpr int64_t RB = row_bytes(D, FMT);
     const int bh = blockIdx.y;
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
-    const int N = ceil_div(g.seq_lens[b], block_size_of(g, h));
-    const int j0 = blockIdx.x * kBuildTile;
+    const int bs = block_size_of(g, h);
+    const int N = ceil_div(g.seq_lens[b], bs);
+    const int bpt = kBuildTileTokens / bs;
+    const int j0 = blockIdx.x * bpt;
     if (j0 >= N) return;
     const int64_t row0 = g.off[bh];
     const int c8 = threadIdx.x % TPB;
@@ -254,10 +257,10 @@ __global__ __launch_bounds__(256) void k_centroid_quantize(Geom g, const float* 
         s[e] = scale[(int64_t)bh * D + c8 * 8 + e];
         z[e] = lo[(int64_t)bh * D + c8 * 8 + e];
     }
-    for (int jj = threadIdx.x / TPB; jj < kBuildTile; jj += ROWS) {
+    for (int jj = threadIdx.x / TPB; jj < bpt; jj += ROWS) {
         const int j = j0 + jj;
         if (j >= N) break;
-        const float* src = staging + ((int64_t)bh * tiles * kBuildTile + j) * D + c8 * 8;
+        const float* src = staging + ((int64_t)bh * stage_rows + j) * D + c8 * 8;
         const float4 u0 = reinterpret_cast<const float4*>(src)[0];
         const float4 u1 = reinterpret_cast<const float4*>(src)[1];
         const float c[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
@@ -285,12 +288,13 @@ __global__ __launch_bounds__(256) void k_centroid_quantize(Geom g, const float* 
 template <typename T, int D>
 hipError_t build_impl(const Geom& g, const BuildArgs& a, hipStream_t s) {
     const dim3 grid(a.tiles, g.B * g.Hkv);
-    hipLaunchKernelGGL((k_centroid_mean<T, D>), grid, dim3(256), 0, s, g, a.staging, a.pmin, a.pmax, a.tiles);
+    hipLaunchKernelGGL((k_centroid_mean<T, D>), grid, dim3(256), 0, s, g, a.staging, a.pmin, a.pmax, a.tiles,
+                       a.stage_rows);
     hipLaunchKernelGGL((k_centroid_range<D>), dim3(g.B * g.Hkv), dim3(kRangeThreads), 0, s, g, a.pmin, a.pmax,
                        a.tiles, a.fmt, a.scale, a.lo);
 #define ABS_QUANT(F_)                                                                                         \
     hipLaunchKernelGGL((k_centroid_quantize<D, F_>), grid, dim3(256), 0, s, g, a.staging, a.scale, a.lo, a.codes, \
-                       a.tiles)
+                       a.stage_rows)
     switch (a.fmt) {
         case kInt4Sym: ABS_QUANT(kInt4Sym); break;
         case kInt8: ABS_QUANT(kInt8); break;

@@ -37,18 +37,20 @@ enum CentFmt { kInt4 = 0, kInt4Sym = 1, kInt8 = 2, kInt4Tensor = 3, kBf16 = 4 };
 __host__ __device__ constexpr int fmt_bits(int fmt) { return fmt == kInt8 ? 8 : fmt == kBf16 ? 16 : 4; }
 __host__ __device__ constexpr int64_t row_bytes(int D, int fmt) { return (int64_t)D * fmt_bits(fmt) / 8; }
 
-// Centroid build: blocks per workgroup tile, and the tile count the host
-// derives from the largest N_{b,h}.
-constexpr int kBuildTile = 64;
+// Centroid build: a workgroup tile covers kBuildTileTokens tokens of one
+// (b, h), i.e. kBuildTileTokens / bs_h blocks (64 at block size 16), so every
+// tile holds the same number of keys whatever the head's block size.
+constexpr int kBuildTileTokens = 1024;
 
 struct BuildArgs {
     uint8_t* codes;
     float* scale;
     float* lo;
-    float* staging;   // [B*Hkv][tiles * kBuildTile][D] fp32 centroids
+    float* staging;   // [B*Hkv][stage_rows][D] fp32 centroids
     float* pmin;      // [B*Hkv][tiles][D]
     float* pmax;      // [B*Hkv][tiles][D]
-    int tiles;        // ceil(max N / kBuildTile)
+    int tiles;        // ceil(max L / kBuildTileTokens)
+    int stage_rows;   // largest N_{b,h}
     int fmt;          // CentFmt
 };
 
