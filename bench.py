@@ -2,7 +2,7 @@
 """Decode-step benchmark of the AB-Sparse library on one MI355X.
 
 One step = the whole decode hot path for one layer over one batch:
-abs_score_select (INT4 centroid scoring + top-K) then abs_sparse_decode
+abs_score_select (centroid scoring, INT4 by default, + top-K) then abs_sparse_decode
 (split attention over the selected pages, merged in the same launch), on
 inputs already resident in HBM.  The centroid build (prefill-time) is timed separately and reported
 under "build".
