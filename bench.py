@@ -16,6 +16,9 @@ Prints ONE JSON line (see the "metric" field).  Options:
     --steps K --warmup W   timed / untimed steps (default 200 / 20)
     --workload cfgN        0..4 (default 3: batch 4, 128K context, budget 4096)
     --replicas R           layer copies cycled through (default 8)
+    --layers N             instead of copies of one layer, N distinct layers
+                           of the workload (their own data and block maps),
+                           cycled through; each step is one layer
     --no-cpu-baseline      skip timing the CPU oracle
     --context N            override the workload's context length (tokens)
     --batch B              override the workload's batch (sequences)
@@ -77,6 +80,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="cfg3")
     ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--layers", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", type=int, default=0)
@@ -139,21 +143,33 @@ def main():
 
     base = A.PagedKV.from_host(Hq, x.k_cache, x.v_cache, x.page_table, x.seq_lens, x.block_size, x.dtype, dev)
     q = A.upload(x.q, dev, x.dtype)
-    R = max(1, args.replicas)
-    layers = [base]
-    for _ in range(R - 1):
-        layers.append(A.PagedKV(base.k_cache.clone(), base.v_cache.clone(), base.page_table, base.seq_lens,
-                                base.seq_lens_host, base.block_size, base.block_size_host, base.centroid_off,
-                                Hq, x.dtype))
+    R = max(1, args.layers or args.replicas)
+    layers, qs = [base], [q]
+    for r in range(1, R):
+        if args.layers:
+            xr = W.make_layer(w, r, block_sizes=None if args.block_map == "drawn"
+                              else [int(args.block_map)] * w.num_kv_heads)
+            layers.append(A.PagedKV.from_host(Hq, xr.k_cache, xr.v_cache, xr.page_table, xr.seq_lens, xr.block_size,
+                                              xr.dtype, dev))
+            qs.append(A.upload(xr.q, dev, xr.dtype))
+            del xr
+        else:
+            layers.append(A.PagedKV(base.k_cache.clone(), base.v_cache.clone(), base.page_table, base.seq_lens,
+                                    base.seq_lens_host, base.block_size, base.block_size_host, base.centroid_off,
+                                    Hq, x.dtype))
+            qs.append(q)
+    if args.layers:
+        print(f"[bench] {R} distinct layers generated and uploaded in {time.time() - t0:.1f}s", file=sys.stderr,
+              flush=True)
     fmt = args.centroid_format
     code_bits = {"int8": 8, "bf16": 16}.get(fmt, 4)
-    cents = [A.Centroids.empty(base, fmt) for _ in range(R)]
+    cents = [A.Centroids.empty(L, fmt) for L in layers]
     stream = torch.cuda.current_stream()
     sh = int(stream.cuda_stream)
-    ws_b = A.workspace(base.workspace_bytes(budget, A.ABS_OP_BUILD), dev)
-    ws_s = A.workspace(base.workspace_bytes(budget, A.ABS_OP_SELECT), dev)
-    ws_d = A.workspace(base.workspace_bytes(budget, A.ABS_OP_DECODE), dev)
-    cap = base.select_capacity(budget)
+    ws_b = A.workspace(max(L.workspace_bytes(budget, A.ABS_OP_BUILD) for L in layers), dev)
+    ws_s = A.workspace(max(L.workspace_bytes(budget, A.ABS_OP_SELECT) for L in layers), dev)
+    ws_d = A.workspace(max(L.workspace_bytes(budget, A.ABS_OP_DECODE) for L in layers), dev)
+    cap = max(L.select_capacity(budget) for L in layers)
     sel = torch.zeros((B, w.num_kv_heads, cap), dtype=torch.int32, device=dev)
     cnt = torch.zeros((B, w.num_kv_heads), dtype=torch.int32, device=dev)
     out = torch.empty((B, Hq, D), dtype=A.torch_dtype(x.dtype), device=dev)
@@ -174,13 +190,15 @@ def main():
     def select_call(i, st):
         r = i % R
         L = layers[r]
-        A.abs_score_select(L.kv, L.bmap, cents[r].desc, int(q.data_ptr()), budget, int(sel.data_ptr()), cap,
+        A.abs_score_select(L.kv, L.bmap, cents[r].desc, int(qs[r].data_ptr()), budget, int(sel.data_ptr()), cap,
                            int(cnt.data_ptr()), int(ws_s.data_ptr()), ws_s.numel(), st)
 
     def decode_call(i, st):
-        L = layers[i % R]
-        A.abs_sparse_decode(L.kv, L.bmap, int(q.data_ptr()), int(sel.data_ptr()), cap, int(cnt.data_ptr()), budget,
-                            sm, int(out.data_ptr()), int(lse.data_ptr()), int(ws_d.data_ptr()), ws_d.numel(), st)
+        r = i % R
+        L = layers[r]
+        A.abs_sparse_decode(L.kv, L.bmap, int(qs[r].data_ptr()), int(sel.data_ptr()), cap, int(cnt.data_ptr()),
+                            budget, sm, int(out.data_ptr()), int(lse.data_ptr()), int(ws_d.data_ptr()), ws_d.numel(),
+                            st)
 
     def step(i, st):
         select_call(i, st)
@@ -190,6 +208,7 @@ def main():
     # calls (one per layer copy), so host launch cost stays out of the timing
     for i in range(max(args.warmup, R)):
         step(i, sh)
+    step(0, sh)   # the diagnostic below reads layer 0's selection
     torch.cuda.synchronize()
     recall = needle_recall(x, sel.cpu().numpy(), cnt.cpu().numpy())
     if args.calibrate_copy > 0:
@@ -258,7 +277,9 @@ def main():
     upd_us = float(np.median([timed(g_upd, sreps) / (sreps * R) * 1e3 for _ in range(5)]))
 
     naive = None
-    if args.naive_per_size:
+    if args.naive_per_size and args.layers:
+        print("[bench] --naive-per-size uses copies of one layer; ignored with --layers", file=sys.stderr)
+    elif args.naive_per_size:
         naive = naive_per_size(A, torch, x, layers, q, budget, sm, fmt, R, capture, timed, sreps)
 
     ab = algorithmic_bytes(x, budget, lambda L, bs: min(L, max(1, budget // bs) * bs), code_bits)
@@ -289,7 +310,7 @@ def main():
         "config": {"workload": w.name, "batch": B, "context": int(w.context), "q_heads": Hq,
                    "kv_heads": w.num_kv_heads, "head_dim": D, "token_budget": budget, "page_size": 16,
                    "block_sizes": x.block_size.tolist(), "block_map": args.block_map, "centroid_format": fmt,
-                   "kv_replicas": R},
+                   "kv_replicas": None if args.layers else R, "layers": args.layers or 1},
         "roofline": {"bound": "hbm", "kernel": "k_sparse_decode (abs_sparse_decode: split, merge in the same launch)",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
