@@ -16,6 +16,7 @@
 #include <cstdio>
 #include <cstring>
 
+#include "decode_layout.hpp"
 #include "launch.hpp"
 
 namespace {
@@ -61,6 +62,9 @@ abs_status check_geometry(const abs_paged_kv* kv, const abs_block_map* map, Plan
                     kv->num_q_heads, kv->num_kv_heads);
     if (kv->num_kv_heads > absk::kMaxKvHeads)
         return fail(ABS_ERR_UNSUPPORTED, "num_kv_heads %d > %d", kv->num_kv_heads, absk::kMaxKvHeads);
+    if ((int64_t)kv->num_seqs * kv->num_kv_heads > 65536)   // (b, h) pairs index a grid dimension
+        return fail(ABS_ERR_UNSUPPORTED, "num_seqs * num_kv_heads = %lld > 65536",
+                    (long long)kv->num_seqs * kv->num_kv_heads);
     const int G = kv->num_q_heads / kv->num_kv_heads;
     if (G > 8) return fail(ABS_ERR_UNSUPPORTED, "query group size %d > 8", G);
     if (kv->head_dim != 64 && kv->head_dim != 128)
@@ -167,68 +171,8 @@ size_t select_bytes(const Plan& p) {
     return align_up((size_t)p.g.B * p.g.Hkv * score_stride(p) * sizeof(float));
 }
 
-struct DecodeLayout {
-    int ppw = 8, chunk = 8, splits = 1;
-    bool pipelined = false;
-    size_t arrive = 0, ml = 0, o = 0, bytes = 0;
-};
-
-// Build-time tuning of the decode launch (see decode_layout).
-#ifndef ABS_DECODE_TARGET_WGS
-#define ABS_DECODE_TARGET_WGS 1024
-#endif
-#ifndef ABS_DECODE_MAX_CHUNK
-#define ABS_DECODE_MAX_CHUNK 8
-#endif
-#ifndef ABS_DECODE_PIPE_WGS
-#define ABS_DECODE_PIPE_WGS 256
-#endif
-// At most this many splits per (b, h) outside the double-buffered layout:
-// the merging workgroup reads the splits' partials 8 at a time, so a
-// small layer does better with more pages per workgroup than with a long
-// merge.
-#ifndef ABS_DECODE_MAX_SPLITS
-#define ABS_DECODE_MAX_SPLITS 16
-#endif
-// 1: the last split workgroup of each (b, h) merges (one launch); 0: a merge launch.
-#ifndef ABS_DECODE_FUSED_MERGE
-#define ABS_DECODE_FUSED_MERGE 1
-#endif
-
-// Pages per workgroup: enough workgroups to fill the chip (about
-// ABS_DECODE_TARGET_WGS) but at most kMaxPagesPerWg pages each; pages are
-// held in registers `chunk` at a time.
-DecodeLayout decode_layout(const Plan& p) {
-    DecodeLayout l;
-    const int64_t heads = (int64_t)p.g.B * p.g.Hkv;
-    const int64_t maxp = std::max(p.max_pages_read, 1);
-    const int64_t ideal = std::max<int64_t>(1, ceil_div64(heads * maxp, ABS_DECODE_TARGET_WGS));
-    const int64_t cmax = ABS_DECODE_MAX_CHUNK;
-    l.chunk = (int)std::min<int64_t>(cmax, ideal >= 8 ? 8 : ideal >= 4 ? 4 : ideal >= 2 ? 2 : 1);
-    l.ppw = (int)std::min<int64_t>(absk::kMaxPagesPerWg, ceil_div64(ideal, l.chunk) * l.chunk);
-    l.splits = (int)ceil_div64(maxp, l.ppw);
-    if (l.splits > ABS_DECODE_MAX_SPLITS) {
-        const int64_t need = ceil_div64(maxp, ABS_DECODE_MAX_SPLITS);
-        l.chunk = (int)std::min<int64_t>(cmax, need >= 8 ? 8 : need >= 4 ? 4 : need >= 2 ? 2 : 1);
-        l.ppw = (int)std::min<int64_t>(absk::kMaxPagesPerWg, ceil_div64(need, l.chunk) * l.chunk);
-        l.splits = (int)ceil_div64(maxp, l.ppw);
-    }
-    // Enough pages for two chunks of 8 per workgroup at about
-    // ABS_DECODE_PIPE_WGS workgroups (two per compute unit): stream them
-    // double-buffered instead.
-    if (ABS_DECODE_PIPE_WGS > 0 && heads * maxp >= (int64_t)ABS_DECODE_PIPE_WGS * 16) {
-        const int64_t per = ceil_div64(heads * maxp, ABS_DECODE_PIPE_WGS);
-        l.chunk = 8;
-        l.pipelined = true;
-        l.ppw = (int)std::min<int64_t>(absk::kMaxPagesPerWg, std::max<int64_t>(16, ceil_div64(per, 16) * 16));
-        l.splits = (int)ceil_div64(maxp, l.ppw);
-    }
-    const size_t rows = (size_t)p.g.B * p.g.Hq * l.splits;
-    l.arrive = 0;
-    l.ml = align_up((size_t)p.g.B * p.g.Hkv * sizeof(int32_t));
-    l.o = l.ml + align_up(rows * 2 * sizeof(float));
-    l.bytes = l.o + align_up(rows * p.g.D * sizeof(float));
-    return l;
+absk::DecodeLayout decode_layout(const Plan& p) {
+    return absk::decode_layout(p.g.B, p.g.Hkv, p.g.Hq, p.g.D, p.max_pages_read);
 }
 
 abs_status check_centroids(const abs_centroids* c) {
@@ -443,7 +387,7 @@ abs_status abs_sparse_decode(const abs_paged_kv* kv, const abs_block_map* map, c
         return fail(ABS_ERR_INVALID_ARG, "null q, sel, sel_count or out");
     if (sel_cap < p.sel_cap) return fail(ABS_ERR_INVALID_ARG, "sel_cap %d < required %d", sel_cap, p.sel_cap);
     if (!std::isfinite(sm_scale)) return fail(ABS_ERR_INVALID_ARG, "sm_scale is not finite");
-    const DecodeLayout l = decode_layout(p);
+    const absk::DecodeLayout l = decode_layout(p);
     if (workspace == nullptr || workspace_bytes < l.bytes)
         return fail(ABS_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", l.bytes, workspace_bytes);
     absk::DecodeArgs a;

@@ -73,7 +73,8 @@ typedef enum abs_op {
  *       the current decode token included.  seq_lens_host: the same values on
  *       the host (launch sizes are computed from it; it must equal seq_lens).
  * Supported: page_size 16, head_dim 64 or 128, num_kv_heads <= 64,
- * num_q_heads / num_kv_heads in 1..8, 1 <= L_b <= max_pages_per_seq * 16.
+ * num_seqs * num_kv_heads <= 65536, num_q_heads / num_kv_heads in 1..8,
+ * 1 <= L_b <= max_pages_per_seq * 16.
  */
 typedef struct abs_paged_kv {
     int32_t num_seqs;

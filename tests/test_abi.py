@@ -225,6 +225,13 @@ def test_calibration_call_validation():
     assert status_of(lambda: A.abs_head_recall(h.kv, FAKE, FAKE, FAKE, 0)) == I
 
 
+def test_too_many_sequence_heads_is_unsupported():
+    h = Host(seq_lens=(16,) * 8193, block_size=(16,) * 8, Hq=8)
+    assert status_of(lambda: A.abs_total_blocks(h.kv, h.bmap)) == A.ABS_ERR_UNSUPPORTED
+    h = Host(seq_lens=(16,) * 8192, block_size=(16,) * 8, Hq=8)
+    assert A.abs_total_blocks(h.kv, h.bmap) == 8192 * 8
+
+
 def test_too_many_blocks_per_head_is_unsupported():
     h = Host(seq_lens=(65537 * 16,), block_size=(16,), Hq=1, max_pages=65537)
     cap = A.abs_select_capacity(h.kv, h.bmap, 64)
