@@ -96,3 +96,37 @@ def test_update_matches_oracle(oracle_mod, name, kw, lens, appended):
     ref_out, ref_lse = oracle_mod.attend(x.q, x.k_cache, x.v_cache, x.page_table, L, x.block_size, sel_h, cnt_h,
                                          sm, x.dtype)
     check_attention(out.float().cpu().numpy(), lse.cpu().numpy(), ref_out, ref_lse, x.dtype)
+
+
+@pytest.mark.parametrize("appended", [1, 17])
+def test_update_full_size_sampled(oracle_mod, appended):
+    """128K-token contexts, 4 sequences (the benchmark's workload): build at
+    L - appended, update to L; the oracle recomputes the first and the last
+    sequence on their own (bit-exact codes and clamp counts)."""
+    w = P[3]
+    x = W.make_layer(w, 0)
+    L = x.seq_lens.astype(np.int32)
+    L0 = (L - appended).astype(np.int32)
+    Hkv, D = x.k_cache.shape[1], x.k_cache.shape[3]
+    print(f"[gpu update] full size {w.name} appended={appended} bs={x.block_size.tolist()}", flush=True)
+    kv0 = A.PagedKV.from_host(x.q.shape[1], x.k_cache, x.v_cache, x.page_table, L0, x.block_size, x.dtype,
+                              capacity_tokens=int(L.max()))
+    cents = A.build_centroids(kv0, A.Centroids.empty(kv0))
+    oor = torch.full((len(L), Hkv), -1, dtype=torch.int32, device="cuda")
+    A.update_centroids(kv0.with_lengths(L), cents, appended, oor)
+    torch.cuda.synchronize()
+    off = kv0.centroid_off.cpu().numpy()
+    got = unpack_codes(cents.codes.cpu().numpy())
+    got_oor = oor.cpu().numpy()
+    for b in sorted({0, len(L) - 1}):
+        pt = x.page_table[b:b + 1]
+        c0 = oracle_mod.centroids(x.k_cache, pt, L0[b:b + 1], x.block_size, x.dtype)
+        qz0 = oracle_mod.quantize(c0, L0[b:b + 1], x.block_size)
+        off_b = off[b * Hkv:(b + 1) * Hkv + 1] - off[b * Hkv]
+        start = spread(qz0.codes, L0[b:b + 1], x.block_size, off_b, D)
+        want, want_oor = oracle_mod.update(x.k_cache, pt, L[b:b + 1], L0[b:b + 1], x.block_size, off_b,
+                                           oracle_mod.Quantized(start, qz0.scale, qz0.lo), x.dtype)
+        np.testing.assert_array_equal(got[off[b * Hkv]:off[(b + 1) * Hkv]], want)
+        np.testing.assert_array_equal(got_oor[b], want_oor[0])
+    del kv0, cents
+    torch.cuda.empty_cache()
