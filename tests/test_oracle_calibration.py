@@ -103,3 +103,22 @@ def test_planted_sensitivity_is_recovered(oracle_mod):
     assert norm[1, 1] > 0.97 and norm[2, 1] < 0.9
     assert (norm[1:, 2:] > 0.99).all()
     np.testing.assert_array_equal(oracle_mod.assign_block_sizes(R, 0.95), [16, 32, 64, 64])
+
+
+def test_recall_averages_the_whole_query_group(oracle_mod):
+    """One KV head, a group of 4 query heads: head 0's query is zero
+    (uniform attention: it keeps exactly kept/L = 64/256 of its mass), heads
+    1-3 point at one key hard enough that all their mass sits on it, and its
+    block is selected.  The head's recall is the group mean, (0.25 + 3)/4."""
+    w = W.PRESETS[0].scaled(batch=1, num_q_heads=4, num_kv_heads=1, head_dim=64, context=256, dtype="f32",
+                            token_budget=64, needles_per_head=0, fixed_block_sizes=(16,))
+    x = W.make_layer(w, needles=False)
+    keys = W.contiguous_kv(x, "k", 0)[0]
+    t_star = 77
+    k = keys[t_star].astype(np.float64)
+    x.q[0, 0, :] = 0.0
+    x.q[0, 1:, :] = (400.0 * k / np.linalg.norm(k)).astype(np.float32)
+    r = oracle_mod.head_recall(x, 16, 64, sm(64))
+    _, sel, cnt = _select(oracle_mod, x, 16, 64)
+    assert t_star // 16 in sel[0, 0, :cnt[0, 0]].tolist()
+    np.testing.assert_allclose(r, [(0.25 + 3.0) / 4.0], rtol=0, atol=1e-9)
