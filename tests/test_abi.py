@@ -244,3 +244,32 @@ def test_status_strings():
     assert A.abs_status_str(A.ABS_OK) == "ok"
     assert A.abs_status_str(A.ABS_ERR_WORKSPACE) == "workspace too small"
     assert A.abs_status_str(99) == "unknown status"
+
+
+def test_host_calls_from_plain_c(tmp_path):
+    """tests/c/host_calls.c links libabs.so from C and calls every host-side
+    function of abs.h; its results equal the binding's and the closed forms
+    (N = ceil(L / bs), K = min(N, max(1, budget // bs)))."""
+    exe = tmp_path / "host_calls"
+    lib_dir = os.path.dirname(A.LIB_PATH)
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "c", "host_calls.c"), "-L", lib_dir, "-labs",
+                    f"-Wl,-rpath,{lib_dir}", "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout
+    got = {l.split()[0]: l.split()[1:] for l in out.splitlines()}
+    lens, bs = [300, 77, 1], [16, 64]
+    n = [-(-L // b) for L in lens for b in bs]
+    assert int(got["total_blocks"][0]) == sum(n)
+    assert [int(v) for v in got["offsets"]] == [0] + np.cumsum(n).tolist()
+    ncap = [-(-512 // b) for _ in lens for b in bs]
+    assert [int(v) for v in got["offsets_capacity"]] == [0] + np.cumsum(ncap).tolist()
+    assert int(got["select_capacity"][0]) == max(min(-(-L // b), max(1, 100 // b)) for L in lens for b in bs)
+    h = Host(seq_lens=lens, block_size=bs, Hq=8, D=128)
+    assert [int(v) for v in got["workspace"]] == [A.abs_workspace_bytes(h.kv, h.bmap, 100, op) for op in range(3)]
+    assert [int(v) for v in got["row_bytes"]] == [64, 64, 128, 64, 256]
+    assert [int(v) for v in got["assign"]] == [32, 16, 64]
+    assert int(got["status_page_size"][0]) == A.ABS_ERR_UNSUPPORTED
+    assert int(got["status_block_size"][0]) == A.ABS_ERR_UNSUPPORTED
+    assert int(got["status_capacity"][0]) == A.ABS_ERR_INVALID_ARG
+    assert int(got["status_budget"][0]) == A.ABS_ERR_INVALID_ARG
+    assert got["last_error_nonempty"] == ["1"]
