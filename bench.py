@@ -59,7 +59,7 @@ METRIC = "sparse decode attn queries/s per layer at 32K/128K ctx; achieved HBM G
 # a hash of the kernel sources they were taken with; any other source
 # reports null.
 TRAFFIC = {
-    ("llama8b-128k-b4-bf16", 131072, "drawn", "378046e3d43281f5"): 68929662,
+    ("llama8b-128k-b4-bf16", 131072, "drawn", "8db91bef208b41e2"): 68857665,
 }
 KERNEL_SOURCES = ("decode.hip", "device.hpp", "launch.hpp", "decode_layout.hpp")   # kernel + its launch layout
 
@@ -311,7 +311,7 @@ def main():
                    "kv_heads": w.num_kv_heads, "head_dim": D, "token_budget": budget, "page_size": 16,
                    "block_sizes": x.block_size.tolist(), "block_map": args.block_map, "centroid_format": fmt,
                    "kv_replicas": None if args.layers else R, "layers": args.layers or 1},
-        "roofline": {"bound": "hbm", "kernel": "k_sparse_decode (abs_sparse_decode: split, merge in the same launch)",
+        "roofline": {"bound": "hbm", "kernel": "k_sparse_decode_ws (abs_sparse_decode: split, merge in the same launch)",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes": ab["decode"], "avg_us": round(dec_avg, 3),

@@ -14,6 +14,10 @@
 //         chunk); otherwise it is reduced over the 16 lanes of a DPP row.
 //         Logits are kept in log2 units (q pre-scaled by sm_scale*log2 e).
 //         The workgroup's (m, l, o[D]) per query head is its partial.
+//         bf16 layers with D = 128 and groups of up to 4 heads use the
+//         wavefront-split form instead (k_sparse_decode_ws): each wavefront
+//         streams its own pages with its own softmax state, and the four
+//         states meet only at the end.
 // merge:  M = max m_s, l = sum 2^(m_s-M) l_s, out = sum 2^(m_s-M) o_s / l,
 //         lse = (M + log2 l) * ln 2.  Done in the split launch by the last
 //         workgroup to finish each (b, h): partials are written with
@@ -59,6 +63,15 @@ constexpr bool kPipeFits = sizeof(T) == 2 && (D == 64 || GT <= 4);
 // Build-time switch: 0 keeps q.k on the vector ALUs for bf16 as well.
 #ifndef ABS_DECODE_MATRIX
 #define ABS_DECODE_MATRIX 1
+#endif
+// 1: bf16 layers with D = 128 and up to 4 query heads per KV head use the
+// wavefront-split kernel for 8-page and double-buffered layouts.
+#ifndef ABS_DECODE_WAVES
+#define ABS_DECODE_WAVES 1
+#endif
+// Page buffers per wavefront in the wavefront-split kernel.
+#ifndef ABS_DECODE_WS_DEPTH
+#define ABS_DECODE_WS_DEPTH 1
 #endif
 // Row groups of the double-buffered matrix-core kernel (1 or 2).
 #ifndef ABS_DECODE_ROWGROUPS
@@ -463,6 +476,277 @@ __global__ __launch_bounds__(256 * RG, (DecodeOccupancy<T, D, GT, PIPE, MF>::val
     }
 }
 
+// WS: the wavefront-split form of the split kernel (bf16, D = 128, q.k on
+// the matrix cores).  Wavefront w owns pages w, w + 4, w + 8, ... of the
+// workgroup's range and keeps its own running (m, l, o) over them: the MFMA
+// gives every lane S[head][token lane%16] of a page, the page's max and sum
+// per head are DPP reductions over a 16-lane row (the four rows hold the
+// same values), and P.V runs with each lane owning 2 of the 128 channels for
+// all G heads, the 16 tokens' probabilities broadcast with readlane.  Four
+// pages per wavefront are in flight (two for groups of 8).  No LDS and no barrier until the four
+// wavefronts' states are combined at the end.
+template <int GT>
+__global__ __launch_bounds__(256, 2) void k_sparse_decode_ws(Geom g, const uint16_t* __restrict__ q,
+                                                             const int32_t* __restrict__ sel, int sel_cap,
+                                                             const int32_t* __restrict__ count, float qscale,
+                                                             float* __restrict__ part_ml, float* __restrict__ part_o,
+                                                             int splits, int ppw, int32_t* __restrict__ arrive,
+                                                             uint16_t* __restrict__ out, float* __restrict__ lse) {
+    using T = uint16_t;
+    constexpr int D = 128;
+    constexpr int KSTEPS = D / 32;
+    constexpr int GP = (GT + 3) / 4;
+    constexpr int DEPTH = ABS_DECODE_WS_DEPTH;           // page buffers per wavefront
+    constexpr float NEG = -__builtin_inff();
+    const int split = blockIdx.x;
+    const int bh = blockIdx.y;
+    const int b = bh / g.Hkv, h = bh - b * g.Hkv;
+    const int wave = threadIdx.x / 64;
+    const int wl = threadIdx.x & 63;
+
+    const int spb = block_size_of(g, h) / kPage;      // pages per block (stride): 1, 2 or 4
+    const int sh = __builtin_ctz(spb);
+    const int p0 = split * ppw;                        // ppw <= 64
+    const int gp = p0 + wl;
+    const bool in_row = wl < ppw && gp < sel_cap * spb;
+    const int sv = sel[(int64_t)bh * sel_cap + min(gp >> sh, sel_cap - 1)];   // unconditional, clamped
+    const int L = g.seq_lens[b];
+    const int npages = ceil_div(L, kPage);
+    const int N = ceil_div(L, spb * kPage);
+    const int K = min(max(count[bh], 0), sel_cap);
+    const int total = min(K * spb, splits * ppw);      // selected pages of (b, h)
+    int ph = -1, lp = 0;
+    if (in_row) {
+        lp = min(max(sv, 0), N - 1) * spb + (gp & (spb - 1));
+        if (lp < npages) {
+            const int pg = g.page_table[(int64_t)b * g.max_pages + lp];
+            if (pg >= 0 && pg < g.num_pages) ph = pg;
+        }
+    }
+    if (gp >= total) ph = -1;
+
+    Words<4> qa[GP][KSTEPS];
+    {
+        const int m4 = (wl & 15) & 3;
+#pragma unroll
+        for (int pp = 0; pp < GP; ++pp) {
+            const int head = h * g.G + min(4 * pp + m4, g.G - 1);
+#pragma unroll
+            for (int st = 0; st < KSTEPS; ++st)
+                qa[pp][st] = load_words<4>(q + ((int64_t)b * g.Hq + head) * D + st * 32 + (wl >> 4) * 8);
+        }
+    }
+
+    __shared__ float s_red[4][GT];
+    __shared__ __align__(16) float s_o[4][GT][D];
+    __shared__ float s_l[4][GT];
+
+    // this wavefront's running state; m and l are the same in every lane
+    float m[GT], l[GT], o[GT][2];
+#pragma unroll
+    for (int gg = 0; gg < GT; ++gg) {
+        m[gg] = NEG;
+        l[gg] = 0.0f;
+        o[gg][0] = o[gg][1] = 0.0f;
+    }
+    const bool active = __builtin_amdgcn_readfirstlane(ph) >= 0;
+    if (active) {
+        const T* kc = reinterpret_cast<const T*>(g.k);
+        const T* vc = reinterpret_cast<const T*>(g.v);
+        const uint32_t k_off = (uint32_t)(((wl & 15) * D + (wl >> 4) * 8) * sizeof(T));
+        const uint32_t v_off = (uint32_t)(2 * wl * sizeof(T));
+        const int nvalid = min(max(total - p0, 0), ppw);             // pages of this workgroup
+        const int npw = nvalid > wave ? (nvalid - wave + 3) / 4 : 0;   // ... of this wavefront
+        auto issue = [&](int c, Words<4>(&kw)[KSTEPS], Words<1>(&vw)[kPage]) {
+            const int pg = __builtin_amdgcn_readlane(ph, c);
+            const int64_t base = ((int64_t)(pg >= 0 ? pg : 0) * g.Hkv + h) * (kPage * D);
+#pragma unroll
+            for (int st = 0; st < KSTEPS; ++st) kw[st] = load_words_at<4>(kc + base + st * 32, k_off);
+#pragma unroll
+            for (int t = 0; t < kPage; ++t) vw[t] = load_words_at<1>(vc + base + t * D, v_off);
+        };
+        auto consume = [&](int c, const Words<4>(&kw)[KSTEPS], const Words<1>(&vw)[kPage]) {
+            const int pg = __builtin_amdgcn_readlane(ph, c);
+            const int t0 = __builtin_amdgcn_readlane(lp, c) * kPage;
+            const bool valid = pg >= 0 && t0 + (wl & 15) < L;
+            float sc[GT];
+#pragma unroll
+            for (int pp = 0; pp < GP; ++pp) {
+                f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int st = 0; st < KSTEPS; ++st)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[pp][st]),
+                                                                  __builtin_bit_cast(bf16x8_t, kw[st]), acc, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (4 * pp + i < GT) sc[4 * pp + i] = valid ? acc[i] * qscale : NEG;
+            }
+            float p[GT];
+#pragma unroll
+            for (int gg = 0; gg < GT; ++gg) {
+                const float mn = fmaxf(m[gg], row16_max(sc[gg]));
+                const float ms = mn == NEG ? 0.0f : mn;       // no valid token yet: exponents give 0
+                const float alpha = exp2_approx(m[gg] - ms);
+                p[gg] = exp2_approx(sc[gg] - ms);
+                l[gg] = l[gg] * alpha + row16_sum(p[gg]);
+                o[gg][0] *= alpha;
+                o[gg][1] *= alpha;
+                m[gg] = mn;
+            }
+#pragma unroll
+            for (int t = 0; t < kPage; ++t) {
+                const float v0 = bf16_lo(vw[t].w[0]), v1 = bf16_hi(vw[t].w[0]);
+#pragma unroll
+                for (int gg = 0; gg < GT; ++gg) {
+                    const float pt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p[gg]), t));
+                    o[gg][0] = fmaf(pt, v0, o[gg][0]);
+                    o[gg][1] = fmaf(pt, v1, o[gg][1]);
+                }
+            }
+        };
+        Words<4> kb[DEPTH][KSTEPS];
+        Words<1> vb[DEPTH][kPage];
+#pragma unroll
+        for (int k = 0; k < DEPTH; ++k)
+            if (k < npw) issue(wave + 4 * k, kb[k], vb[k]);
+        for (int i0 = 0; i0 < npw; i0 += DEPTH) {
+#pragma unroll
+            for (int k = 0; k < DEPTH; ++k) {
+                const int i = i0 + k;
+                if (i < npw) {
+                    consume(wave + 4 * i, kb[k], vb[k]);
+                    if (i + DEPTH < npw) issue(wave + 4 * (i + DEPTH), kb[k], vb[k]);
+                }
+            }
+        }
+
+        // wavefronts -> workgroup: the common max, then each wavefront's
+        // rescaled state to LDS; every thread then sums two channels over
+        // the four wavefronts
+        if (wl == 0) {
+#pragma unroll
+            for (int gg = 0; gg < GT; ++gg) s_red[wave][gg] = m[gg];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int gg = 0; gg < GT; ++gg) {
+            float M = s_red[0][gg];
+#pragma unroll
+            for (int w = 1; w < 4; ++w) M = fmaxf(M, s_red[w][gg]);
+            const float f = m[gg] == NEG ? 0.0f : exp2_approx(m[gg] - M);
+            *reinterpret_cast<float2*>(&s_o[wave][gg][2 * wl]) = make_float2(o[gg][0] * f, o[gg][1] * f);
+            if (wl == 0) s_l[wave][gg] = l[gg] * f;
+        }
+        __syncthreads();
+    }
+
+    // This workgroup's share of (b, h), per (query head, channel pair): the
+    // wavefront sums from LDS, or an empty partial (m = -inf) when the workgroup is
+    // in the selected range but all of its pages are empty.
+    const bool fused = arrive != nullptr;
+    const bool holds = p0 < total;                      // active implies holds
+    const int nact = ceil_div(total, ppw);              // workgroups holding pages of (b, h)
+    if (holds) {
+        for (int idx = 2 * (int)threadIdx.x; idx < GT * D; idx += 2 * (int)blockDim.x) {
+            const int gg = idx / D, d = idx - gg * D;
+            if (gg >= g.G) continue;
+            float2 acc = make_float2(0.0f, 0.0f);
+            float mg = NEG, ls = 0.0f;
+            if (active) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float2 v = *reinterpret_cast<const float2*>(&s_o[r][gg][d]);
+                    acc.x += v.x;
+                    acc.y += v.y;
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ls += s_l[r][gg];
+                mg = s_red[0][gg];
+#pragma unroll
+                for (int w = 1; w < 4; ++w) mg = fmaxf(mg, s_red[w][gg]);
+            }
+            const int64_t bi = (int64_t)b * g.Hq + h * g.G + gg;
+            const int64_t prow = bi * splits + split;
+            if (fused && nact == 1) {
+                write_output(out, lse, bi, d, acc, mg, ls, D);        // the only workgroup of (b, h)
+            } else if (fused) {
+                store2_agent(part_o + prow * D + d, acc.x, acc.y);
+                if (d == 0) store2_agent(part_ml + prow * 2, mg, ls);
+            } else {
+                *reinterpret_cast<float2*>(part_o + prow * D + d) = acc;
+                if (d == 0) {
+                    part_ml[prow * 2 + 0] = mg;
+                    part_ml[prow * 2 + 1] = ls;
+                }
+            }
+        }
+    } else if (fused && total == 0 && split == 0) {
+        // nothing selected for (b, h): zero output, lse = -inf
+        for (int idx = 2 * (int)threadIdx.x; idx < GT * D; idx += 2 * (int)blockDim.x) {
+            const int gg = idx / D, d = idx - gg * D;
+            if (gg < g.G)
+                write_output(out, lse, (int64_t)b * g.Hq + h * g.G + gg, d, make_float2(0.0f, 0.0f), NEG, 0.0f, D);
+        }
+    }
+    if (!fused || !holds || nact == 1) return;
+
+    // Hand-off: partials are written with agent-scope (L2 write-through)
+    // stores; once every thread's stores have completed, one agent-scope
+    // atomic counts the arrival.  The last of the nact workgroups resets the
+    // counter for the next call and merges, reading with agent-scope loads.
+    __shared__ int s_last;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int prev = __hip_atomic_fetch_add(arrive + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = prev == nact - 1;
+        if (prev == nact - 1) __hip_atomic_store(arrive + bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    constexpr int MB = ABS_DECODE_MERGE_BATCH;   // partials per merge pass
+    for (int idx = 2 * (int)threadIdx.x; idx < GT * D; idx += 2 * (int)blockDim.x) {
+        const int gg = idx / D, d = idx - gg * D;
+        if (gg >= g.G) continue;
+        const int64_t bi = (int64_t)b * g.Hq + h * g.G + gg;
+        const float* ml = part_ml + bi * splits * 2;
+        const float* po = part_o + bi * splits * D + d;
+        float mg = NEG, ls = 0.0f;
+        float2 acc = make_float2(0.0f, 0.0f);
+        for (int s0 = 0; s0 < nact; s0 += MB) {
+            // 2 MB loads in flight (indices clamped, so no load waits on a
+            // branch), then one max and one weighted sum over the MB splits
+            float2 mlv[MB], ov[MB];
+#pragma unroll
+            for (int k = 0; k < MB; ++k) {
+                const int sk = min(s0 + k, nact - 1);
+                mlv[k] = load2_agent(ml + 2 * sk);
+                ov[k] = load2_agent(po + (int64_t)sk * D);
+            }
+            float bm = NEG;
+#pragma unroll
+            for (int k = 0; k < MB; ++k)
+                if (s0 + k < nact) bm = fmaxf(bm, mlv[k].x);
+            const float mn = fmaxf(mg, bm);
+            if (mn == NEG) continue;                      // only empty partials so far
+            const float a = mg == NEG ? 0.0f : exp2f(mg - mn);
+            ls *= a;
+            acc.x *= a;
+            acc.y *= a;
+#pragma unroll
+            for (int k = 0; k < MB; ++k) {
+                const float w = s0 + k < nact ? exp2f(mlv[k].x - mn) : 0.0f;   // empty partial: m = -inf, w = 0
+                ls = fmaf(mlv[k].y, w, ls);
+                acc.x = fmaf(ov[k].x, w, acc.x);
+                acc.y = fmaf(ov[k].y, w, acc.y);
+            }
+            mg = mn;
+        }
+        write_output(out, lse, bi, d, acc, mg, ls, D);
+    }
+}
+
 // One workgroup per (b, query head): merge the partials of the splits that
 // held pages of (b, h).  Thread (group sg, channel d) folds splits sg,
 // sg + NG, ... with an online max/sum (its loads are independent, so they are
@@ -543,7 +827,15 @@ hipError_t decode_gt(const Geom& g, const DecodeArgs& a, hipStream_t s) {
     // (a pipelined plan on a variant that does not fit runs the plain 8-page loop)
     // (fp32 rows of 8 query heads at D = 128 hold at most 4 pages at once)
     constexpr bool kWide = sizeof(T) == 4 && D * GT >= 1024;
-    if (a.pipelined && kPipeFits<T, D, GT>) {
+    // bf16, D = 128, up to 4 query heads per group: the wavefront-split kernel
+    // (at 8 heads its per-lane state outgrows the plain matrix-core kernel's)
+    constexpr bool kWaveSplit = kMatrix && D == 128 && GT <= 4;
+    if (ABS_DECODE_WAVES && kWaveSplit && (a.pipelined || a.chunk == 8)) {
+        if constexpr (kWaveSplit)
+            hipLaunchKernelGGL((k_sparse_decode_ws<GT>), grid, dim3(256), 0, s, g,
+                               reinterpret_cast<const uint16_t*>(a.q), a.sel, a.sel_cap, a.count, qscale, a.part_ml,
+                               a.part_o, a.splits, a.pages_per_wg, a.arrive, reinterpret_cast<uint16_t*>(a.out), a.lse);
+    } else if (a.pipelined && kPipeFits<T, D, GT>) {
         if constexpr (kPipeFits<T, D, GT>) launch_split<T, D, GT, 8, true, kMatrix, kRowGroups>(grid, g, a, qscale, s);
     } else if ((a.chunk == 8 || a.pipelined) && !kWide) {
         if constexpr (!kWide) launch_split<T, D, GT, 8, false, kMatrix, 1>(grid, g, a, qscale, s);
