@@ -69,7 +69,7 @@ constexpr bool kPipeFits = sizeof(T) == 2 && (D == 64 || GT <= 4);
 #ifndef ABS_DECODE_WAVES
 #define ABS_DECODE_WAVES 1
 #endif
-// Page buffers per wavefront in the wavefront-split kernel.
+// Page buffers per wavefront in the wavefront-split kernel (1 measured best).
 #ifndef ABS_DECODE_WS_DEPTH
 #define ABS_DECODE_WS_DEPTH 1
 #endif
@@ -482,9 +482,11 @@ __global__ __launch_bounds__(256 * RG, (DecodeOccupancy<T, D, GT, PIPE, MF>::val
 // gives every lane S[head][token lane%16] of a page, the page's max and sum
 // per head are DPP reductions over a 16-lane row (the four rows hold the
 // same values), and P.V runs with each lane owning 2 of the 128 channels for
-// all G heads, the 16 tokens' probabilities broadcast with readlane.  Four
-// pages per wavefront are in flight (two for groups of 8).  No LDS and no barrier until the four
-// wavefronts' states are combined at the end.
+// all G heads, the 16 tokens' probabilities broadcast with readlane.  One
+// page buffer per wavefront (ABS_DECODE_WS_DEPTH): the compiler issues the
+// next page's loads while the current page is folded, and more buffers
+// measured slower.  No LDS and no barrier until the four wavefronts' states
+// are combined at the end.
 template <int GT>
 __global__ __launch_bounds__(256, 2) void k_sparse_decode_ws(Geom g, const uint16_t* __restrict__ q,
                                                              const int32_t* __restrict__ sel, int sel_cap,
