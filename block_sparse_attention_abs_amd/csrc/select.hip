@@ -14,8 +14,9 @@
 //         of codes each (head_dim/32 lanes for INT4, head_dim/16 for INT8,
 //         head_dim/8 for bf16 centroids, whose w_d is qbar_d and c0 = 0),
 //         so one load instruction reads a contiguous 1 KiB run per
-//         wavefront; all of a lane's code loads are issued before the
-//         workgroup's query prologue.
+//         wavefront.  Every load is unconditional (offsets clamped), the
+//         query, scale and lo first, then all of a lane's code rows, so
+//         the fold waits only for the former.
 // top-K:  one workgroup per (b, h); thread t owns block indices
 //         [t*KPT, (t+1)*KPT) as order-preserving 32-bit keys in registers.
 //         1. min/max of the scores; a 2048-bin histogram of the scores'
@@ -55,43 +56,56 @@ __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restr
     constexpr int RPL = kScoreBlocksPerWg / GPW;   // block rows per lane group
     constexpr int RB = D * BITS / 8;          // bytes per row
     constexpr int PER = 32 / BITS;            // channels per 32-bit word
+    static_assert(NT >= D, "one thread per channel folds the query");
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
+    const int64_t row0 = g.off[bh];
     const int N = ceil_div(g.seq_lens[b], block_size_of(g, h));
     const int j0 = tile * kScoreBlocksPerWg;
-    if (j0 >= N) return;
-    const int64_t row0 = g.off[bh];
     const int sub = threadIdx.x % LPB;
     const int grp = threadIdx.x / LPB;
 
-    // RPL block rows per lane group, GPW consecutive rows per step (contiguous runs)
+    // Every load below is unconditional (offsets clamped), so all of them are
+    // in flight together and none waits on a branch; the query group, scale
+    // and lo go first, so that the fold below waits only for them.  A tile
+    // past the end of a shorter sequence (j0 >= N, in the per-sequence grid)
+    // runs through and stores nothing.
+    const int dch = min((int)threadIdx.x, D - 1);    // this thread's channel (threads < D)
+    float qv[GT], sc = 0.0f, zp = 0.0f;
+#pragma unroll
+    for (int gg = 0; gg < GT; ++gg)
+        qv[gg] = Elem<T>::load1(q + ((int64_t)b * g.Hq + h * g.G + min(gg, g.G - 1)) * D + dch);
+    if constexpr (BITS != 16) {
+        sc = scale[(int64_t)bh * D + dch];
+        zp = lo[(int64_t)bh * D + dch];
+    }
+    // RPL block rows per lane group, GPW consecutive rows per step (contiguous
+    // runs); a row at or beyond N reads row N - 1 again (N >= 1) and is not
+    // stored
     uint4 v[RPL];
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
-        const int j = j0 + r * GPW + grp;
-        v[r] = make_uint4(0u, 0u, 0u, 0u);
-        if (j < N) v[r] = *reinterpret_cast<const uint4*>(codes + (row0 + j) * RB + sub * 16);
+        const int j = min(j0 + r * GPW + grp, N - 1);
+        v[r] = *reinterpret_cast<const uint4*>(codes + (row0 + j) * RB + sub * 16);
     }
 
     // per channel: w_d = qbar_d * scale_d and z_d = qbar_d * lo_d (fp64, LDS);
-    // bf16 centroids are values already: w_d = qbar_d, z_d = 0
-    __shared__ double w[D], z[D];
-    if (threadIdx.x < D) {
-        const int d = threadIdx.x;
-        float qv[GT];
-#pragma unroll
-        for (int gg = 0; gg < GT; ++gg)
-            qv[gg] = Elem<T>::load1(q + ((int64_t)b * g.Hq + h * g.G + min(gg, g.G - 1)) * D + d);
+    // bf16 centroids are values already: w_d = qbar_d, z_d = 0.  Every thread
+    // writes its slot (those past D are never read), so no branch holds the
+    // loads above back.
+    __shared__ double w[NT], z[NT];
+    {
+        // the group's G heads count, the padding slots (G < GT) add +0; the
+        // mask is opaque to the optimizer, which would otherwise move a
+        // padding slot's load into a branch behind the code loads
         double qbar = 0.0;
 #pragma unroll
-        for (int gg = 0; gg < GT; ++gg) qbar += gg < g.G ? (double)qv[gg] : 0.0;
-        if constexpr (BITS == 16) {
-            w[d] = qbar;
-            z[d] = 0.0;
-        } else {
-            const float sc = scale[(int64_t)bh * D + d], zp = lo[(int64_t)bh * D + d];
-            w[d] = qbar * (double)sc;
-            z[d] = qbar * (double)zp;
+        for (int gg = 0; gg < GT; ++gg) {
+            uint32_t keep = gg < g.G ? ~0u : 0u;
+            asm volatile("" : "+v"(keep));
+            qbar += (double)__uint_as_float(__float_as_uint(qv[gg]) & keep);
         }
+        w[threadIdx.x] = BITS == 16 ? qbar : qbar * (double)sc;
+        z[threadIdx.x] = BITS == 16 ? 0.0 : qbar * (double)zp;
     }
     __syncthreads();
 
@@ -196,6 +210,29 @@ __global__ __launch_bounds__(NT) void k_topk(Geom g, const float* __restrict__ s
                                              int32_t* __restrict__ sel, int sel_cap, int32_t* __restrict__ count) {
     const int bh = blockIdx.x;
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
+
+    // Thread t owns indices [t*KPT, t*KPT + nv).  Its scores are loaded before
+    // the row length is known (that takes a read of seq_lens), so the two
+    // reads overlap.  The loads are unconditional, their offsets clamped into
+    // the row's stride (a multiple of 4 that is at least N): a clamped slot is
+    // at or beyond N and never used.
+    const int base = threadIdx.x * KPT;
+    const float* row = scores + (int64_t)bh * stride;
+    float f[KPT];
+    if constexpr (KPT % 4 == 0) {
+#pragma unroll
+        for (int e = 0; e < KPT; e += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(row + min(base + e, stride - 4));
+            f[e] = v.x;
+            f[e + 1] = v.y;
+            f[e + 2] = v.z;
+            f[e + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) f[e] = row[min(base + e, stride - 1)];
+    }
+
     const int bs = block_size_of(g, h);
     const int N = ceil_div(g.seq_lens[b], bs);
     const int K = min(N, max(1, budget / bs));
@@ -205,32 +242,10 @@ __global__ __launch_bounds__(NT) void k_topk(Geom g, const float* __restrict__ s
         for (int j = threadIdx.x; j < N; j += NT) out[j] = j;
         return;
     }
-
-    // Thread t owns indices [t*KPT, t*KPT + nv); most threads are full (nv =
-    // KPT) and run the unguarded forms of the loops below.
-    const int base = threadIdx.x * KPT;
+    // most threads are full (nv = KPT) and run the unguarded forms of the
+    // loops below
     const int nv = min(max(N - base, 0), KPT);
     const bool full = nv == KPT;
-    const float* row = scores + (int64_t)bh * stride;
-    float f[KPT];
-    if (full) {
-        if constexpr (KPT % 4 == 0) {
-#pragma unroll
-            for (int e = 0; e < KPT; e += 4) {
-                const float4 v = *reinterpret_cast<const float4*>(row + base + e);
-                f[e] = v.x;
-                f[e + 1] = v.y;
-                f[e + 2] = v.z;
-                f[e + 3] = v.w;
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < KPT; ++e) f[e] = row[base + e];
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < KPT; ++e) f[e] = e < nv ? row[base + e] : 0.0f;
-    }
     float mn = __builtin_inff(), mx = -__builtin_inff();
     if (full) {
 #pragma unroll
