@@ -354,6 +354,7 @@ abs_status abs_score_select(const abs_paged_kv* kv, const abs_block_map* map, co
     a.sel_cap = sel_cap;
     a.budget = token_budget;
     a.max_n = p.max_n;
+    a.max_len = p.max_len;
     // the exact list of score tiles, when it fits the kernel arguments
     uint32_t tiles[absk::kMaxScoreTiles];
     a.ntiles = 0;

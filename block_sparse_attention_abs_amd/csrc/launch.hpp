@@ -101,6 +101,7 @@ struct SelectArgs {
     int sel_cap;
     int budget;
     int max_n;        // largest N_{b,h}
+    int max_len;      // largest L_b
     int ntiles;       // score tiles over all heads
     const uint32_t* tiles_host;   // their list (host, valid during the call) or null
     HeadTiles head_tiles;         // per-head cumulative tiles for the longest sequence

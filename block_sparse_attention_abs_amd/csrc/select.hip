@@ -206,23 +206,26 @@ constexpr int kBins = 2048;
 constexpr int kCandCap = 512;
 
 template <int NT, int KPT>
-__global__ __launch_bounds__(NT) void k_topk(Geom g, const float* __restrict__ scores, int stride, int budget,
-                                             int32_t* __restrict__ sel, int sel_cap, int32_t* __restrict__ count) {
+__global__ __launch_bounds__(NT) void k_topk(Geom g, const float* __restrict__ scores, int stride, int max_len,
+                                             int budget, int32_t* __restrict__ sel, int sel_cap,
+                                             int32_t* __restrict__ count) {
     const int bh = blockIdx.x;
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
+    const int bs = block_size_of(g, h);
 
     // Thread t owns indices [t*KPT, t*KPT + nv).  Its scores are loaded before
     // the row length is known (that takes a read of seq_lens), so the two
-    // reads overlap.  The loads are unconditional, their offsets clamped into
-    // the row's stride (a multiple of 4 that is at least N): a clamped slot is
-    // at or beyond N and never used.
+    // reads overlap.  The loads are unconditional, their offsets clamped to
+    // the head's longest row, rounded up to a multiple of 4 (cap: at least N,
+    // at most the stride): a clamped slot is at or beyond N and never used.
     const int base = threadIdx.x * KPT;
     const float* row = scores + (int64_t)bh * stride;
+    const int cap = min(stride, (ceil_div(max_len, bs) + 3) & ~3);
     float f[KPT];
     if constexpr (KPT % 4 == 0) {
 #pragma unroll
         for (int e = 0; e < KPT; e += 4) {
-            const float4 v = *reinterpret_cast<const float4*>(row + min(base + e, stride - 4));
+            const float4 v = *reinterpret_cast<const float4*>(row + min(base + e, cap - 4));
             f[e] = v.x;
             f[e + 1] = v.y;
             f[e + 2] = v.z;
@@ -230,10 +233,9 @@ __global__ __launch_bounds__(NT) void k_topk(Geom g, const float* __restrict__ s
         }
     } else {
 #pragma unroll
-        for (int e = 0; e < KPT; ++e) f[e] = row[min(base + e, stride - 1)];
+        for (int e = 0; e < KPT; ++e) f[e] = row[min(base + e, cap - 1)];
     }
 
-    const int bs = block_size_of(g, h);
     const int N = ceil_div(g.seq_lens[b], bs);
     const int K = min(N, max(1, budget / bs));
     int32_t* out = sel + (int64_t)bh * sel_cap;
@@ -486,8 +488,8 @@ hipError_t select_impl(const Geom& g, const SelectArgs& a, hipStream_t s) {
     else launch_score<T, D, 4>(g, a, s);
     const dim3 tgrid(g.B * g.Hkv);
 #define ABS_TOPK(NT_, KPT_)                                                                                  \
-    hipLaunchKernelGGL((k_topk<NT_, KPT_>), tgrid, dim3(NT_), 0, s, g, a.scores, a.stride, a.budget, a.sel, \
-                       a.sel_cap, a.count)
+    hipLaunchKernelGGL((k_topk<NT_, KPT_>), tgrid, dim3(NT_), 0, s, g, a.scores, a.stride, a.max_len, a.budget, \
+                       a.sel, a.sel_cap, a.count)
     // ABS_TOPK_NT threads, each holding up to 32 keys; 1024 x 64 beyond that
     constexpr int NT = ABS_TOPK_NT;
     const int n = a.max_n;
