@@ -7,9 +7,12 @@
 //   mean:     one workgroup per (tile of 1024 tokens, b*Hkv + h), i.e. 64,
 //             32 or 16 blocks.  16 lanes own a cache row (16 x head_dim/16
 //             channels); 16 row-groups work on 16 blocks at a time,
-//             streaming each page's 16 rows with 16 independent wide loads.  Sums are fp64 (exact for bf16 keys), so
-//             the fp32 centroid is the correctly rounded mean.  Per-channel
-//             min/max of the tile is reduced with shuffles + LDS.
+//             streaming each page's 16 rows with 16 independent wide
+//             non-temporal loads.  Sums are fp64 in token order, as the
+//             oracle's (exact unless a block's keys in one channel span
+//             more than about 39 binades for bf16, 23 for fp32), so the fp32
+//             centroid is the correctly rounded mean.  Per-channel min/max
+//             of the tile is reduced with shuffles + LDS.
 //   range:    per (b, h, channel): min/max over tiles -> lo, scale (fp32).
 //   quantize: code = clamp(rint((c - lo) / scale), 0, 15), two per byte.
 // The other storage formats (Figure 8's precision comparison) change only
@@ -64,7 +67,7 @@ __global__ __launch_bounds__(256) void k_centroid_mean(Geom g, float* __restrict
             const int rows = min(kPage, t1 - t);
             Words<NW> w[kPage];
 #pragma unroll
-            for (int r = 0; r < kPage; ++r) w[r] = r < rows ? load_words<NW>(src + r * D) : zero_words<NW>();
+            for (int r = 0; r < kPage; ++r) w[r] = r < rows ? load_words_stream<NW>(src + r * D) : zero_words<NW>();
 #pragma unroll
             for (int r = 0; r < kPage; ++r)
 #pragma unroll
@@ -313,8 +316,9 @@ hipError_t build_impl(const Geom& g, const BuildArgs& a, hipStream_t s) {
 // clamped to the format's code range, counting the clamped codes).  One workgroup per (b, h).
 // Each 16-lane row group loads one 16-token page of a recomputed block (all
 // pages at once) and sums its rows in order in fp64; the page sums are then
-// added in page order (exact for bf16 keys, like the build's sums) and the
-// mean is coded by one thread per channel.
+// added in page order (exact, and so equal to the build's in-order sums,
+// unless a block's keys in one channel span more than about 39 binades for
+// bf16, 23 for fp32) and the mean is coded by one thread per channel.
 template <typename T, int D, int FMT>
 __global__ __launch_bounds__(256) void k_centroid_update(Geom g, int appended, const float* __restrict__ scale,
                                                          const float* __restrict__ lo, uint8_t* __restrict__ codes,

@@ -222,21 +222,21 @@ __global__ __launch_bounds__(256 * RG, (DecodeOccupancy<T, D, GT, PIPE, MF>::val
                     const int64_t base = ((int64_t)(pg >= 0 ? pg : 0) * g.Hkv + h) * (kPage * D);
 #pragma unroll
                     for (int st = 0; st < KSTEPS; ++st)
-                        kw[j * KSTEPS + st] = load_words_at<4>(kc + base + st * 32, k_off);
+                        kw[j * KSTEPS + st] = load_words_stream_at<4>(kc + base + st * 32, k_off);
                 }
             } else {
 #pragma unroll
                 for (int i = 0; i < CH; ++i) {   // branch-free: empty slots re-read page 0 and are masked later
                     const int pg = __builtin_amdgcn_readlane(ph, c0 + i);
                     const int64_t base = ((int64_t)(pg >= 0 ? pg : 0) * g.Hkv + h) * (kPage * D);
-                    kw[i] = load_words_at<NW>(kc + base, lane_off);
+                    kw[i] = load_words_stream_at<NW>(kc + base, lane_off);
                 }
             }
 #pragma unroll
             for (int k = 0; k < PPC; ++k) {   // this row group's pages rg, rg + RG, ...
                 const int pg = __builtin_amdgcn_readlane(ph, c0 + RG * k + rg);
                 const int64_t base = ((int64_t)(pg >= 0 ? pg : 0) * g.Hkv + h) * (kPage * D);
-                vw[k] = load_words_at<NW>(vc + base, lane_off);
+                vw[k] = load_words_stream_at<NW>(vc + base, lane_off);
             }
         };
         // fold the chunk at c0 into this row's running (m, l, o)
@@ -563,9 +563,9 @@ __global__ __launch_bounds__(256, 2) void k_sparse_decode_ws(Geom g, const uint1
             const int pg = __builtin_amdgcn_readlane(ph, c);
             const int64_t base = ((int64_t)(pg >= 0 ? pg : 0) * g.Hkv + h) * (kPage * D);
 #pragma unroll
-            for (int st = 0; st < KSTEPS; ++st) kw[st] = load_words_at<4>(kc + base + st * 32, k_off);
+            for (int st = 0; st < KSTEPS; ++st) kw[st] = load_words_stream_at<4>(kc + base + st * 32, k_off);
 #pragma unroll
-            for (int t = 0; t < kPage; ++t) vw[t] = load_words_at<1>(vc + base + t * D, v_off);
+            for (int t = 0; t < kPage; ++t) vw[t] = load_words_stream_at<1>(vc + base + t * D, v_off);
         };
         auto consume = [&](int c, const Words<4>(&kw)[KSTEPS], const Words<1>(&vw)[kPage]) {
             const int pg = __builtin_amdgcn_readlane(ph, c);

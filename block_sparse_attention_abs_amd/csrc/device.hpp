@@ -63,6 +63,38 @@ __device__ __forceinline__ Words<NW> load_words_at(const void* uniform_base, uin
     return load_words<NW>(static_cast<const char*>(uniform_base) + byte_off);
 }
 
+// The same with non-temporal loads, for data read once per call (key and
+// value pages, centroid codes): they are kept out of the caches' way.
+template <int NW>
+__device__ __forceinline__ Words<NW> load_words_stream(const void* p) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    Words<NW> r;
+    if constexpr (NW % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < NW / 4; ++i) {
+            const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + i);
+            r.w[4 * i + 0] = u.x;
+            r.w[4 * i + 1] = u.y;
+            r.w[4 * i + 2] = u.z;
+            r.w[4 * i + 3] = u.w;
+        }
+    } else if constexpr (NW == 2) {
+        const u32x2 u = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+        r.w[0] = u.x;
+        r.w[NW - 1] = u.y;
+    } else {
+        static_assert(NW == 1, "1, 2 or a multiple of 4 words");
+        r.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    }
+    return r;
+}
+
+template <int NW>
+__device__ __forceinline__ Words<NW> load_words_stream_at(const void* uniform_base, uint32_t byte_off) {
+    return load_words_stream<NW>(static_cast<const char*>(uniform_base) + byte_off);
+}
+
 template <int NW>
 __device__ __forceinline__ Words<NW> zero_words() {
     Words<NW> r;

@@ -85,7 +85,8 @@ __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restr
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
         const int j = min(j0 + r * GPW + grp, N - 1);
-        v[r] = *reinterpret_cast<const uint4*>(codes + (row0 + j) * RB + sub * 16);
+        const Words<4> cw = load_words_stream<4>(codes + (row0 + j) * RB + sub * 16);
+        v[r] = make_uint4(cw.w[0], cw.w[1], cw.w[2], cw.w[3]);
     }
 
     // per channel: w_d = qbar_d * scale_d and z_d = qbar_d * lo_d (fp64, LDS);
