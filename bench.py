@@ -59,7 +59,7 @@ METRIC = "sparse decode attn queries/s per layer at 32K/128K ctx; achieved HBM G
 # a hash of the kernel sources they were taken with; any other source
 # reports null.
 TRAFFIC = {
-    ("llama8b-128k-b4-bf16", 131072, "drawn", "c06a16f4f1ffb135"): 68858590,
+    ("llama8b-128k-b4-bf16", 131072, "drawn", "31319041a83d6a0d"): 68863925,
 }
 KERNEL_SOURCES = ("decode.hip", "device.hpp", "launch.hpp", "decode_layout.hpp")   # kernel + its launch layout
 
