@@ -10,12 +10,15 @@ under "build".
 Cold-cache honesty: the 256 MB Infinity Cache would hold a step's selected
 pages between repeats, so the layer is replicated R times in HBM (distinct
 copies of the K/V pools and of the centroid stores) and step i works on copy
-i mod R; with R = 8 every copy is evicted before it comes round again.
+i mod R.  By default R is the smallest count, at least 8, whose copies
+together hold twice the Infinity Cache in selected pages (8 at 128K x 4,
+64 at 32K x 1), within 64 copies and 64 GiB of K/V, so every copy is evicted
+before it comes round again.
 
 Prints ONE JSON line (see the "metric" field).  Options:
     --steps K --warmup W   timed / untimed steps (default 200 / 20)
     --workload cfgN        0..4 (default 3: batch 4, 128K context, budget 4096)
-    --replicas R           layer copies cycled through (default 8)
+    --replicas R           layer copies cycled through (default: see above)
     --layers N             instead of copies of one layer, N distinct layers
                            of the workload (their own data and block maps),
                            cycled through; each step is one layer
@@ -64,6 +67,20 @@ TRAFFIC = {
 KERNEL_SOURCES = ("decode.hip", "device.hpp", "launch.hpp", "decode_layout.hpp")   # kernel + its launch layout
 
 
+INFINITY_CACHE = 256 << 20
+
+
+def auto_replicas(w, x) -> int:
+    """Layer copies whose selected K/V pages add up to twice the Infinity
+    Cache (at least 8, at most 64 copies and 64 GiB of K/V)."""
+    sz = 2 if x.dtype == "bf16" else 4
+    sel_tokens = sum(min(w.token_budget, int(L)) for L in x.seq_lens) * w.num_kv_heads
+    step_bytes = max(1, sel_tokens * w.head_dim * 2 * sz)
+    kv_bytes = max(1, x.k_cache.nbytes + x.v_cache.nbytes)
+    r = max(8, -(-2 * INFINITY_CACHE // step_bytes))
+    return int(max(8, min(r, 64, (64 << 30) // kv_bytes)))
+
+
 def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
@@ -79,7 +96,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="cfg3")
-    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--replicas", type=int, default=0)
     ap.add_argument("--layers", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -143,7 +160,7 @@ def main():
 
     base = A.PagedKV.from_host(Hq, x.k_cache, x.v_cache, x.page_table, x.seq_lens, x.block_size, x.dtype, dev)
     q = A.upload(x.q, dev, x.dtype)
-    R = max(1, args.layers or args.replicas)
+    R = max(1, args.layers or args.replicas or auto_replicas(w, x))
     layers, qs = [base], [q]
     for r in range(1, R):
         if args.layers:
