@@ -2,9 +2,12 @@
 """Decode-step benchmark of the AB-Sparse library on one MI355X.
 
 One step = the whole decode hot path for one layer over one batch:
-abs_score_select (centroid scoring, INT4 by default, + top-K) then abs_sparse_decode
-(split attention over the selected pages, merged in the same launch), on
-inputs already resident in HBM.  The centroid build (prefill-time) is timed separately and reported
+centroid scoring (INT4 by default), top-K, and split attention over the
+selected pages merged in the same launch, on inputs already resident in HBM.
+By default a step is one abs_select_decode call (the scores, then the top-K
+inside the decode launch); --separate times abs_score_select then
+abs_sparse_decode instead.  Both forms are timed; "step_call" names the one
+`value` is from.  The centroid build (prefill-time) is timed separately and reported
 under "build".
 
 Cold-cache honesty: the 256 MB Infinity Cache would hold a step's selected
@@ -30,6 +33,7 @@ Prints ONE JSON line (see the "metric" field).  Options:
     --centroid-format F    int4 (default), int4_sym, int8, int4_tensor, bf16
     --warm-cache           also time R steps on one layer copy (Infinity
                            Cache warm), reported as warm_cache_step_us
+    --separate             a step is abs_score_select + abs_sparse_decode
     --naive-per-size       also time the per-block-size variant: the heads of
                            each block size as a layer of their own (cache
                            copied per group before timing), one select and
@@ -64,7 +68,7 @@ METRIC = "sparse decode attn queries/s per layer at 32K/128K ctx; achieved HBM G
 TRAFFIC = {
     ("llama8b-128k-b4-bf16", 131072, "drawn", "31319041a83d6a0d"): 68863925,
 }
-KERNEL_SOURCES = ("decode.hip", "device.hpp", "launch.hpp", "decode_layout.hpp")   # kernel + its launch layout
+KERNEL_SOURCES = ("decode.hip", "device.hpp", "launch.hpp", "decode_layout.hpp", "topk.hpp")   # kernel + its launch layout
 
 
 INFINITY_CACHE = 256 << 20
@@ -106,6 +110,7 @@ def parse():
     ap.add_argument("--block-map", default="drawn", choices=["drawn", "16", "32", "64"])
     ap.add_argument("--warm-cache", action="store_true")
     ap.add_argument("--naive-per-size", action="store_true")
+    ap.add_argument("--separate", action="store_true")
     ap.add_argument("--centroid-format", default="int4",
                     choices=["int4", "int4_sym", "int8", "int4_tensor", "bf16"])
     return ap.parse_args()
@@ -186,6 +191,7 @@ def main():
     ws_b = A.workspace(max(L.workspace_bytes(budget, A.ABS_OP_BUILD) for L in layers), dev)
     ws_s = A.workspace(max(L.workspace_bytes(budget, A.ABS_OP_SELECT) for L in layers), dev)
     ws_d = A.workspace(max(L.workspace_bytes(budget, A.ABS_OP_DECODE) for L in layers), dev)
+    ws_sd = A.workspace(max(L.workspace_bytes(budget, A.ABS_OP_SELECT_DECODE) for L in layers), dev)
     cap = max(L.select_capacity(budget) for L in layers)
     sel = torch.zeros((B, w.num_kv_heads, cap), dtype=torch.int32, device=dev)
     cnt = torch.zeros((B, w.num_kv_heads), dtype=torch.int32, device=dev)
@@ -217,9 +223,18 @@ def main():
                             budget, sm, int(out.data_ptr()), int(lse.data_ptr()), int(ws_d.data_ptr()), ws_d.numel(),
                             st)
 
-    def step(i, st):
+    def separate_step(i, st):
         select_call(i, st)
         decode_call(i, st)
+
+    def fused_step(i, st):
+        r = i % R
+        L = layers[r]
+        A.abs_select_decode(L.kv, L.bmap, cents[r].desc, int(qs[r].data_ptr()), budget, sm, int(sel.data_ptr()),
+                            cap, int(cnt.data_ptr()), int(out.data_ptr()), int(lse.data_ptr()),
+                            int(ws_sd.data_ptr()), ws_sd.numel(), st)
+
+    step = separate_step if args.separate else fused_step
 
     # eager warm-up, then each timed unit is a HIP graph of R back-to-back
     # calls (one per layer copy), so host launch cost stays out of the timing
@@ -248,6 +263,7 @@ def main():
         return g
 
     g_step, g_sel, g_dec = capture(step), capture(select_call), capture(decode_call)
+    g_fused, g_sep = capture(fused_step), capture(separate_step)
     torch.cuda.synchronize()
 
     def timed(g, reps, tail=None):
@@ -277,6 +293,11 @@ def main():
     sreps = max(1, min(reps, 32))
     sel_us = np.array([timed(g_sel, sreps) / (sreps * R) * 1e3 for _ in range(5)])
     dec_us = np.array([timed(g_dec, sreps) / (sreps * R) * 1e3 for _ in range(5)])
+    # both step forms, timed the same way, alternating
+    form_us = {"fused": [], "separate": []}
+    for _ in range(5):
+        form_us["fused"].append(timed(g_fused, sreps) / (sreps * R) * 1e3)
+        form_us["separate"].append(timed(g_sep, sreps) / (sreps * R) * 1e3)
     # warm Infinity Cache, for reference: R steps on the same layer copy
     warm_us = None
     if args.warm_cache:
@@ -337,6 +358,9 @@ def main():
         "cpu_baseline": cpu,
         "step": {"algorithmic_bytes": ab["step"], "hbm_gbs": round(ab["step"] / (ms_per_step * 1e-3) / 1e9, 1),
                  "hbm_frac": round(ab["step"] / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                 "step_call": "abs_score_select + abs_sparse_decode" if args.separate else "abs_select_decode",
+                 "select_decode_step_us": round(float(np.median(form_us["fused"])), 3),
+                 "separate_calls_step_us": round(float(np.median(form_us["separate"])), 3),
                  "score_select_us": round(float(np.median(sel_us)), 3), "sparse_decode_us": round(dec_avg, 3),
                  "sparse_decode_us_min_max": [round(float(dec_us.min()), 3), round(float(dec_us.max()), 3)],
                  "step_us_p10_p50_p90": [round(float(np.percentile(per_rep, q)), 3) for q in (10, 50, 90)],

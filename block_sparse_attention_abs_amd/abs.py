@@ -23,14 +23,14 @@ LIB_PATH = os.path.join(_PKG, "libabs.so")
 
 ABS_OK, ABS_ERR_INVALID_ARG, ABS_ERR_UNSUPPORTED, ABS_ERR_WORKSPACE, ABS_ERR_HIP = range(5)
 ABS_F32, ABS_BF16 = 0, 1
-ABS_OP_BUILD, ABS_OP_SELECT, ABS_OP_DECODE = 0, 1, 2
+ABS_OP_BUILD, ABS_OP_SELECT, ABS_OP_DECODE, ABS_OP_SELECT_DECODE = 0, 1, 2, 3
 # abs_centroid_format, by name
 CENTROID_FORMATS = {"int4": 0, "int4_sym": 1, "int8": 2, "int4_tensor": 3, "bf16": 4}
 
 EXPORTS = ("abs_status_str", "abs_last_error", "abs_total_blocks", "abs_centroid_offsets",
            "abs_centroid_offsets_capacity", "abs_centroid_row_bytes", "abs_select_capacity", "abs_workspace_bytes", "abs_build_centroids",
-           "abs_update_centroids", "abs_score_select", "abs_sparse_decode", "abs_head_recall",
-           "abs_assign_block_sizes")
+           "abs_update_centroids", "abs_score_select", "abs_sparse_decode", "abs_select_decode",
+           "abs_head_recall", "abs_assign_block_sizes")
 
 
 class abs_paged_kv(C.Structure):
@@ -92,6 +92,8 @@ def lib():
         L.abs_score_select.argtypes = [KV, MAP, CEN, P, i32, P, i32, P, P, C.c_size_t, P]
         L.abs_sparse_decode.restype = st
         L.abs_sparse_decode.argtypes = [KV, MAP, P, P, i32, P, i32, C.c_float, P, P, P, C.c_size_t, P]
+        L.abs_select_decode.restype = st
+        L.abs_select_decode.argtypes = [KV, MAP, CEN, P, i32, C.c_float, P, i32, P, P, P, P, C.c_size_t, P]
         L.abs_head_recall.restype = st
         L.abs_head_recall.argtypes = [KV, P, P, P, P]
         L.abs_assign_block_sizes.restype = st
@@ -176,6 +178,14 @@ def abs_sparse_decode(kv, bmap, q_ptr: int, sel_ptr: int, sel_cap: int, count_pt
                       stream: int) -> None:
     _check(lib().abs_sparse_decode(C.byref(kv), C.byref(bmap), q_ptr, sel_ptr, sel_cap, count_ptr, token_budget,
                                    sm_scale, out_ptr, lse_ptr, ws_ptr, ws_bytes, stream), "abs_sparse_decode")
+
+
+def abs_select_decode(kv, bmap, cents, q_ptr: int, token_budget: int, sm_scale: float, sel_ptr: int, sel_cap: int,
+                      count_ptr: int, out_ptr: int, lse_ptr: Optional[int], ws_ptr: int, ws_bytes: int,
+                      stream: int) -> None:
+    _check(lib().abs_select_decode(C.byref(kv), C.byref(bmap), C.byref(cents), q_ptr, token_budget, sm_scale,
+                                   sel_ptr, sel_cap, count_ptr, out_ptr, lse_ptr, ws_ptr, ws_bytes, stream),
+           "abs_select_decode")
 
 
 def abs_head_recall(kv, lse_sel_ptr: int, lse_full_ptr: int, recall_ptr: int, stream: int) -> None:
@@ -360,6 +370,17 @@ def sparse_decode(kv: PagedKV, q, sel, count, budget: int, sm_scale: float, out,
     ws = workspace(need, kv.k_cache.device) if ws is None else ws
     abs_sparse_decode(kv.kv, kv.bmap, _ptr(q), _ptr(sel), int(sel.shape[-1]), _ptr(count), budget, sm_scale,
                       _ptr(out), _ptr(lse) if lse is not None else None, _ptr(ws), ws.numel(),
+                      current_stream() if stream is None else stream)
+
+
+def select_decode(kv: PagedKV, cents: Centroids, q, budget: int, sm_scale: float, sel, count, out, lse=None,
+                  ws=None, stream: Optional[int] = None) -> None:
+    """score_select then sparse_decode through abs_select_decode (fewer launches).
+    A workspace passed in must have been zero-filled before its first use."""
+    need = kv.workspace_bytes(budget, ABS_OP_SELECT_DECODE)
+    ws = workspace(need, kv.k_cache.device) if ws is None else ws
+    abs_select_decode(kv.kv, kv.bmap, cents.desc, _ptr(q), budget, sm_scale, _ptr(sel), int(sel.shape[-1]),
+                      _ptr(count), _ptr(out), _ptr(lse) if lse is not None else None, _ptr(ws), ws.numel(),
                       current_stream() if stream is None else stream)
 
 

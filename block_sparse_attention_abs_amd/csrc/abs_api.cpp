@@ -193,6 +193,74 @@ abs_status hip_status(hipError_t e, const char* what) {
     return ok();
 }
 
+// Checks shared by the calls that select (after plan_budget).
+abs_status check_select(const Plan& p, const abs_centroids* cents, const void* q, const int32_t* sel,
+                        int32_t sel_cap, const int32_t* sel_count) {
+    if (abs_status st = check_centroids(cents)) return st;
+    if (q == nullptr || sel == nullptr || sel_count == nullptr)
+        return fail(ABS_ERR_INVALID_ARG, "null q, sel or sel_count");
+    if (sel_cap < p.sel_cap) return fail(ABS_ERR_INVALID_ARG, "sel_cap %d < required %d", sel_cap, p.sel_cap);
+    if (p.max_n > absk::kMaxBlocksPerHead)
+        return fail(ABS_ERR_UNSUPPORTED, "%d blocks in one head (max %d)", p.max_n, absk::kMaxBlocksPerHead);
+    return ok();
+}
+
+// Launch arguments of the select stage; `scores` is its workspace, `tiles`
+// storage for the score tile list (read during the launch).
+void fill_select_args(const Plan& p, const abs_paged_kv* kv, const abs_block_map* map, const abs_centroids* cents,
+                      const void* q, int32_t token_budget, int32_t* sel, int32_t sel_cap, int32_t* sel_count,
+                      void* scores, uint32_t* tiles, absk::SelectArgs* a) {
+    a->codes = cents->codes;
+    a->scale = cents->scale;
+    a->lo = cents->lo;
+    a->fmt = cents->format;
+    a->q = q;
+    a->scores = reinterpret_cast<float*>(scores);
+    a->stride = score_stride(p);
+    a->sel = sel;
+    a->count = sel_count;
+    a->sel_cap = sel_cap;
+    a->budget = token_budget;
+    a->max_n = p.max_n;
+    a->max_len = p.max_len;
+    // the exact list of score tiles, when it fits the kernel arguments
+    a->ntiles = 0;
+    for (int b = 0; b < p.g.B; ++b)
+        for (int h = 0; h < p.g.Hkv; ++h) {
+            const int64_t n = ceil_div64(ceil_div64(kv->seq_lens_host[b], map->block_size_host[h]),
+                                         absk::kScoreBlocksPerWg);
+            for (int64_t t = 0; t < n; ++t, ++a->ntiles)
+                if (a->ntiles < absk::kMaxScoreTiles) tiles[a->ntiles] = (uint32_t)(b * p.g.Hkv + h) << 8 | (uint32_t)t;
+        }
+    a->tiles_host = a->ntiles <= absk::kMaxScoreTiles ? tiles : nullptr;
+    // per-head cumulative tiles of the longest sequence (the grid when the list does not fit)
+    a->head_tiles.cum[0] = 0;
+    for (int h = 0; h < p.g.Hkv; ++h)
+        a->head_tiles.cum[h + 1] =
+            a->head_tiles.cum[h] +
+            (uint32_t)ceil_div64(ceil_div64(p.max_len, map->block_size_host[h]), absk::kScoreBlocksPerWg);
+}
+
+// Launch arguments of the decode stage; `ws` is its workspace.
+void fill_decode_args(const absk::DecodeLayout& l, const void* q, const int32_t* sel, int32_t sel_cap,
+                      const int32_t* sel_count, float sm_scale, void* out, float* lse, void* ws,
+                      absk::DecodeArgs* a) {
+    a->q = q;
+    a->sel = sel;
+    a->count = sel_count;
+    a->sel_cap = sel_cap;
+    a->sm_scale = sm_scale;
+    a->out = out;
+    a->lse = lse;
+    a->part_ml = reinterpret_cast<float*>(ws_at(ws, l.ml));
+    a->part_o = reinterpret_cast<float*>(ws_at(ws, l.o));
+    a->arrive = ABS_DECODE_FUSED_MERGE ? reinterpret_cast<int32_t*>(ws_at(ws, l.arrive)) : nullptr;
+    a->pages_per_wg = l.ppw;
+    a->chunk = l.chunk;
+    a->pipelined = l.pipelined;
+    a->splits = l.splits;
+}
+
 }  // namespace
 
 extern "C" {
@@ -282,6 +350,10 @@ abs_status abs_workspace_bytes(const abs_paged_kv* kv, const abs_block_map* map,
             if (abs_status st = plan_budget(kv, map, token_budget, &p)) return st;
             *bytes = decode_layout(p).bytes;
             return ok();
+        case ABS_OP_SELECT_DECODE:
+            if (abs_status st = plan_budget(kv, map, token_budget, &p)) return st;
+            *bytes = select_bytes(p) + decode_layout(p).bytes;
+            return ok();
     }
     return fail(ABS_ERR_INVALID_ARG, "unknown op %d", (int)op);
 }
@@ -332,48 +404,13 @@ abs_status abs_score_select(const abs_paged_kv* kv, const abs_block_map* map, co
     if (abs_status st = check_geometry(kv, map, &p)) return st;
     if (abs_status st = require_device(p, false)) return st;
     if (abs_status st = plan_budget(kv, map, token_budget, &p)) return st;
-    if (abs_status st = check_centroids(cents)) return st;
-    if (q == nullptr || sel == nullptr || sel_count == nullptr)
-        return fail(ABS_ERR_INVALID_ARG, "null q, sel or sel_count");
-    if (sel_cap < p.sel_cap) return fail(ABS_ERR_INVALID_ARG, "sel_cap %d < required %d", sel_cap, p.sel_cap);
-    if (p.max_n > absk::kMaxBlocksPerHead)
-        return fail(ABS_ERR_UNSUPPORTED, "%d blocks in one head (max %d)", p.max_n, absk::kMaxBlocksPerHead);
+    if (abs_status st = check_select(p, cents, q, sel, sel_cap, sel_count)) return st;
     const size_t need = select_bytes(p);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(ABS_ERR_WORKSPACE, "select needs %zu workspace bytes, got %zu", need, workspace_bytes);
     absk::SelectArgs a;
-    a.codes = cents->codes;
-    a.scale = cents->scale;
-    a.lo = cents->lo;
-    a.fmt = cents->format;
-    a.q = q;
-    a.scores = reinterpret_cast<float*>(workspace);
-    a.stride = score_stride(p);
-    a.sel = sel;
-    a.count = sel_count;
-    a.sel_cap = sel_cap;
-    a.budget = token_budget;
-    a.max_n = p.max_n;
-    a.max_len = p.max_len;
-    // the exact list of score tiles, when it fits the kernel arguments
     uint32_t tiles[absk::kMaxScoreTiles];
-    a.ntiles = 0;
-    for (int b = 0; b < p.g.B; ++b)
-        for (int h = 0; h < p.g.Hkv; ++h) {
-            const int64_t n = ceil_div64(ceil_div64(kv->seq_lens_host[b], map->block_size_host[h]),
-                                         absk::kScoreBlocksPerWg);
-            for (int64_t t = 0; t < n; ++t, ++a.ntiles)
-                if (a.ntiles < absk::kMaxScoreTiles) tiles[a.ntiles] = (uint32_t)(b * p.g.Hkv + h) << 8 | (uint32_t)t;
-        }
-    a.tiles_host = a.ntiles <= absk::kMaxScoreTiles ? tiles : nullptr;
-    // per-head cumulative tiles of the longest sequence (the grid when the list does not fit)
-    int max_len = 0;
-    for (int b = 0; b < p.g.B; ++b) max_len = std::max(max_len, kv->seq_lens_host[b]);
-    a.head_tiles.cum[0] = 0;
-    for (int h = 0; h < p.g.Hkv; ++h)
-        a.head_tiles.cum[h + 1] =
-            a.head_tiles.cum[h] +
-            (uint32_t)ceil_div64(ceil_div64(max_len, map->block_size_host[h]), absk::kScoreBlocksPerWg);
+    fill_select_args(p, kv, map, cents, q, token_budget, sel, sel_cap, sel_count, workspace, tiles, &a);
     return hip_status(absk::launch_select(p.g, p.dt, a, static_cast<hipStream_t>(stream)), "score_select");
 }
 
@@ -392,21 +429,38 @@ abs_status abs_sparse_decode(const abs_paged_kv* kv, const abs_block_map* map, c
     if (workspace == nullptr || workspace_bytes < l.bytes)
         return fail(ABS_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", l.bytes, workspace_bytes);
     absk::DecodeArgs a;
-    a.q = q;
-    a.sel = sel;
-    a.count = sel_count;
-    a.sel_cap = sel_cap;
-    a.sm_scale = sm_scale;
-    a.out = out;
-    a.lse = lse;
-    a.part_ml = reinterpret_cast<float*>(ws_at(workspace, l.ml));
-    a.part_o = reinterpret_cast<float*>(ws_at(workspace, l.o));
-    a.arrive = ABS_DECODE_FUSED_MERGE ? reinterpret_cast<int32_t*>(ws_at(workspace, l.arrive)) : nullptr;
-    a.pages_per_wg = l.ppw;
-    a.chunk = l.chunk;
-    a.pipelined = l.pipelined;
-    a.splits = l.splits;
+    fill_decode_args(l, q, sel, sel_cap, sel_count, sm_scale, out, lse, workspace, &a);
     return hip_status(absk::launch_decode(p.g, p.dt, a, static_cast<hipStream_t>(stream)), "sparse_decode");
+}
+
+abs_status abs_select_decode(const abs_paged_kv* kv, const abs_block_map* map, const abs_centroids* cents,
+                             const void* q, int32_t token_budget, float sm_scale, int32_t* sel, int32_t sel_cap,
+                             int32_t* sel_count, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    Plan p;
+    if (abs_status st = check_geometry(kv, map, &p)) return st;
+    if (abs_status st = require_device(p, true)) return st;
+    if (abs_status st = plan_budget(kv, map, token_budget, &p)) return st;
+    if (abs_status st = check_select(p, cents, q, sel, sel_cap, sel_count)) return st;
+    if (out == nullptr) return fail(ABS_ERR_INVALID_ARG, "null out");
+    if (!std::isfinite(sm_scale)) return fail(ABS_ERR_INVALID_ARG, "sm_scale is not finite");
+    const size_t sbytes = select_bytes(p);
+    const absk::DecodeLayout l = decode_layout(p);
+    if (workspace == nullptr || workspace_bytes < sbytes + l.bytes)
+        return fail(ABS_ERR_WORKSPACE, "select_decode needs %zu workspace bytes, got %zu", sbytes + l.bytes,
+                    workspace_bytes);
+    absk::SelectArgs sa;
+    uint32_t tiles[absk::kMaxScoreTiles];
+    fill_select_args(p, kv, map, cents, q, token_budget, sel, sel_cap, sel_count, workspace, tiles, &sa);
+    absk::DecodeArgs da;
+    fill_decode_args(l, q, sel, sel_cap, sel_count, sm_scale, out, lse, ws_at(workspace, sbytes), &da);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (absk::select_decode_fusable(p.g, p.dt, sa, da)) {
+        if (abs_status e = hip_status(absk::launch_scores(p.g, p.dt, sa, st), "select_decode (scores)")) return e;
+        return hip_status(absk::launch_select_decode(p.g, p.dt, sa, da, st), "select_decode");
+    }
+    if (abs_status e = hip_status(absk::launch_select(p.g, p.dt, sa, st), "select_decode (select)")) return e;
+    return hip_status(absk::launch_decode(p.g, p.dt, da, st), "select_decode (decode)");
 }
 
 abs_status abs_head_recall(const abs_paged_kv* kv, const float* lse_sel, const float* lse_full, float* recall,

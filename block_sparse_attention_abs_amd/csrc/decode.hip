@@ -27,6 +27,7 @@
 //         switch keeps the older form, a second launch with one workgroup
 //         per (b, query head).
 #include "device.hpp"
+#include "topk.hpp"
 
 // Build-time tuning: partials the merging workgroup loads per pass.
 #ifndef ABS_DECODE_MERGE_BATCH
@@ -487,13 +488,15 @@ __global__ __launch_bounds__(256 * RG, (DecodeOccupancy<T, D, GT, PIPE, MF>::val
 // next page's loads while the current page is folded, and more buffers
 // measured slower.  No LDS and no barrier until the four wavefronts' states
 // are combined at the end.
-template <int GT>
-__global__ __launch_bounds__(256, 2) void k_sparse_decode_ws(Geom g, const uint16_t* __restrict__ q,
-                                                             const int32_t* __restrict__ sel, int sel_cap,
-                                                             const int32_t* __restrict__ count, float qscale,
-                                                             float* __restrict__ part_ml, float* __restrict__ part_o,
-                                                             int splits, int ppw, int32_t* __restrict__ arrive,
-                                                             uint16_t* __restrict__ out, float* __restrict__ lse) {
+// The body, for a lane whose page gp = split * ppw + lane lies in selected
+// block sv (the selection entry at position gp >> log2(pages per block),
+// clamped into the row) of a head with K selected blocks; NW wavefronts in
+// the workgroup, of which 0-3 do the work.
+template <int GT, int NW>
+__device__ __forceinline__ void ws_decode(const Geom& g, const uint16_t* __restrict__ q, int sv, int K, int sel_cap,
+                                          float qscale, float* __restrict__ part_ml, float* __restrict__ part_o,
+                                          int splits, int ppw, int32_t* __restrict__ arrive,
+                                          uint16_t* __restrict__ out, float* __restrict__ lse) {
     using T = uint16_t;
     constexpr int D = 128;
     constexpr int KSTEPS = D / 32;
@@ -505,17 +508,16 @@ __global__ __launch_bounds__(256, 2) void k_sparse_decode_ws(Geom g, const uint1
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
     const int wave = threadIdx.x / 64;
     const int wl = threadIdx.x & 63;
+    const bool worker = NW == 4 || wave < 4;
 
     const int spb = block_size_of(g, h) / kPage;      // pages per block (stride): 1, 2 or 4
     const int sh = __builtin_ctz(spb);
     const int p0 = split * ppw;                        // ppw <= 64
     const int gp = p0 + wl;
     const bool in_row = wl < ppw && gp < sel_cap * spb;
-    const int sv = sel[(int64_t)bh * sel_cap + min(gp >> sh, sel_cap - 1)];   // unconditional, clamped
     const int L = g.seq_lens[b];
     const int npages = ceil_div(L, kPage);
     const int N = ceil_div(L, spb * kPage);
-    const int K = min(max(count[bh], 0), sel_cap);
     const int total = min(K * spb, splits * ppw);      // selected pages of (b, h)
     int ph = -1, lp = 0;
     if (in_row) {
@@ -558,7 +560,9 @@ __global__ __launch_bounds__(256, 2) void k_sparse_decode_ws(Geom g, const uint1
         const uint32_t k_off = (uint32_t)(((wl & 15) * D + (wl >> 4) * 8) * sizeof(T));
         const uint32_t v_off = (uint32_t)(2 * wl * sizeof(T));
         const int nvalid = min(max(total - p0, 0), ppw);             // pages of this workgroup
-        const int npw = nvalid > wave ? (nvalid - wave + 3) / 4 : 0;   // ... of this wavefront
+        // ... of this wavefront; only wavefronts 0-3 stream pages (a launch
+        // with more wavefronts, for the fused top-K, idles the others here)
+        const int npw = worker && nvalid > wave ? (nvalid - wave + 3) / 4 : 0;
         auto issue = [&](int c, Words<4>(&kw)[KSTEPS], Words<1>(&vw)[kPage]) {
             const int pg = __builtin_amdgcn_readlane(ph, c);
             const int64_t base = ((int64_t)(pg >= 0 ? pg : 0) * g.Hkv + h) * (kPage * D);
@@ -625,19 +629,21 @@ __global__ __launch_bounds__(256, 2) void k_sparse_decode_ws(Geom g, const uint1
         // wavefronts -> workgroup: the common max, then each wavefront's
         // rescaled state to LDS; every thread then sums two channels over
         // the four wavefronts
-        if (wl == 0) {
+        if (wl == 0 && worker) {
 #pragma unroll
             for (int gg = 0; gg < GT; ++gg) s_red[wave][gg] = m[gg];
         }
         __syncthreads();
+        if (worker) {
 #pragma unroll
-        for (int gg = 0; gg < GT; ++gg) {
-            float M = s_red[0][gg];
+            for (int gg = 0; gg < GT; ++gg) {
+                float M = s_red[0][gg];
 #pragma unroll
-            for (int w = 1; w < 4; ++w) M = fmaxf(M, s_red[w][gg]);
-            const float f = m[gg] == NEG ? 0.0f : exp2_approx(m[gg] - M);
-            *reinterpret_cast<float2*>(&s_o[wave][gg][2 * wl]) = make_float2(o[gg][0] * f, o[gg][1] * f);
-            if (wl == 0) s_l[wave][gg] = l[gg] * f;
+                for (int w = 1; w < 4; ++w) M = fmaxf(M, s_red[w][gg]);
+                const float f = m[gg] == NEG ? 0.0f : exp2_approx(m[gg] - M);
+                *reinterpret_cast<float2*>(&s_o[wave][gg][2 * wl]) = make_float2(o[gg][0] * f, o[gg][1] * f);
+                if (wl == 0) s_l[wave][gg] = l[gg] * f;
+            }
         }
         __syncthreads();
     }
@@ -747,6 +753,56 @@ __global__ __launch_bounds__(256, 2) void k_sparse_decode_ws(Geom g, const uint1
         }
         write_output(out, lse, bi, d, acc, mg, ls, D);
     }
+}
+
+// The selection read from sel / sel_count (abs_sparse_decode).
+template <int GT>
+__global__ __launch_bounds__(256, 2) void k_sparse_decode_ws(Geom g, const uint16_t* __restrict__ q,
+                                                             const int32_t* __restrict__ sel, int sel_cap,
+                                                             const int32_t* __restrict__ count, float qscale,
+                                                             float* __restrict__ part_ml, float* __restrict__ part_o,
+                                                             int splits, int ppw, int32_t* __restrict__ arrive,
+                                                             uint16_t* __restrict__ out, float* __restrict__ lse) {
+    const int bh = blockIdx.y;
+    const int sh = __builtin_ctz(block_size_of(g, bh % g.Hkv) / kPage);
+    const int gp = blockIdx.x * ppw + (int)(threadIdx.x & 63);
+    const int sv = sel[(int64_t)bh * sel_cap + min(gp >> sh, sel_cap - 1)];   // unconditional, clamped
+    const int K = min(max(count[bh], 0), sel_cap);
+    ws_decode<GT, 4>(g, q, sv, K, sel_cap, qscale, part_ml, part_o, splits, ppw, arrive, out, lse);
+}
+
+// Top-K and decode in one launch (abs_select_decode): every split workgroup
+// of (b, h) runs the head's top-K over the score row itself (topk.hpp, 512
+// threads of KPT keys, as the top-K launch), keeps in LDS the selected blocks
+// at the positions its pages cover, and decodes them with wavefronts 0-3;
+// split 0 also writes sel and sel_count.  The workgroups of a head compute
+// the same selection from the same row.
+template <int GT, int KPT>
+__global__ __launch_bounds__(512) void k_select_decode_ws(Geom g, const float* __restrict__ scores, int stride,
+                                                          int max_len, int budget, int32_t* __restrict__ sel,
+                                                          int sel_cap, int32_t* __restrict__ count,
+                                                          const uint16_t* __restrict__ q, float qscale,
+                                                          float* __restrict__ part_ml, float* __restrict__ part_o,
+                                                          int splits, int ppw, int32_t* __restrict__ arrive,
+                                                          uint16_t* __restrict__ out, float* __restrict__ lse) {
+    const int split = blockIdx.x;
+    const int bh = blockIdx.y;
+    const int sh = __builtin_ctz(block_size_of(g, bh % g.Hkv) / kPage);
+    const int first = (split * ppw) >> sh;            // selection positions first .. first + 63 (ppw <= 64)
+    __shared__ int32_t s_blk[kMaxPagesPerWg];
+    int32_t* row_out = sel + (int64_t)bh * sel_cap;
+    const int K = topk_rows<kFusedThreads, KPT>(g, bh, scores + (int64_t)bh * stride, stride, max_len, budget,
+                                                [&](uint32_t p, int32_t j) {
+                                                    if (split == 0 && p < (uint32_t)sel_cap) row_out[p] = j;
+                                                    const uint32_t r = p - (uint32_t)first;
+                                                    if (r < (uint32_t)kMaxPagesPerWg) s_blk[r] = j;
+                                                });
+    if (split == 0 && threadIdx.x == 0) count[bh] = K;
+    __syncthreads();
+    const int gp = split * ppw + (int)(threadIdx.x & 63);
+    const int sv = s_blk[min(max((gp >> sh) - first, 0), kMaxPagesPerWg - 1)];   // positions >= K: unused
+    ws_decode<GT, kFusedThreads / 64>(g, q, sv, min(K, sel_cap), sel_cap, qscale, part_ml, part_o, splits, ppw,
+                                      arrive, out, lse);
 }
 
 // One workgroup per (b, query head): merge the partials of the splits that
@@ -867,6 +923,47 @@ hipError_t decode_impl(const Geom& g, const DecodeArgs& a, hipStream_t s) {
 hipError_t launch_decode(const Geom& g, DType dt, const DecodeArgs& a, hipStream_t s) {
     if (dt == DType::BF16) return g.D == 128 ? decode_impl<uint16_t, 128>(g, a, s) : decode_impl<uint16_t, 64>(g, a, s);
     return g.D == 128 ? decode_impl<float, 128>(g, a, s) : decode_impl<float, 64>(g, a, s);
+}
+
+// The fused form covers the layers the wavefront-split decode serves (the
+// same conditions as in decode_gt) whose heads have at most 512 x 32 blocks,
+// and is used where it measured faster than the separate launches: heads of
+// at most 4096 blocks, or a split grid that fits the 256 compute units once
+// (beyond that, two workgroups of a compute unit each repeat their head's
+// top-K of up to 16384 keys; 128K x 16: 68.6 against 68.0 us per step).
+bool select_decode_fusable(const Geom& g, DType dt, const SelectArgs& s, const DecodeArgs& a) {
+    const bool served = ABS_DECODE_WAVES && ABS_DECODE_MATRIX && dt == DType::BF16 && g.D == 128 && g.G <= 4 &&
+                        (a.pipelined || a.chunk == 8) && a.arrive != nullptr && s.max_n <= kFusedTopkMaxN;
+    const bool faster = s.max_n <= 4096 || (int64_t)a.splits * g.B * g.Hkv <= kComputeUnits;
+    return served && faster;
+}
+
+namespace {
+
+template <int GT, int KPT>
+void launch_fused(const Geom& g, const SelectArgs& s, const DecodeArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL((k_select_decode_ws<GT, KPT>), dim3(a.splits, g.B * g.Hkv), dim3(kFusedThreads), 0, st, g, s.scores,
+                       s.stride, s.max_len, s.budget, s.sel, s.sel_cap, s.count,
+                       reinterpret_cast<const uint16_t*>(a.q), a.sm_scale * kLog2e, a.part_ml, a.part_o, a.splits,
+                       a.pages_per_wg, a.arrive, reinterpret_cast<uint16_t*>(a.out), a.lse);
+}
+
+template <int GT>
+void launch_fused_gt(const Geom& g, const SelectArgs& s, const DecodeArgs& a, hipStream_t st) {
+    if (s.max_n <= kFusedThreads * 4) launch_fused<GT, 4>(g, s, a, st);
+    else if (s.max_n <= kFusedThreads * 8) launch_fused<GT, 8>(g, s, a, st);
+    else if (s.max_n <= kFusedThreads * 16) launch_fused<GT, 16>(g, s, a, st);
+    else launch_fused<GT, 32>(g, s, a, st);
+}
+
+}  // namespace
+
+hipError_t launch_select_decode(const Geom& g, DType dt, const SelectArgs& s, const DecodeArgs& a, hipStream_t st) {
+    if (!select_decode_fusable(g, dt, s, a)) return hipErrorInvalidValue;
+    if (g.G <= 1) launch_fused_gt<1>(g, s, a, st);
+    else if (g.G <= 2) launch_fused_gt<2>(g, s, a, st);
+    else launch_fused_gt<4>(g, s, a, st);
+    return hipGetLastError();
 }
 
 }  // namespace absk

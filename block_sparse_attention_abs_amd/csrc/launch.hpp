@@ -131,6 +131,16 @@ constexpr int kMaxPagesPerWg = 64;
 
 hipError_t launch_decode(const Geom& g, DType dt, const DecodeArgs& a, hipStream_t s);
 
+// abs_select_decode: the score launch alone (launch_scores), then one launch
+// that runs the top-K inside the split decode (launch_select_decode), when
+// select_decode_fusable(); otherwise launch_select and launch_decode.
+constexpr int kFusedThreads = 512;                 // the fused launch's workgroup: the top-K launch's width
+constexpr int kFusedTopkMaxN = kFusedThreads * 32;
+constexpr int kComputeUnits = 256;                 // MI355X
+hipError_t launch_scores(const Geom& g, DType dt, const SelectArgs& a, hipStream_t s);
+bool select_decode_fusable(const Geom& g, DType dt, const SelectArgs& s, const DecodeArgs& a);
+hipError_t launch_select_decode(const Geom& g, DType dt, const SelectArgs& s, const DecodeArgs& a, hipStream_t st);
+
 // Calibration: recall[h] = mean over (b, query heads of h) of exp(lse_sel - lse_full).
 hipError_t launch_head_recall(int B, int Hq, int Hkv, const float* lse_sel, const float* lse_full, float* recall,
                               hipStream_t s);

@@ -57,7 +57,8 @@ typedef enum abs_dtype {
 typedef enum abs_op {
     ABS_OP_BUILD = 0,    /* abs_build_centroids */
     ABS_OP_SELECT = 1,   /* abs_score_select */
-    ABS_OP_DECODE = 2    /* abs_sparse_decode */
+    ABS_OP_DECODE = 2,   /* abs_sparse_decode */
+    ABS_OP_SELECT_DECODE = 3   /* abs_select_decode */
 } abs_op;
 
 /*
@@ -275,6 +276,27 @@ abs_status abs_sparse_decode(const abs_paged_kv *kv, const abs_block_map *map, c
                              const int32_t *sel, int32_t sel_cap, const int32_t *sel_count,
                              int32_t token_budget, float sm_scale, void *out, float *lse,
                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * abs_score_select followed by abs_sparse_decode on the same query, in fewer
+ * launches: the scores in one launch, then the top-K inside the decode's
+ * split launch (every workgroup of a head selects the head's blocks itself
+ * from the scores, keeps the positions its pages cover, and the first one
+ * writes sel and sel_count).  sel, sel_count, out and lse are written as the
+ * two calls write them, with the same values (the same arithmetic).  The
+ * fused launch serves bf16 caches with head_dim 128, up to 4 query heads per
+ * KV head and at most 8192 blocks per head; other layers run the two calls'
+ * launches, with the same results.
+ *   Arguments: as abs_score_select and abs_sparse_decode (token_budget is
+ *   both the selection budget and the decode's).
+ *   workspace: >= abs_workspace_bytes(ABS_OP_SELECT_DECODE) bytes: the select
+ *       workspace (abs_workspace_bytes(ABS_OP_SELECT) bytes), then the
+ *       decode workspace, whose zero-filling rule applies to this region.
+ */
+abs_status abs_select_decode(const abs_paged_kv *kv, const abs_block_map *map, const abs_centroids *cents,
+                             const void *q, int32_t token_budget, float sm_scale, int32_t *sel,
+                             int32_t sel_cap, int32_t *sel_count, void *out, float *lse, void *workspace,
+                             size_t workspace_bytes, void *stream);
 
 /*
  * Offline block-size calibration (Figure 3 of the page: per-head recall at

@@ -25,7 +25,7 @@ def header_functions():
 
 def test_exports_every_declared_call():
     names = header_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     assert sorted(A.EXPORTS) == names
     L = A.lib()
     for n in names:
@@ -92,8 +92,12 @@ def test_geometry_helpers_agree_with_oracle(oracle_mod):
     assert off[:-1].tolist() == [r[2] for r in rows] and off[-1] == oracle_mod.total_blocks(h.sl, h.bs)
     for budget in (1, 17, 64, 100, 4096):
         assert A.abs_select_capacity(h.kv, h.bmap, budget) == oracle_mod.sel_capacity(h.sl, h.bs, budget)
-    for op in (A.ABS_OP_BUILD, A.ABS_OP_SELECT, A.ABS_OP_DECODE):
+    for op in (A.ABS_OP_BUILD, A.ABS_OP_SELECT, A.ABS_OP_DECODE, A.ABS_OP_SELECT_DECODE):
         assert A.abs_workspace_bytes(h.kv, h.bmap, 64, op) > 0
+    # the fused call's workspace: the select workspace, then the decode workspace
+    assert A.abs_workspace_bytes(h.kv, h.bmap, 64, A.ABS_OP_SELECT_DECODE) == (
+        A.abs_workspace_bytes(h.kv, h.bmap, 64, A.ABS_OP_SELECT) + A.abs_workspace_bytes(h.kv, h.bmap, 64,
+                                                                                          A.ABS_OP_DECODE))
     cap = A.abs_centroid_offsets_capacity(h.kv, h.bmap, 400)
     np.testing.assert_array_equal(cap, oracle_mod.csr_offsets(h.sl, h.bs, capacity_tokens=400))
     assert status_of(lambda: A.abs_centroid_offsets_capacity(h.kv, h.bmap, 299)) == A.ABS_ERR_INVALID_ARG
@@ -160,6 +164,17 @@ def test_call_level_validation():
                                                 need_s, 0)) == I
     assert status_of(lambda: A.abs_sparse_decode(h.kv, h.bmap, FAKE, FAKE, cap, FAKE, 64, float("nan"), FAKE,
                                                  None, FAKE, need_d, 0)) == I
+    need_sd = A.abs_workspace_bytes(h.kv, h.bmap, 64, A.ABS_OP_SELECT_DECODE)
+    assert status_of(lambda: A.abs_select_decode(h.kv, h.bmap, h.cents, FAKE, 64, 0.125, FAKE, cap, FAKE, FAKE,
+                                                 None, FAKE, need_sd - 1, 0)) == W
+    assert status_of(lambda: A.abs_select_decode(h.kv, h.bmap, h.cents, FAKE, 64, 0.125, FAKE, cap - 1, FAKE,
+                                                 FAKE, None, FAKE, need_sd, 0)) == I
+    assert status_of(lambda: A.abs_select_decode(h.kv, h.bmap, h.cents, FAKE, 64, 0.125, FAKE, cap, FAKE, None,
+                                                 None, FAKE, need_sd, 0)) == I
+    assert status_of(lambda: A.abs_select_decode(h.kv, h.bmap, h.cents, FAKE, 64, float("inf"), FAKE, cap, FAKE,
+                                                 FAKE, None, FAKE, need_sd, 0)) == I
+    assert status_of(lambda: A.abs_select_decode(h.kv, h.bmap, h.cents, None, 64, 0.125, FAKE, cap, FAKE, FAKE,
+                                                 None, FAKE, need_sd, 0)) == I
     assert status_of(lambda: A.abs_update_centroids(h.kv, h.bmap, h.cents, -1, None, 0)) == I
     assert status_of(lambda: A.abs_update_centroids(h.kv, h.bmap, A.abs_centroids(codes=FAKE, scale=None, lo=FAKE),
                                                     1, None, 0)) == I
