@@ -1,7 +1,9 @@
 // One decode step through the C ABI from a plain host program (no Python,
 // no torch): HIP runtime allocations, the descriptors of abs.h, centroid
-// build, score + select, sparse decode.  Inputs come from raw files written
-// by the test (fp32 caches), outputs go to raw files it compares.
+// build, score + select, sparse decode; then the same step through
+// abs_select_decode, which must give the same bytes (exit status 1 if not).
+// Inputs come from raw files written by the test (fp32 caches), outputs go
+// to raw files it compares.
 //
 //   decode_step DIR B HQ HKV D MAXPAGES NPAGES BUDGET BS_0 .. BS_{HKV-1}
 //
@@ -12,6 +14,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <cstring>
 #include <cstdlib>
 #include <string>
 #include <vector>
@@ -127,10 +130,10 @@ int main(int argc, char** argv) {
     HIP_OK(hipMalloc((void**)&cents.scale, (size_t)B * Hkv * D * sizeof(float)));
     HIP_OK(hipMalloc((void**)&cents.lo, (size_t)B * Hkv * D * sizeof(float)));
 
-    size_t ws_bytes[3];
-    for (int op = 0; op < 3; ++op) ABS_OK_(abs_workspace_bytes(&kv, &map, budget, (abs_op)op, &ws_bytes[op]));
-    void* ws[3];
-    for (int op = 0; op < 3; ++op) {
+    size_t ws_bytes[4];
+    for (int op = 0; op < 4; ++op) ABS_OK_(abs_workspace_bytes(&kv, &map, budget, (abs_op)op, &ws_bytes[op]));
+    void* ws[4];
+    for (int op = 0; op < 4; ++op) {
         HIP_OK(hipMalloc(&ws[op], ws_bytes[op] ? ws_bytes[op] : 256));
         HIP_OK(hipMemset(ws[op], 0, ws_bytes[op] ? ws_bytes[op] : 256));   // the decode workspace starts zeroed
     }
@@ -160,6 +163,35 @@ int main(int argc, char** argv) {
     HIP_OK(hipMemcpy(cnt.data(), dcnt, cnt.size() * sizeof(int32_t), hipMemcpyDeviceToHost));
     HIP_OK(hipMemcpy(out.data(), dout, out.size() * sizeof(float), hipMemcpyDeviceToHost));
     HIP_OK(hipMemcpy(lse.data(), dlse, lse.size() * sizeof(float), hipMemcpyDeviceToHost));
+
+    // the same step through abs_select_decode, into fresh outputs: it must
+    // give the same bytes
+    int32_t *dsel2 = nullptr, *dcnt2 = nullptr;
+    float *dout2 = nullptr, *dlse2 = nullptr;
+    HIP_OK(hipMalloc((void**)&dsel2, sel.size() * sizeof(int32_t)));
+    HIP_OK(hipMemset(dsel2, 0xFF, sel.size() * sizeof(int32_t)));
+    HIP_OK(hipMalloc((void**)&dcnt2, cnt.size() * sizeof(int32_t)));
+    HIP_OK(hipMalloc((void**)&dout2, out.size() * sizeof(float)));
+    HIP_OK(hipMalloc((void**)&dlse2, lse.size() * sizeof(float)));
+    ABS_OK_(abs_select_decode(&kv, &map, &cents, dq, budget, sm_scale, dsel2, sel_cap, dcnt2, dout2, dlse2,
+                              ws[ABS_OP_SELECT_DECODE], ws_bytes[ABS_OP_SELECT_DECODE], stream));
+    HIP_OK(hipStreamSynchronize(stream));
+    std::vector<int32_t> sel2(sel.size()), cnt2(cnt.size());
+    std::vector<float> out2(out.size()), lse2(lse.size());
+    HIP_OK(hipMemcpy(sel2.data(), dsel2, sel2.size() * sizeof(int32_t), hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(cnt2.data(), dcnt2, cnt2.size() * sizeof(int32_t), hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(out2.data(), dout2, out2.size() * sizeof(float), hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(lse2.data(), dlse2, lse2.size() * sizeof(float), hipMemcpyDeviceToHost));
+    bool same = cnt2 == cnt && std::memcmp(out2.data(), out.data(), out.size() * sizeof(float)) == 0 &&
+                std::memcmp(lse2.data(), lse.data(), lse.size() * sizeof(float)) == 0;
+    for (size_t r = 0; same && r < cnt.size(); ++r)
+        same = std::memcmp(&sel2[r * sel_cap], &sel[r * sel_cap], (size_t)cnt[r] * sizeof(int32_t)) == 0;
+    if (!same) {
+        std::fprintf(stderr, "abs_select_decode differs from abs_score_select + abs_sparse_decode\n");
+        return 1;
+    }
+    for (void* p : {(void*)dsel2, (void*)dcnt2, (void*)dout2, (void*)dlse2}) HIP_OK(hipFree(p));
+
     if (!write_file(dir + "/sel.bin", sel) || !write_file(dir + "/count.bin", cnt) ||
         !write_file(dir + "/out.bin", out) || !write_file(dir + "/lse.bin", lse))
         return 1;
@@ -167,7 +199,7 @@ int main(int argc, char** argv) {
 
     HIP_OK(hipStreamDestroy(stream));
     for (void* p : {(void*)dk, (void*)dv, (void*)dq, (void*)dpt, (void*)dlens, (void*)dbs, (void*)doff,
-                    (void*)cents.codes, (void*)cents.scale, (void*)cents.lo, ws[0], ws[1], ws[2], (void*)dsel,
+                    (void*)cents.codes, (void*)cents.scale, (void*)cents.lo, ws[0], ws[1], ws[2], ws[3], (void*)dsel,
                     (void*)dcnt, (void*)dout, (void*)dlse})
         HIP_OK(hipFree(p));
     return 0;
