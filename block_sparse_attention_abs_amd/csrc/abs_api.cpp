@@ -223,6 +223,7 @@ void fill_select_args(const Plan& p, const abs_paged_kv* kv, const abs_block_map
     a->budget = token_budget;
     a->max_n = p.max_n;
     a->max_len = p.max_len;
+    a->total_blocks = p.total_blocks;
     // the exact list of score tiles, when it fits the kernel arguments
     a->ntiles = 0;
     for (int b = 0; b < p.g.B; ++b)

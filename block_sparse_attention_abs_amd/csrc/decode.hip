@@ -927,14 +927,17 @@ hipError_t launch_decode(const Geom& g, DType dt, const DecodeArgs& a, hipStream
 
 // The fused form covers the layers the wavefront-split decode serves (the
 // same conditions as in decode_gt) whose heads have at most 512 x 32 blocks,
-// and is used where it measured faster than the separate launches: heads of
-// at most 4096 blocks, or a split grid that fits the 256 compute units once
-// (beyond that, two workgroups of a compute unit each repeat their head's
-// top-K of up to 16384 keys; 128K x 16: 68.6 against 68.0 us per step).
+// and is used where it measured faster than the separate launches (every
+// split workgroup repeats its head's top-K): heads of at most 6144 blocks on
+// average, and either at most 4096 in every head or a split grid that fits
+// the 256 compute units once.  Measured against the separate launches at
+// 4 x 128K / 256K: drawn map (one head at block size 16) -1.1 / -0.7 us per
+// step, every head at 16: +0.3 / +1.7 us; 16 x 128K (512 workgroups): +0.6.
 bool select_decode_fusable(const Geom& g, DType dt, const SelectArgs& s, const DecodeArgs& a) {
     const bool served = ABS_DECODE_WAVES && ABS_DECODE_MATRIX && dt == DType::BF16 && g.D == 128 && g.G <= 4 &&
                         (a.pipelined || a.chunk == 8) && a.arrive != nullptr && s.max_n <= kFusedTopkMaxN;
-    const bool faster = s.max_n <= 4096 || (int64_t)a.splits * g.B * g.Hkv <= kComputeUnits;
+    const bool faster = s.total_blocks <= (int64_t)6144 * g.B * g.Hkv &&
+                        (s.max_n <= 4096 || (int64_t)a.splits * g.B * g.Hkv <= kComputeUnits);
     return served && faster;
 }
 

@@ -102,6 +102,7 @@ struct SelectArgs {
     int budget;
     int max_n;        // largest N_{b,h}
     int max_len;      // largest L_b
+    int64_t total_blocks;   // sum of N_{b,h}
     int ntiles;       // score tiles over all heads
     const uint32_t* tiles_host;   // their list (host, valid during the call) or null
     HeadTiles head_tiles;         // per-head cumulative tiles for the longest sequence
