@@ -1,11 +1,11 @@
 """abs_select_decode (scores, then the top-K inside the split decode launch)
 against the two separate calls and against the oracle, through the C ABI.
 
-The fused launch runs the same selection (the same top-K code, 256 threads
-per head instead of 512) and the same decode arithmetic on the same pages, so
-sel, sel_count, out and lse must equal the separate calls' bit for bit.
+The fused launch runs the same selection (the top-K launch's code, 512
+threads per head) and the same decode arithmetic on the same pages, so sel,
+sel_count, out and lse must equal the separate calls' bit for bit.
 Layers the fused launch does not serve (fp32, head_dim 64, 8-head groups,
-more than 8192 blocks in a head) run the separate launches and must give the
+16384 blocks in every head) run the separate launches and must give the
 same results too.  Against the oracle: the selection rule and the attention
 tolerances of gpu_pipeline.
 """
@@ -23,13 +23,15 @@ P = W.PRESETS
 
 
 def _case(name):
-    if name == "b2-16k":                       # 1024 blocks at most: 8 keys per thread
+    if name == "b2-16k":                       # 1024 blocks at most: 4 keys per thread
         return W.make_layer(P[2].scaled(batch=2, context=16384))
     if name == "ragged-4k":
         return W.make_layer(P[1].scaled(batch=3, context=4096, token_budget=512), seq_lens=[4096, 3001, 77])
-    if name == "b1-128k":                      # 8192 blocks in the block-size-16 head: 32 keys per thread
+    if name == "b1-128k":                      # 8192 blocks in the block-size-16 head: 16 keys per thread
         return W.make_layer(P[3].scaled(batch=1))
-    if name == "b1-64k-bs16":                  # 4096 blocks in every head: 16 keys per thread
+    if name == "b1-256k":                      # 16384 blocks in that head: 32 keys per thread
+        return W.make_layer(P[3].scaled(batch=1, context=262144))
+    if name == "b1-64k-bs16":                  # 4096 blocks in every head: 8 keys per thread
         return W.make_layer(P[1].scaled(context=65536, fixed_block_sizes=(16,) * 8))
     if name == "gqa2":
         return W.make_layer(P[1].scaled(num_q_heads=16, batch=2, context=6000), seq_lens=[6000, 2500])
@@ -42,13 +44,13 @@ def _case(name):
         return W.make_layer(P[1].scaled(head_dim=64, batch=2, context=3000))
     if name == "gqa8":
         return W.make_layer(P[1].scaled(num_q_heads=16, num_kv_heads=2, batch=2, context=3000))
-    if name == "b1-256k-bs16":                 # 16384 blocks in a head
+    if name == "b1-256k-bs16":                 # 16384 blocks in every head
         return W.make_layer(P[1].scaled(context=262144, fixed_block_sizes=(16,) * 8, token_budget=4096))
     raise KeyError(name)
 
 
-CASES = ["b2-16k", "ragged-4k", "b1-128k", "b1-64k-bs16", "gqa2", "budget-covers", "f32", "d64", "gqa8",
-         "b1-256k-bs16"]
+CASES = ["b2-16k", "ragged-4k", "b1-128k", "b1-256k", "b1-64k-bs16", "gqa2", "budget-covers", "f32", "d64",
+         "gqa8", "b1-256k-bs16"]
 
 
 def _fused(g, budget, sm, ws):
