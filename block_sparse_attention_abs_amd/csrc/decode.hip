@@ -791,12 +791,22 @@ __global__ __launch_bounds__(512) void k_select_decode_ws(Geom g, const float* _
     const int first = (split * ppw) >> sh;            // selection positions first .. first + 63 (ppw <= 64)
     __shared__ int32_t s_blk[kMaxPagesPerWg];
     int32_t* row_out = sel + (int64_t)bh * sel_cap;
-    const int K = topk_rows<kFusedThreads, KPT>(g, bh, scores + (int64_t)bh * stride, stride, max_len, budget,
-                                                [&](uint32_t p, int32_t j) {
-                                                    if (split == 0 && p < (uint32_t)sel_cap) row_out[p] = j;
-                                                    const uint32_t r = p - (uint32_t)first;
-                                                    if (r < (uint32_t)kMaxPagesPerWg) s_blk[r] = j;
-                                                });
+    auto emit = [&](uint32_t p, int32_t j) {
+        if (split == 0 && p < (uint32_t)sel_cap) row_out[p] = j;
+        const uint32_t r = p - (uint32_t)first;
+        if (r < (uint32_t)kMaxPagesPerWg) s_blk[r] = j;
+    };
+    // keys per thread for this head's longest row (up to KPT, the layer's):
+    // heads with larger blocks finish their top-K sooner
+    const float* srow = scores + (int64_t)bh * stride;
+    const int nh = ceil_div(max_len, block_size_of(g, bh % g.Hkv));
+    int K;
+    if (KPT > 4 && nh <= kFusedThreads * 4)
+        K = topk_rows<kFusedThreads, 4>(g, bh, srow, stride, max_len, budget, emit);
+    else if (KPT > 8 && nh <= kFusedThreads * 8)
+        K = topk_rows<kFusedThreads, (KPT > 8 ? 8 : KPT)>(g, bh, srow, stride, max_len, budget, emit);
+    else
+        K = topk_rows<kFusedThreads, KPT>(g, bh, srow, stride, max_len, budget, emit);
     if (split == 0 && threadIdx.x == 0) count[bh] = K;
     __syncthreads();
     const int gp = split * ppw + (int)(threadIdx.x & 63);
