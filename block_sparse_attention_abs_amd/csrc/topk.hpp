@@ -12,7 +12,8 @@
 //   2. the bin b* holding the K-th largest score, and how many scores lie in
 //      higher bins;
 //   3. the few candidates in b* are ranked exactly by (score desc, index
-//      asc), giving the threshold pair (tau_key, tau_index); if b* is crowded
+//      asc), by one wavefront when there are at most 64 of them, giving the
+//      threshold pair (tau_key, tau_index); if b* is crowded
 //      (heavy ties) an 8-bit radix select over the keys gives the same pair
 //      instead;
 //   4. keep key > tau_key, or key == tau_key and index <= tau_index; a block
@@ -205,8 +206,31 @@ __device__ __forceinline__ int topk_rows(const Geom& g, int bh, const float* __r
             }
         }
         __syncthreads();
-        const uint32_t nc = s_ncand;
-        if (nc <= (uint32_t)kCandCap) {
+        const uint32_t nc = __builtin_amdgcn_readfirstlane(s_ncand);
+        if (nc <= 64u) {
+            // the usual case, a few candidates: lane t of wavefront 0 holds
+            // candidate t and counts the ones ranked before it, reading them
+            // from the other lanes (readlane) rather than from LDS
+            if (threadIdx.x < 64) {
+                const uint32_t t = threadIdx.x;
+                const float vt = s_cand_val[min(t, nc - 1)];         // nc >= need >= 1
+                const int32_t it = s_cand_idx[min(t, nc - 1)];
+                uint32_t rank = 0;
+                for (uint32_t u = 0; u < nc; ++u) {
+                    const float vu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vt), (int)u));
+                    const int32_t iu = __builtin_amdgcn_readlane(it, (int)u);
+                    rank += (vu > vt || (vu == vt && iu < it)) ? 1u : 0u;
+                }
+                if (t < nc && rank == need - 1) {
+                    s_tau_key = __float_as_uint(vt);
+                    s_tau_idx = it;
+                }
+            }
+            __syncthreads();
+            tau_f = __uint_as_float(s_tau_key);
+            tau_idx = s_tau_idx;
+            resolved = true;
+        } else if (nc <= (uint32_t)kCandCap) {
             for (uint32_t t = threadIdx.x; t < nc; t += NT) {
                 const float vt = s_cand_val[t];
                 const int32_t it = s_cand_idx[t];
