@@ -103,7 +103,8 @@ def test_fused_equals_separate_calls_and_oracle(oracle_mod, case):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("name,context,K,n10,n5", [("few-below", 4096, 32, 10, 50), ("crowded", 4096, 32, 10, 200),
+@pytest.mark.parametrize("name,context,K,n10,n5", [("few-below", 4096, 32, 10, 50), ("edge-64", 4096, 32, 10, 64),
+                                                    ("edge-65", 4096, 32, 10, 65), ("crowded", 4096, 32, 10, 200),
                                                     ("overflow", 16384, 32, 0, 600)])
 def test_fused_ties(name, context, K, n10, n5):
     """Runs of equal scores at the threshold (the construction of

@@ -23,6 +23,8 @@ pytestmark = pytest.mark.gpu
 #       name          context  K   |a=10|  |a=5|
 CASES = [("few-below", 4096, 32, 10, 50),     # threshold bin = the a=5 group: 50 candidates, 22 kept
          ("few-all", 4096, 32, 0, 40),        # every kept block is a candidate
+         ("edge-64", 4096, 32, 10, 64),       # 64 candidates: the most one wavefront ranks
+         ("edge-65", 4096, 32, 10, 65),       # 65: ranked through LDS by the candidates' threads
          ("crowded", 4096, 32, 10, 200),      # 200 candidates
          ("overflow", 16384, 32, 0, 600)]     # more than the candidate list holds: radix select
 
@@ -74,6 +76,10 @@ def test_threshold_ties(oracle_mod, name, context, K, n10, n5, dtype):
             assert len(np.unique(sc[s5])) == 1 and sc[s5].min() > sc[rest].max()
             if len(s10):
                 assert len(np.unique(sc[s10])) == 1 and sc[s10].min() > sc[s5].max()
+            if name.startswith("edge"):
+                # the a = 5 group alone fills the threshold bin: every other
+                # score lies more than two of the 2048 bin widths below it
+                assert sc[s5].min() - sc[rest].max() > 2 * (sc.max() - sc.min()) / 2048
             want = np.sort(np.concatenate([s10, s5[:K - len(s10)]]))
             assert r.count[b, h] == K
             np.testing.assert_array_equal(r.sel[b, h, :K], want)
