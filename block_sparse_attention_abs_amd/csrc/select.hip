@@ -83,7 +83,12 @@ __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restr
     // bf16 centroids are values already: w_d = qbar_d, z_d = 0.  Every thread
     // writes its slot (those past D are never read), so no branch holds the
     // loads above back.
-    __shared__ double w[NT], z[NT];
+    // one padding slot after each lane's CPL channels: the LPB lanes of a
+    // row, which read the same n-th channel of their own runs, then hit
+    // different LDS banks (unpadded, their addresses are 256 B apart for
+    // INT4 and conflict)
+    constexpr int CS = CPL + 1;
+    __shared__ double w[NT + NT / CPL], z[NT + NT / CPL];
     {
         // the group's G heads count, the padding slots (G < GT) add +0; the
         // mask is opaque to the optimizer, which would otherwise move a
@@ -95,8 +100,9 @@ __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restr
             asm volatile("" : "+v"(keep));
             qbar += (double)__uint_as_float(__float_as_uint(qv[gg]) & keep);
         }
-        w[threadIdx.x] = BITS == 16 ? qbar : qbar * (double)sc;
-        z[threadIdx.x] = BITS == 16 ? 0.0 : qbar * (double)zp;
+        const int slot = threadIdx.x + threadIdx.x / CPL;
+        w[slot] = BITS == 16 ? qbar : qbar * (double)sc;
+        z[slot] = BITS == 16 ? 0.0 : qbar * (double)zp;
     }
     __syncthreads();
 
@@ -106,8 +112,8 @@ __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restr
     double wr[CPL], c0 = 0.0;
 #pragma unroll
     for (int n = 0; n < CPL; ++n) {
-        wr[n] = w[sub * CPL + n];
-        if constexpr (BITS != 16) c0 += z[sub * CPL + n];
+        wr[n] = w[sub * CS + n];
+        if constexpr (BITS != 16) c0 += z[sub * CS + n];
     }
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
