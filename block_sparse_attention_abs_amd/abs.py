@@ -30,6 +30,7 @@ CENTROID_FORMATS = {"int4": 0, "int4_sym": 1, "int8": 2, "int4_tensor": 3, "bf16
 EXPORTS = ("abs_status_str", "abs_last_error", "abs_total_blocks", "abs_centroid_offsets",
            "abs_centroid_offsets_capacity", "abs_centroid_row_bytes", "abs_select_capacity", "abs_workspace_bytes", "abs_build_centroids",
            "abs_update_centroids", "abs_score_select", "abs_sparse_decode", "abs_select_decode",
+           "abs_describe_launch", "abs_reset_workspace", "abs_set_debug_checks",
            "abs_head_recall", "abs_assign_block_sizes")
 
 
@@ -48,6 +49,13 @@ class abs_block_map(C.Structure):
 class abs_centroids(C.Structure):
     _fields_ = [("codes", C.c_void_p), ("scale", C.c_void_p), ("lo", C.c_void_p), ("format", C.c_int32),
                 ("reserved0", C.c_int32)]
+
+
+class abs_launch_plan(C.Structure):
+    _fields_ = [("splits", C.c_int32), ("pages_per_wg", C.c_int32), ("chunk", C.c_int32),
+                ("pipelined", C.c_int32), ("fused", C.c_int32), ("score_workgroups", C.c_int32),
+                ("max_blocks", C.c_int32), ("sel_cap", C.c_int32), ("compute_units", C.c_int32),
+                ("reserved", C.c_int32 * 7)]
 
 
 class AbsError(RuntimeError):
@@ -94,6 +102,12 @@ def lib():
         L.abs_sparse_decode.argtypes = [KV, MAP, P, P, i32, P, i32, C.c_float, P, P, P, C.c_size_t, P]
         L.abs_select_decode.restype = st
         L.abs_select_decode.argtypes = [KV, MAP, CEN, P, i32, C.c_float, P, i32, P, P, P, P, C.c_size_t, P]
+        L.abs_describe_launch.restype = st
+        L.abs_describe_launch.argtypes = [KV, MAP, i32, C.POINTER(abs_launch_plan)]
+        L.abs_reset_workspace.restype = st
+        L.abs_reset_workspace.argtypes = [KV, MAP, i32, st, P, C.c_size_t, P]
+        L.abs_set_debug_checks.restype = i32
+        L.abs_set_debug_checks.argtypes = [i32]
         L.abs_head_recall.restype = st
         L.abs_head_recall.argtypes = [KV, P, P, P, P]
         L.abs_assign_block_sizes.restype = st
@@ -186,6 +200,22 @@ def abs_select_decode(kv, bmap, cents, q_ptr: int, token_budget: int, sm_scale: 
     _check(lib().abs_select_decode(C.byref(kv), C.byref(bmap), C.byref(cents), q_ptr, token_budget, sm_scale,
                                    sel_ptr, sel_cap, count_ptr, out_ptr, lse_ptr, ws_ptr, ws_bytes, stream),
            "abs_select_decode")
+
+
+def abs_describe_launch(kv, bmap, token_budget: int) -> dict:
+    plan = abs_launch_plan()
+    _check(lib().abs_describe_launch(C.byref(kv), C.byref(bmap), token_budget, C.byref(plan)),
+           "abs_describe_launch")
+    return {f: int(getattr(plan, f)) for f, _ in abs_launch_plan._fields_ if f != "reserved"}
+
+
+def abs_reset_workspace(kv, bmap, token_budget: int, op: int, ws_ptr: int, ws_bytes: int, stream: int) -> None:
+    _check(lib().abs_reset_workspace(C.byref(kv), C.byref(bmap), token_budget, op, ws_ptr, ws_bytes, stream),
+           "abs_reset_workspace")
+
+
+def abs_set_debug_checks(enable: bool) -> bool:
+    return bool(lib().abs_set_debug_checks(1 if enable else 0))
 
 
 def abs_head_recall(kv, lse_sel_ptr: int, lse_full_ptr: int, recall_ptr: int, stream: int) -> None:
@@ -305,6 +335,9 @@ class PagedKV:
     def workspace_bytes(self, budget: int, op: int) -> int:
         return abs_workspace_bytes(self.kv, self.bmap, budget, op)
 
+    def launch_plan(self, budget: int) -> dict:
+        return abs_describe_launch(self.kv, self.bmap, budget)
+
 
 @dataclass
 class Centroids:
@@ -376,7 +409,7 @@ def sparse_decode(kv: PagedKV, q, sel, count, budget: int, sm_scale: float, out,
 def select_decode(kv: PagedKV, cents: Centroids, q, budget: int, sm_scale: float, sel, count, out, lse=None,
                   ws=None, stream: Optional[int] = None) -> None:
     """score_select then sparse_decode through abs_select_decode (fewer launches).
-    A workspace passed in must have been zero-filled before its first use."""
+    The call zero-fills the decode's arrival counters itself."""
     need = kv.workspace_bytes(budget, ABS_OP_SELECT_DECODE)
     ws = workspace(need, kv.k_cache.device) if ws is None else ws
     abs_select_decode(kv.kv, kv.bmap, cents.desc, _ptr(q), budget, sm_scale, _ptr(sel), int(sel.shape[-1]),

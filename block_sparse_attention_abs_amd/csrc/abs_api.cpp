@@ -5,13 +5,16 @@
 // K_{b,h} = min(N, max(1, floor(budget / bs_h))), the CSR centroid offsets,
 // the page count each head reads), carves the caller's workspace, sizes the
 // grids, and enqueues the kernels on the caller's stream.  It never
-// allocates, frees or synchronizes, and nothing is read back from the device.
+// allocates, frees or synchronizes, and nothing is read back from the device
+// (except with the debug checks on, abs_set_debug_checks).
 #include "abs.h"
 
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
+#include <vector>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -35,6 +38,30 @@ abs_status ok() {
     g_err[0] = '\0';
     return ABS_OK;
 }
+
+// Compute units of the current device, read once per device (256 on an
+// MI355X; fewer on a partitioned one).  Without a device (host-only use of
+// the sizing calls) the MI355X figure is assumed.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+int device_compute_units() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    int n = g_cus[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
+        (void)hipGetLastError();
+        n = 256;
+    }
+    g_cus[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+std::atomic<int> g_debug_checks{0};
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -113,6 +140,7 @@ abs_status check_geometry(const abs_paged_kv* kv, const abs_block_map* map, Plan
     p->max_n = 0;
     p->max_len = 0;
     for (int b = 0; b < g.B; ++b) p->max_len = std::max(p->max_len, kv->seq_lens_host[b]);
+    g.max_len = p->max_len;
     for (int b = 0; b < g.B; ++b)
         for (int h = 0; h < g.Hkv; ++h) {
             const int64_t n = ceil_div64(kv->seq_lens_host[b], map->block_size_host[h]);
@@ -142,8 +170,39 @@ abs_status require_device(const Plan& p, bool need_v) {
     if (g.k == nullptr || (need_v && g.v == nullptr)) return fail(ABS_ERR_INVALID_ARG, "null cache pointer");
     if (g.page_table == nullptr || g.seq_lens == nullptr)
         return fail(ABS_ERR_INVALID_ARG, "null page_table or seq_lens");
-    if (p.block_size_dev == nullptr || g.off == nullptr)
-        return fail(ABS_ERR_INVALID_ARG, "null block_size or centroid_off");
+    if (g.off == nullptr) return fail(ABS_ERR_INVALID_ARG, "null centroid_off");
+    return ok();
+}
+
+// Debug checks (abs_set_debug_checks): read the device copies back and compare
+// them with what the host sized the launch from.  Synchronizes the stream.
+abs_status debug_check(const Plan& p, const abs_paged_kv* kv, const abs_block_map* map, hipStream_t st) {
+    if (g_debug_checks.load(std::memory_order_relaxed) == 0) return ok();
+    const absk::Geom& g = p.g;
+    std::vector<int32_t> lens(g.B), bs(g.Hkv), pt((size_t)g.B * g.max_pages);
+    hipError_t e = hipMemcpyAsync(lens.data(), g.seq_lens, lens.size() * 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess && map->block_size != nullptr)
+        e = hipMemcpyAsync(bs.data(), map->block_size, bs.size() * 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(pt.data(), g.page_table, pt.size() * 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(ABS_ERR_HIP, "debug check read-back: %s", hipGetErrorString(e));
+    for (int b = 0; b < g.B; ++b) {
+        if (lens[b] != kv->seq_lens_host[b])
+            return fail(ABS_ERR_INVALID_ARG, "debug check: seq_lens[%d] = %d on the device, %d on the host", b,
+                        lens[b], kv->seq_lens_host[b]);
+        const int np = (kv->seq_lens_host[b] + 15) / 16;
+        for (int i = 0; i < np; ++i) {
+            const int32_t id = pt[(size_t)b * g.max_pages + i];
+            if (id < 0 || id >= g.num_pages)
+                return fail(ABS_ERR_INVALID_ARG, "debug check: page_table[%d][%d] = %d outside [0, %lld)", b, i, id,
+                            (long long)g.num_pages);
+        }
+    }
+    if (map->block_size != nullptr)
+        for (int h = 0; h < g.Hkv; ++h)
+            if (bs[h] != map->block_size_host[h])
+                return fail(ABS_ERR_INVALID_ARG, "debug check: block_size[%d] = %d on the device, %d on the host", h,
+                            bs[h], map->block_size_host[h]);
     return ok();
 }
 
@@ -172,7 +231,7 @@ size_t select_bytes(const Plan& p) {
 }
 
 absk::DecodeLayout decode_layout(const Plan& p) {
-    return absk::decode_layout(p.g.B, p.g.Hkv, p.g.Hq, p.g.D, p.max_pages_read);
+    return absk::decode_layout(p.g.B, p.g.Hkv, p.g.Hq, p.g.D, p.max_pages_read, device_compute_units());
 }
 
 abs_status check_centroids(const abs_centroids* c) {
@@ -224,6 +283,8 @@ void fill_select_args(const Plan& p, const abs_paged_kv* kv, const abs_block_map
     a->max_n = p.max_n;
     a->max_len = p.max_len;
     a->total_blocks = p.total_blocks;
+    a->zero_counters = nullptr;
+    a->n_zero = 0;
     // the exact list of score tiles, when it fits the kernel arguments
     a->ntiles = 0;
     for (int b = 0; b < p.g.B; ++b)
@@ -260,6 +321,7 @@ void fill_decode_args(const absk::DecodeLayout& l, const void* q, const int32_t*
     a->chunk = l.chunk;
     a->pipelined = l.pipelined;
     a->splits = l.splits;
+    a->compute_units = device_compute_units();
 }
 
 }  // namespace
@@ -378,6 +440,7 @@ abs_status abs_build_centroids(const abs_paged_kv* kv, const abs_block_map* map,
     a.tiles = l.tiles;
     a.stage_rows = p.max_n;
     a.fmt = out->format;
+    if (abs_status st = debug_check(p, kv, map, static_cast<hipStream_t>(stream))) return st;
     return hip_status(absk::launch_build(p.g, p.dt, a, static_cast<hipStream_t>(stream)), "build_centroids");
 }
 
@@ -395,6 +458,7 @@ abs_status abs_update_centroids(const abs_paged_kv* kv, const abs_block_map* map
     a.out_of_range = out_of_range;
     a.appended = appended;
     a.fmt = cents->format;
+    if (abs_status st = debug_check(p, kv, map, static_cast<hipStream_t>(stream))) return st;
     return hip_status(absk::launch_update(p.g, p.dt, a, static_cast<hipStream_t>(stream)), "update_centroids");
 }
 
@@ -412,6 +476,7 @@ abs_status abs_score_select(const abs_paged_kv* kv, const abs_block_map* map, co
     absk::SelectArgs a;
     uint32_t tiles[absk::kMaxScoreTiles];
     fill_select_args(p, kv, map, cents, q, token_budget, sel, sel_cap, sel_count, workspace, tiles, &a);
+    if (abs_status st = debug_check(p, kv, map, static_cast<hipStream_t>(stream))) return st;
     return hip_status(absk::launch_select(p.g, p.dt, a, static_cast<hipStream_t>(stream)), "score_select");
 }
 
@@ -431,6 +496,7 @@ abs_status abs_sparse_decode(const abs_paged_kv* kv, const abs_block_map* map, c
         return fail(ABS_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", l.bytes, workspace_bytes);
     absk::DecodeArgs a;
     fill_decode_args(l, q, sel, sel_cap, sel_count, sm_scale, out, lse, workspace, &a);
+    if (abs_status st = debug_check(p, kv, map, static_cast<hipStream_t>(stream))) return st;
     return hip_status(absk::launch_decode(p.g, p.dt, a, static_cast<hipStream_t>(stream)), "sparse_decode");
 }
 
@@ -455,7 +521,12 @@ abs_status abs_select_decode(const abs_paged_kv* kv, const abs_block_map* map, c
     fill_select_args(p, kv, map, cents, q, token_budget, sel, sel_cap, sel_count, workspace, tiles, &sa);
     absk::DecodeArgs da;
     fill_decode_args(l, q, sel, sel_cap, sel_count, sm_scale, out, lse, ws_at(workspace, sbytes), &da);
+    // the first launch zero-fills the decode's arrival counters, so the
+    // decode region needs no zero-filling by the caller
+    sa.zero_counters = da.arrive;
+    sa.n_zero = da.arrive != nullptr ? p.g.B * p.g.Hkv : 0;
     const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (abs_status e = debug_check(p, kv, map, st)) return e;
     if (absk::select_decode_fusable(p.g, p.dt, sa, da)) {
         if (abs_status e = hip_status(absk::launch_scores(p.g, p.dt, sa, st), "select_decode (scores)")) return e;
         return hip_status(absk::launch_select_decode(p.g, p.dt, sa, da, st), "select_decode");
@@ -463,6 +534,55 @@ abs_status abs_select_decode(const abs_paged_kv* kv, const abs_block_map* map, c
     if (abs_status e = hip_status(absk::launch_select(p.g, p.dt, sa, st), "select_decode (select)")) return e;
     return hip_status(absk::launch_decode(p.g, p.dt, da, st), "select_decode (decode)");
 }
+
+abs_status abs_describe_launch(const abs_paged_kv* kv, const abs_block_map* map, int32_t token_budget,
+                               abs_launch_plan* plan) {
+    if (plan == nullptr) return fail(ABS_ERR_INVALID_ARG, "null output");
+    Plan p;
+    if (abs_status st = check_geometry(kv, map, &p)) return st;
+    if (abs_status st = plan_budget(kv, map, token_budget, &p)) return st;
+    const absk::DecodeLayout l = decode_layout(p);
+    absk::SelectArgs sa{};
+    uint32_t tiles[absk::kMaxScoreTiles];
+    abs_centroids none{};
+    fill_select_args(p, kv, map, &none, nullptr, token_budget, nullptr, p.sel_cap, nullptr, nullptr, tiles, &sa);
+    absk::DecodeArgs da{};
+    // a placeholder workspace address (never dereferenced): the arrival
+    // counters' presence decides the merge form
+    void* const ws_placeholder = reinterpret_cast<void*>(uintptr_t{kAlign});
+    fill_decode_args(l, nullptr, nullptr, p.sel_cap, nullptr, 1.0f, nullptr, nullptr, ws_placeholder, &da);
+    std::memset(plan, 0, sizeof *plan);
+    plan->splits = l.splits;
+    plan->pages_per_wg = l.ppw;
+    plan->chunk = l.chunk;
+    plan->pipelined = l.pipelined ? 1 : 0;
+    plan->fused = absk::select_decode_fusable(p.g, p.dt, sa, da) ? 1 : 0;
+    plan->score_workgroups = sa.ntiles <= absk::kMaxScoreTiles ? sa.ntiles : (int32_t)(sa.head_tiles.cum[p.g.Hkv] * p.g.B);
+    plan->max_blocks = p.max_n;
+    plan->sel_cap = p.sel_cap;
+    plan->compute_units = da.compute_units;
+    return ok();
+}
+
+abs_status abs_reset_workspace(const abs_paged_kv* kv, const abs_block_map* map, int32_t token_budget, abs_op op,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    Plan p;
+    if (abs_status st = check_geometry(kv, map, &p)) return st;
+    if (abs_status st = plan_budget(kv, map, token_budget, &p)) return st;
+    if (op != ABS_OP_DECODE && op != ABS_OP_SELECT_DECODE)
+        return fail(ABS_ERR_INVALID_ARG, "op %d has no state to reset (ABS_OP_DECODE or ABS_OP_SELECT_DECODE)",
+                    (int)op);
+    const absk::DecodeLayout l = decode_layout(p);
+    const size_t at = op == ABS_OP_DECODE ? 0 : select_bytes(p);
+    if (workspace == nullptr || workspace_bytes < at + l.bytes)
+        return fail(ABS_ERR_WORKSPACE, "workspace of %zu bytes, op %d needs %zu", workspace_bytes, (int)op,
+                    at + l.bytes);
+    return hip_status(absk::launch_zero(reinterpret_cast<int32_t*>(ws_at(workspace, at + l.arrive)),
+                                        p.g.B * p.g.Hkv, static_cast<hipStream_t>(stream)),
+                      "reset_workspace");
+}
+
+int32_t abs_set_debug_checks(int32_t enable) { return g_debug_checks.exchange(enable != 0 ? 1 : 0); }
 
 abs_status abs_head_recall(const abs_paged_kv* kv, const float* lse_sel, const float* lse_full, float* recall,
                            void* stream) {

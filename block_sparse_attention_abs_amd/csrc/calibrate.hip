@@ -1,4 +1,5 @@
-// Per-head recall for the offline block-size calibration (AB-Sparse page:
+// Small service kernels: the zero fill of a decode workspace's arrival
+// counters, and the per-head recall for the offline block-size calibration (AB-Sparse page:
 // Figure 3's normalized recall against block size, and the per-head
 // block-size heatmap printed after it).
 //
@@ -29,7 +30,17 @@ __global__ __launch_bounds__(64) void k_head_recall(int B, int Hq, int Hkv, cons
     if (threadIdx.x == 0) recall[h] = (float)(acc / (double)n);
 }
 
+__global__ __launch_bounds__(256) void k_zero(int32_t* __restrict__ p, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_zero(int32_t* p, int n, hipStream_t s) {
+    if (n > 0) hipLaunchKernelGGL(k_zero, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
 
 hipError_t launch_head_recall(int B, int Hq, int Hkv, const float* lse_sel, const float* lse_full, float* recall,
                               hipStream_t s) {

@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void k_centroid_mean(Geom g, float* __restrict
     constexpr int GROUPS = 256 / kRowLanes;               // 16 blocks in flight
     const int bh = blockIdx.y;
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
-    const int L = g.seq_lens[b];
+    const int L = seq_len(g, b);
     const int bs = block_size_of(g, h);
     const int N = ceil_div(L, bs);
     const int bpt = kBuildTileTokens / bs;                // blocks per tile
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kRangeThreads) void k_centroid_range(Geom g, const 
     const int bh = blockIdx.x;
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
     const int bs = block_size_of(g, h);
-    const int nt = ceil_div(ceil_div(g.seq_lens[b], bs), kBuildTileTokens / bs);
+    const int nt = ceil_div(ceil_div(seq_len(g, b), bs), kBuildTileTokens / bs);
     const int d = threadIdx.x % D, stripe = threadIdx.x / D;
     const float* pn = pmin + (int64_t)bh * tiles * D + d;
     const float* px = pmax + (int64_t)bh * tiles * D + d;
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(256) void k_centroid_quantize(Geom g, const float* 
     const int bh = blockIdx.y;
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
     const int bs = block_size_of(g, h);
-    const int N = ceil_div(g.seq_lens[b], bs);
+    const int N = centroid_rows(g, bh, ceil_div(seq_len(g, b), bs));
     const int bpt = kBuildTileTokens / bs;
     const int j0 = blockIdx.x * bpt;
     if (j0 >= N) return;
@@ -330,10 +330,10 @@ __global__ __launch_bounds__(256) void k_centroid_update(Geom g, int appended, c
     constexpr int64_t RB = row_bytes(D, FMT);
     const int bh = blockIdx.x;
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
-    const int L = g.seq_lens[b];
+    const int L = seq_len(g, b);
     const int bs = block_size_of(g, h);
     const int ppb = bs / kPage;                           // pages per block
-    const int N = ceil_div(L, bs);
+    const int N = centroid_rows(g, bh, ceil_div(L, bs));
     const int j_first = (max(1, L - appended) - 1) / bs;
     const int64_t row0 = g.off[bh];
     const int lane = threadIdx.x & (kRowLanes - 1);

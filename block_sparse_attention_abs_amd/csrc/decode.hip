@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256 * RG, (DecodeOccupancy<T, D, GT, PIPE, MF>::val
     const int gp = p0 + wl;
     const bool in_row = wl < ppw && gp < sel_cap * spb;
     const int sv = sel[(int64_t)bh * sel_cap + min(gp >> sh, sel_cap - 1)];   // unconditional, clamped
-    const int L = g.seq_lens[b];
+    const int L = seq_len(g, b);
     const int npages = ceil_div(L, kPage);
     const int N = ceil_div(L, spb * kPage);
     const int K = min(max(count[bh], 0), sel_cap);
@@ -515,7 +515,7 @@ __device__ __forceinline__ void ws_decode(const Geom& g, const uint16_t* __restr
     const int p0 = split * ppw;                        // ppw <= 64
     const int gp = p0 + wl;
     const bool in_row = wl < ppw && gp < sel_cap * spb;
-    const int L = g.seq_lens[b];
+    const int L = seq_len(g, b);
     const int npages = ceil_div(L, kPage);
     const int N = ceil_div(L, spb * kPage);
     const int total = min(K * spb, splits * ppw);      // selected pages of (b, h)
@@ -943,11 +943,12 @@ hipError_t launch_decode(const Geom& g, DType dt, const DecodeArgs& a, hipStream
 // the 256 compute units once.  Measured against the separate launches at
 // 4 x 128K / 256K: drawn map (one head at block size 16) -1.1 / -0.7 us per
 // step, every head at 16: +0.3 / +1.7 us; 16 x 128K (512 workgroups): +0.6.
+// (The compute units are the device's, read at run time.)
 bool select_decode_fusable(const Geom& g, DType dt, const SelectArgs& s, const DecodeArgs& a) {
     const bool served = ABS_DECODE_WAVES && ABS_DECODE_MATRIX && dt == DType::BF16 && g.D == 128 && g.G <= 4 &&
                         (a.pipelined || a.chunk == 8) && a.arrive != nullptr && s.max_n <= kFusedTopkMaxN;
     const bool faster = s.total_blocks <= (int64_t)6144 * g.B * g.Hkv &&
-                        (s.max_n <= 4096 || (int64_t)a.splits * g.B * g.Hkv <= kComputeUnits);
+                        (s.max_n <= 4096 || (int64_t)a.splits * g.B * g.Hkv <= a.compute_units);
     return served && faster;
 }
 

@@ -29,8 +29,10 @@ struct DecodeLayout {
 #ifndef ABS_DECODE_MAX_CHUNK
 #define ABS_DECODE_MAX_CHUNK 8
 #endif
+// Workgroups of the double-buffered layout; 0: one per compute unit of the
+// device (read at run time).
 #ifndef ABS_DECODE_PIPE_WGS
-#define ABS_DECODE_PIPE_WGS 256
+#define ABS_DECODE_PIPE_WGS 0
 #endif
 // At most this many splits per (b, h) outside the double-buffered layout:
 // the merging workgroup reads the splits' partials 8 at a time, so a
@@ -46,8 +48,9 @@ struct DecodeLayout {
 
 // Pages per workgroup: enough workgroups to fill the chip (about
 // ABS_DECODE_TARGET_WGS) but at most kMaxPagesPerWg pages each; pages are
-// held in registers `chunk` at a time.
-inline DecodeLayout decode_layout(int B, int Hkv, int Hq, int D, int max_pages_read) {
+// held in registers `chunk` at a time.  `compute_units`: of the device the
+// launch runs on.
+inline DecodeLayout decode_layout(int B, int Hkv, int Hq, int D, int max_pages_read, int compute_units) {
     DecodeLayout l;
     const int64_t heads = (int64_t)B * Hkv;
     const int64_t maxp = std::max(max_pages_read, 1);
@@ -62,11 +65,11 @@ inline DecodeLayout decode_layout(int B, int Hkv, int Hq, int D, int max_pages_r
         l.ppw = (int)std::min<int64_t>(kMaxPagesPerWg, layout_ceil(need, l.chunk) * l.chunk);
         l.splits = (int)layout_ceil(maxp, l.ppw);
     }
-    // Enough pages for two chunks of 8 per workgroup at about
-    // ABS_DECODE_PIPE_WGS workgroups (one per compute unit): stream them
-    // double-buffered instead.
-    if (ABS_DECODE_PIPE_WGS > 0 && heads * maxp >= (int64_t)ABS_DECODE_PIPE_WGS * 16) {
-        const int64_t per = layout_ceil(heads * maxp, ABS_DECODE_PIPE_WGS);
+    // Enough pages for two chunks of 8 per workgroup at one workgroup per
+    // compute unit: stream them double-buffered instead.
+    const int64_t pipe_wgs = ABS_DECODE_PIPE_WGS > 0 ? ABS_DECODE_PIPE_WGS : std::max(1, compute_units);
+    if (heads * maxp >= pipe_wgs * 16) {
+        const int64_t per = layout_ceil(heads * maxp, pipe_wgs);
         l.chunk = 8;
         l.pipelined = true;
         l.ppw = (int)std::min<int64_t>(kMaxPagesPerWg, std::max<int64_t>(16, layout_ceil(per, 16) * 16));

@@ -15,6 +15,7 @@ namespace absk {
 constexpr int kMaxKvHeads = 64;
 struct Geom {
     int B, Hq, Hkv, D, G, max_pages;
+    int max_len;          // the longest L_b on the host: every buffer is sized from it
     int64_t num_pages;
     const void* k;
     const void* v;
@@ -23,6 +24,18 @@ struct Geom {
     const int64_t* off;
     uint64_t bs_log2[kMaxKvHeads / 32];
 };
+
+// L_b as the kernels use it: the device copy, clamped to [1, the host's
+// longest length], so that a device value that disagrees with the host's
+// (which sized every buffer and grid) cannot index past them.
+__device__ __forceinline__ int seq_len(const Geom& g, int b) { return min(max(g.seq_lens[b], 1), g.max_len); }
+
+// Centroid rows of (b, h) = bh that the kernels touch: its N blocks, capped
+// by the rows the offsets give it (so that a device length that disagrees
+// with the host's cannot index past the centroid store).
+__device__ __forceinline__ int centroid_rows(const Geom& g, int bh, int N) {
+    return (int)min((int64_t)N, g.off[bh + 1] - g.off[bh]);
+}
 
 __device__ __forceinline__ int block_size_of(const Geom& g, int h) {
     const uint64_t w = h < 32 ? g.bs_log2[0] : g.bs_log2[1];
@@ -103,6 +116,8 @@ struct SelectArgs {
     int max_n;        // largest N_{b,h}
     int max_len;      // largest L_b
     int64_t total_blocks;   // sum of N_{b,h}
+    int32_t* zero_counters;   // the score launch zero-fills these n_zero ints first (or null)
+    int n_zero;
     int ntiles;       // score tiles over all heads
     const uint32_t* tiles_host;   // their list (host, valid during the call) or null
     HeadTiles head_tiles;         // per-head cumulative tiles for the longest sequence
@@ -126,6 +141,7 @@ struct DecodeArgs {
     int chunk;        // pages held in registers at a time: 1, 2, 4 or 8
     bool pipelined;   // two chunks in flight (chunk 8, pages_per_wg a multiple of 16)
     int splits;
+    int compute_units;   // of the device the launch runs on
 };
 
 constexpr int kMaxPagesPerWg = 64;
@@ -137,12 +153,14 @@ hipError_t launch_decode(const Geom& g, DType dt, const DecodeArgs& a, hipStream
 // select_decode_fusable(); otherwise launch_select and launch_decode.
 constexpr int kFusedThreads = 512;                 // the fused launch's workgroup: the top-K launch's width
 constexpr int kFusedTopkMaxN = kFusedThreads * 32;
-constexpr int kComputeUnits = 256;                 // MI355X
 hipError_t launch_scores(const Geom& g, DType dt, const SelectArgs& a, hipStream_t s);
 bool select_decode_fusable(const Geom& g, DType dt, const SelectArgs& s, const DecodeArgs& a);
 hipError_t launch_select_decode(const Geom& g, DType dt, const SelectArgs& s, const DecodeArgs& a, hipStream_t st);
 
 // Calibration: recall[h] = mean over (b, query heads of h) of exp(lse_sel - lse_full).
+// Zero n ints at p (a fill kernel: no memset node, so it can be captured).
+hipError_t launch_zero(int32_t* p, int n, hipStream_t s);
+
 hipError_t launch_head_recall(int B, int Hq, int Hkv, const float* lse_sel, const float* lse_full, float* recall,
                               hipStream_t s);
 

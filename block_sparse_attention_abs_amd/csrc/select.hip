@@ -49,7 +49,7 @@ __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restr
     static_assert(NT >= D, "one thread per channel folds the query");
     const int b = bh / g.Hkv, h = bh - b * g.Hkv;
     const int64_t row0 = g.off[bh];
-    const int N = ceil_div(g.seq_lens[b], block_size_of(g, h));
+    const int N = centroid_rows(g, bh, ceil_div(seq_len(g, b), block_size_of(g, h)));
     const int j0 = tile * kScoreBlocksPerWg;
     const int sub = threadIdx.x % LPB;
     const int grp = threadIdx.x / LPB;
@@ -136,13 +136,20 @@ __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restr
     }
 }
 
+// The decode's arrival counters, zeroed by the first score workgroup when
+// the decode follows in the same call (zc null: nothing to do).
+__device__ __forceinline__ void zero_ints(int32_t* zc, int nz) {
+    if (zc != nullptr)
+        for (int i = threadIdx.x; i < nz; i += ABS_SCORE_NT) zc[i] = 0;
+}
+
 // Grid (tiles per sequence, B): x -> (head, tile) by a binary search of the
 // per-head cumulative tile counts (uniform, kernel-argument reads only).
 template <typename T, int D, int GT, int BITS>
 __global__ __launch_bounds__(ABS_SCORE_NT) void k_score_seq(Geom g, const uint8_t* __restrict__ codes,
                                                    const float* __restrict__ scale, const float* __restrict__ lo,
                                                    const T* __restrict__ q, float* __restrict__ scores, int stride,
-                                                   const HeadTiles ht) {
+                                                   const HeadTiles ht, int32_t* __restrict__ zc, int nz) {
     const uint32_t x = blockIdx.x;
     int hl = 0, hh = g.Hkv;                          // ht.cum[hl] <= x < ht.cum[hh]
     while (hh - hl > 1) {
@@ -152,15 +159,17 @@ __global__ __launch_bounds__(ABS_SCORE_NT) void k_score_seq(Geom g, const uint8_
     }
     score_tile<T, D, GT, BITS>(g, codes, scale, lo, q, scores, stride, (int)blockIdx.y * g.Hkv + hl,
                                (int)(x - ht.cum[hl]));
+    if (x == 0 && blockIdx.y == 0) zero_ints(zc, nz);
 }
 
 template <typename T, int D, int GT, int BITS>
 __global__ __launch_bounds__(ABS_SCORE_NT) void k_score_list(Geom g, const uint8_t* __restrict__ codes,
                                                     const float* __restrict__ scale, const float* __restrict__ lo,
                                                     const T* __restrict__ q, float* __restrict__ scores, int stride,
-                                                    const ScoreTiles tl) {
+                                                    const ScoreTiles tl, int32_t* __restrict__ zc, int nz) {
     const uint32_t e = tl.t[blockIdx.x];
     score_tile<T, D, GT, BITS>(g, codes, scale, lo, q, scores, stride, (int)(e >> 8), (int)(e & 255u));
+    if (blockIdx.x == 0) zero_ints(zc, nz);
 }
 
 // Build-time tuning: threads of the top-K workgroup.
@@ -175,7 +184,9 @@ __global__ __launch_bounds__(NT) void k_topk(Geom g, const float* __restrict__ s
     const int bh = blockIdx.x;
     int32_t* out = sel + (int64_t)bh * sel_cap;
     const int K = topk_rows<NT, KPT>(g, bh, scores + (int64_t)bh * stride, stride, max_len, budget,
-                                     [&](uint32_t p, int32_t j) { out[p] = j; });
+                                     [&](uint32_t p, int32_t j) {
+                                         if (p < (uint32_t)sel_cap) out[p] = j;
+                                     });
     if (threadIdx.x == 0) count[bh] = K;
 }
 
@@ -187,7 +198,7 @@ void launch_score(const Geom& g, const SelectArgs& a, hipStream_t s) {
         for (int i = 0; i < a.ntiles; ++i) tl.t[i] = a.tiles_host[i];
 #define ABS_SCORE(GT_)                                                                                    \
     hipLaunchKernelGGL((k_score_list<T, D, GT_, BITS>), dim3(a.ntiles), dim3(ABS_SCORE_NT), 0, s, g, a.codes, \
-                       a.scale, a.lo, q, a.scores, a.stride, tl)
+                       a.scale, a.lo, q, a.scores, a.stride, tl, a.zero_counters, a.n_zero)
         if (g.G <= 1) ABS_SCORE(1);
         else if (g.G <= 2) ABS_SCORE(2);
         else if (g.G <= 4) ABS_SCORE(4);
@@ -197,7 +208,7 @@ void launch_score(const Geom& g, const SelectArgs& a, hipStream_t s) {
         const dim3 sgrid(a.head_tiles.cum[g.Hkv], g.B);
 #define ABS_SCORE(GT_)                                                                                       \
     hipLaunchKernelGGL((k_score_seq<T, D, GT_, BITS>), sgrid, dim3(ABS_SCORE_NT), 0, s, g, a.codes, a.scale, a.lo, \
-                       q, a.scores, a.stride, a.head_tiles)
+                       q, a.scores, a.stride, a.head_tiles, a.zero_counters, a.n_zero)
         if (g.G <= 1) ABS_SCORE(1);
         else if (g.G <= 2) ABS_SCORE(2);
         else if (g.G <= 4) ABS_SCORE(4);

@@ -94,7 +94,7 @@ __device__ __forceinline__ int topk_rows(const Geom& g, int bh, const float* __r
         for (int e = 0; e < KPT; ++e) f[e] = row[min(base + e, cap - 1)];
     }
 
-    const int N = ceil_div(g.seq_lens[b], bs);
+    const int N = ceil_div(seq_len(g, b), bs);
     const int K = min(N, max(1, budget / bs));
     if (K >= N) {
         for (int j = threadIdx.x; j < N; j += NT) emit((uint32_t)j, (int32_t)j);

@@ -17,7 +17,8 @@
  * Conventions for every call:
  *   - All pointers marked "device" are HIP device memory; "host" pointers are
  *     read on the host during the call only.  The caller owns every buffer;
- *     the library never allocates, frees or synchronizes.
+ *     the library never allocates, frees or synchronizes (the debug checks of
+ *     abs_set_debug_checks, off by default, synchronize).
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
  *     default stream).  Outputs are valid once that stream reaches the point
  *     after the call.
@@ -72,7 +73,11 @@ typedef enum abs_op {
  *       Entries past a sequence's ceil(L_b / 16) pages are never read.
  *   seq_lens: device, int32 [num_seqs], L_b = cached tokens of sequence b,
  *       the current decode token included.  seq_lens_host: the same values on
- *       the host (launch sizes are computed from it; it must equal seq_lens).
+ *       the host (launch sizes and every buffer size are computed from it; it
+ *       must equal seq_lens).  The kernels clamp a device length into
+ *       [1, max_b seq_lens_host[b]], so a mismatch cannot index past a
+ *       buffer, but its results are undefined; abs_set_debug_checks(1)
+ *       makes every call compare the two (and the page ids) first.
  * Supported: page_size 16, head_dim 64 or 128, num_kv_heads <= 64,
  * num_seqs * num_kv_heads <= 65536, num_q_heads / num_kv_heads in 1..8,
  * 1 <= L_b <= max_pages_per_seq * 16.
@@ -97,10 +102,12 @@ typedef struct abs_paged_kv {
 /*
  * Block-size map of one layer (the per-head block-size heatmap printed after
  * Figure 3; static per Figure 5's text).
- *   block_size_host / block_size: host / device int32 [num_kv_heads], each in
- *       {16, 32, 64}; bs_h / 16 is the head's page stride.  The two must hold
- *       the same values; the kernels take them from the host copy
- *       (passed in the launch), the device copy must still be non-null.
+ *   block_size_host: host int32 [num_kv_heads], each in {16, 32, 64};
+ *       bs_h / 16 is the head's page stride.  The kernels take the sizes from
+ *       it (they travel in the launch arguments).
+ *   block_size: device int32 [num_kv_heads] or NULL.  The kernels never read
+ *       it; when given, the debug checks (abs_set_debug_checks) compare it
+ *       with block_size_host.
  *   centroid_off: device int64 [num_seqs * num_kv_heads + 1]; the first
  *       centroid row of (b, h) is centroid_off[b * num_kv_heads + h], with
  *       N_{b,h} = ceil(L_b / bs_h) rows.  Fill it with abs_centroid_offsets().
@@ -267,10 +274,13 @@ abs_status abs_score_select(const abs_paged_kv *kv, const abs_block_map *map,
  *   out: device [num_seqs][num_q_heads][head_dim] in kv_dtype.
  *   lse: device f32 [num_seqs][num_q_heads], natural log; may be NULL.
  *   workspace: >= abs_workspace_bytes(ABS_OP_DECODE) bytes: per-(b, h)
- *       arrival counters, then fp32 partials.  It must be zero-filled before
- *       its first use; every completed call leaves the counters at zero, so a
- *       workspace keeps working as long as nothing else writes to it.  Calls
- *       that share a workspace must not overlap in time.
+ *       arrival counters, then fp32 partials.  The counters must be zero
+ *       before the call: zero-fill the workspace before its first use, or
+ *       call abs_reset_workspace(ABS_OP_DECODE).  Every completed call leaves
+ *       them at zero, so a workspace keeps working as long as nothing else
+ *       writes to it; after a call that did not complete (an error on the
+ *       stream), reset it.  Calls that share a workspace must not overlap in
+ *       time.
  */
 abs_status abs_sparse_decode(const abs_paged_kv *kv, const abs_block_map *map, const void *q,
                              const int32_t *sel, int32_t sel_cap, const int32_t *sel_count,
@@ -287,18 +297,65 @@ abs_status abs_sparse_decode(const abs_paged_kv *kv, const abs_block_map *map, c
  * fused launch serves bf16 caches with head_dim 128 and up to 4 query heads
  * per KV head, where it measured faster than the separate launches: at most
  * 6144 blocks per head on average, and either at most 4096 in every head or
- * a split grid within the GPU's 256 compute units (up to 16384 per head).
+ * a split grid within the device's compute units (up to 16384 per head).
  * Other layers run the two calls' launches, with the same results.
  *   Arguments: as abs_score_select and abs_sparse_decode (token_budget is
  *   both the selection budget and the decode's).
  *   workspace: >= abs_workspace_bytes(ABS_OP_SELECT_DECODE) bytes: the select
  *       workspace (abs_workspace_bytes(ABS_OP_SELECT) bytes), then the
- *       decode workspace, whose zero-filling rule applies to this region.
+ *       decode workspace.  No zero-filling is needed: the first launch of
+ *       the call zero-fills the decode's arrival counters.  Calls that share
+ *       a workspace must not overlap in time.
+ * abs_describe_launch() reports which form a layer gets and its launch shape.
  */
 abs_status abs_select_decode(const abs_paged_kv *kv, const abs_block_map *map, const abs_centroids *cents,
                              const void *q, int32_t token_budget, float sm_scale, int32_t *sel,
                              int32_t sel_cap, int32_t *sel_count, void *out, float *lse, void *workspace,
                              size_t workspace_bytes, void *stream);
+
+/*
+ * Launch shape of abs_select_decode / abs_sparse_decode for these
+ * descriptors and budget on the current device (host only; nothing is
+ * enqueued).  The decode splits each (b, h)'s selected pages over `splits`
+ * workgroups of at most `pages_per_wg` pages (the page-level work unit of the
+ * mapping figure after Figure 8: every head reads budget / 16 pages).
+ */
+typedef struct abs_launch_plan {
+    int32_t splits;            /* split workgroups per (b, h) */
+    int32_t pages_per_wg;      /* selected pages one split workgroup reads */
+    int32_t chunk;             /* pages in registers at a time (1, 2, 4 or 8) */
+    int32_t pipelined;         /* 1: the double-buffered layout */
+    int32_t fused;             /* 1: abs_select_decode runs the top-K inside the decode launch */
+    int32_t score_workgroups;  /* workgroups of the score launch */
+    int32_t max_blocks;        /* largest N_{b,h} */
+    int32_t sel_cap;           /* largest K_{b,h} */
+    int32_t compute_units;     /* of the current device, as the library sized the launch for */
+    int32_t reserved[7];
+} abs_launch_plan;
+
+abs_status abs_describe_launch(const abs_paged_kv *kv, const abs_block_map *map, int32_t token_budget,
+                               abs_launch_plan *plan);
+
+/*
+ * Zero-fill the arrival counters of a decode workspace (op = ABS_OP_DECODE:
+ * a workspace of abs_sparse_decode; ABS_OP_SELECT_DECODE: of
+ * abs_select_decode), enqueued on `stream` as one small kernel (no memset, so
+ * it can be captured in a graph).  Needed before the first abs_sparse_decode
+ * on a workspace that was not zero-filled, and after a call that did not
+ * complete.  ABS_ERR_WORKSPACE if the workspace is smaller than op needs.
+ */
+abs_status abs_reset_workspace(const abs_paged_kv *kv, const abs_block_map *map, int32_t token_budget, abs_op op,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Debug checks, off by default (process-wide; returns the previous setting).
+ * When on, every call that enqueues work first reads back the device
+ * seq_lens, the page-table entries of each sequence's pages and (when given)
+ * the device block sizes, synchronizing the stream, and returns
+ * ABS_ERR_INVALID_ARG, enqueuing nothing, if a length or block size differs
+ * from its host copy or a page id lies outside [0, num_pages).
+ */
+int32_t abs_set_debug_checks(int32_t enable);
 
 /*
  * Offline block-size calibration (Figure 3 of the page: per-head recall at

@@ -1,7 +1,8 @@
 /*
  * The host-side calls of abs.h used from plain C (no Python, no GPU): block
  * geometry, centroid offsets, selection capacity, workspace sizes, row
- * bytes, the block-size rule, and the documented error statuses.  Device
+ * bytes, the launch plan, the debug-check switch, the block-size rule, and
+ * the documented error statuses.  Device
  * pointers are placeholders; none of these calls dereferences them.
  * Prints one "name value..." line per result for the test to compare.
  */
@@ -64,6 +65,14 @@ int main(void) {
     for (int f = 0; f < 5; ++f) CHECK(abs_centroid_row_bytes(128, f, &rb[f]));
     printf("row_bytes %lld %lld %lld %lld %lld\n", (long long)rb[0], (long long)rb[1], (long long)rb[2],
            (long long)rb[3], (long long)rb[4]);
+
+    abs_launch_plan plan;
+    CHECK(abs_describe_launch(&kv, &map, 100, &plan));
+    printf("plan %d %d %d %d %d %d %d %d\n", plan.splits, plan.pages_per_wg, plan.chunk, plan.pipelined, plan.fused,
+           plan.score_workgroups, plan.max_blocks, plan.sel_cap);
+    const int32_t was_on = abs_set_debug_checks(1);
+    const int32_t now_on = abs_set_debug_checks(0);
+    printf("debug_checks %d %d\n", was_on, now_on);
 
     const float recall[3 * 3] = {0.8f, 0.8f, 0.5f, 0.79f, 0.5f, 0.5f, 0.5f, 0.4f, 0.5f};
     int32_t map_out[3];

@@ -149,5 +149,12 @@ def check_attention(out, lse, ref_out, ref_lse, dtype):
     return float(err.max()), float(err.mean())
 
 
+def attention_vs_own_selection(out, ref) -> str:
+    """Max and mean |out - oracle output over the oracle's own selection|
+    (reported, not asserted: a tie-band swap legitimately moves it)."""
+    d = np.abs(np.asarray(out, dtype=np.float64) - ref.out)
+    return f"max {d.max():.2e} mean {d.mean():.2e}"
+
+
 def oracle_quant_from_gpu(oracle_mod, g: GpuResult):
     return oracle_mod.Quantized(g.codes, g.scale, g.lo)

@@ -25,7 +25,7 @@ def header_functions():
 
 def test_exports_every_declared_call():
     names = header_functions()
-    assert len(names) == 15
+    assert len(names) == 18
     assert sorted(A.EXPORTS) == names
     L = A.lib()
     for n in names:
@@ -255,6 +255,51 @@ def test_too_many_blocks_per_head_is_unsupported():
                                                 0)) == A.ABS_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("cfg,splits,ppw,pipelined", [(1, 16, 8, 0), (2, 2, 64, 1), (3, 8, 32, 1), (4, 4, 32, 1)])
+def test_launch_plan_of_the_workloads(cfg, splits, ppw, pipelined):
+    """The launch shapes abs_select_decode takes for the 8B-shaped decode
+    workloads (host sizing only: no GPU here, so the MI355X's 256 compute
+    units are assumed): every one runs the top-K inside the decode launch."""
+    from block_sparse_attention_abs_amd import workload as W
+    w = W.PRESETS[cfg]
+    bs = W.block_sizes_for(w, 0)
+    h = Host(seq_lens=(w.context,) * w.batch, block_size=tuple(int(b) for b in bs), Hq=w.num_q_heads,
+             D=w.head_dim, max_pages=w.context // 16)
+    plan = A.abs_describe_launch(h.kv, h.bmap, w.token_budget)
+    assert (plan["splits"], plan["pages_per_wg"], plan["pipelined"], plan["fused"]) == (splits, ppw, pipelined, 1)
+    assert plan["chunk"] == 8 and plan["compute_units"] == 256
+    assert plan["sel_cap"] == A.abs_select_capacity(h.kv, h.bmap, w.token_budget)
+    assert plan["max_blocks"] == max(-(-w.context // int(b)) for b in bs)
+    # every head reads budget / 16 pages, and the splits cover them
+    assert splits * ppw >= w.token_budget // 16
+
+
+def test_reset_and_debug_switch_validation():
+    h = Host()
+    need_d = A.abs_workspace_bytes(h.kv, h.bmap, 64, A.ABS_OP_DECODE)
+    need_sd = A.abs_workspace_bytes(h.kv, h.bmap, 64, A.ABS_OP_SELECT_DECODE)
+    W, I = A.ABS_ERR_WORKSPACE, A.ABS_ERR_INVALID_ARG
+    assert status_of(lambda: A.abs_reset_workspace(h.kv, h.bmap, 64, A.ABS_OP_DECODE, FAKE, need_d - 1, 0)) == W
+    assert status_of(lambda: A.abs_reset_workspace(h.kv, h.bmap, 64, A.ABS_OP_SELECT_DECODE, FAKE, need_sd - 1,
+                                                   0)) == W
+    assert status_of(lambda: A.abs_reset_workspace(h.kv, h.bmap, 64, A.ABS_OP_SELECT_DECODE, None, need_sd, 0)) == W
+    for op in (A.ABS_OP_BUILD, A.ABS_OP_SELECT, 9):
+        assert status_of(lambda: A.abs_reset_workspace(h.kv, h.bmap, 64, op, FAKE, 1 << 30, 0)) == I
+    assert status_of(lambda: A.abs_reset_workspace(h.kv, h.bmap, 0, A.ABS_OP_DECODE, FAKE, 1 << 30, 0)) == I
+    assert A.abs_set_debug_checks(True) is False
+    assert A.abs_set_debug_checks(False) is True
+    assert A.abs_set_debug_checks(False) is False
+
+
+def test_device_block_size_copy_is_optional():
+    """The kernels take block sizes from the host copy; a NULL device copy is
+    accepted (the validation that follows is the workspace size)."""
+    h = Host()
+    h.bmap.block_size = None
+    need_b = A.abs_workspace_bytes(h.kv, h.bmap, 64, A.ABS_OP_BUILD)
+    assert status_of(lambda: A.abs_build_centroids(h.kv, h.bmap, h.cents, FAKE, need_b - 1, 0)) == A.ABS_ERR_WORKSPACE
+
+
 def test_status_strings():
     assert A.abs_status_str(A.ABS_OK) == "ok"
     assert A.abs_status_str(A.ABS_ERR_WORKSPACE) == "workspace too small"
@@ -283,6 +328,10 @@ def test_host_calls_from_plain_c(tmp_path):
     assert [int(v) for v in got["workspace"]] == [A.abs_workspace_bytes(h.kv, h.bmap, 100, op) for op in range(3)]
     assert [int(v) for v in got["row_bytes"]] == [64, 64, 128, 64, 256]
     assert [int(v) for v in got["assign"]] == [32, 16, 64]
+    plan = A.abs_describe_launch(h.kv, h.bmap, 100)
+    assert [int(v) for v in got["plan"]] == [plan[k] for k in ("splits", "pages_per_wg", "chunk", "pipelined",
+                                                               "fused", "score_workgroups", "max_blocks", "sel_cap")]
+    assert got["debug_checks"] == ["0", "1"]
     assert int(got["status_page_size"][0]) == A.ABS_ERR_UNSUPPORTED
     assert int(got["status_block_size"][0]) == A.ABS_ERR_UNSUPPORTED
     assert int(got["status_capacity"][0]) == A.ABS_ERR_INVALID_ARG

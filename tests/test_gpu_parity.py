@@ -13,7 +13,8 @@ import pytest
 import torch
 
 from block_sparse_attention_abs_amd import workload as W
-from gpu_pipeline import GpuLayer, check_attention, check_selection, default_scale, oracle_quant_from_gpu
+from gpu_pipeline import (GpuLayer, attention_vs_own_selection, check_attention, check_selection, default_scale,
+                          oracle_quant_from_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -86,11 +87,20 @@ def test_decode_stage(runs, oracle_mod, case):
 
 @pytest.mark.parametrize("case", CASES)
 def test_end_to_end(runs, oracle_mod, case):
+    """The oracle from the raw inputs: selections under the tie-band rule,
+    outputs against the oracle run over the GPU's selection (so a legitimate
+    near-tie swap is not scored as an attention error); the difference
+    against the oracle's own selection is reported, and held to the same
+    tolerances when the two selections agree."""
     x, _, r, sm = runs(case)
     ref = oracle_mod.run(x, sm_scale=sm)
-    check_selection(oracle_mod, x, ref.quant, ref.scores, r.sel, r.count, x.workload.token_budget)
-    if np.array_equal(ref.count, r.count) and all(
-            np.array_equal(ref.sel[b, h, :k], r.sel[b, h, :k]) for (b, h), k in np.ndenumerate(ref.count)):
+    swaps = check_selection(oracle_mod, x, ref.quant, ref.scores, r.sel, r.count, x.workload.token_budget)
+    out, lse = oracle_mod.attend(x.q, x.k_cache, x.v_cache, x.page_table, x.seq_lens, x.block_size, r.sel, r.count,
+                                 sm, x.dtype)
+    check_attention(r.out, r.lse, out, lse, x.dtype)
+    own = attention_vs_own_selection(r.out, ref)
+    print(f"[gpu parity] {case}: {swaps} tie-band swaps; against the oracle's own selection {own}", flush=True)
+    if swaps == 0:
         check_attention(r.out, r.lse, ref.out, ref.lse, x.dtype)
 
 
@@ -172,17 +182,43 @@ def test_largest_head_65536_blocks(oracle_mod):
     _run_and_compare(oracle_mod, x, budget=4096)
 
 
-@pytest.mark.parametrize("cfg,layer", [(1, 0), (2, 0), (3, 0), (4, 0), (4, 35)])
+# The launch shape abs_select_decode takes for each full-size workload on an
+# MI355X (256 compute units): (splits, pages per workgroup, double-buffered).
+FULL_SIZE_PLAN = {1: (16, 8, 0), 2: (2, 64, 1), 3: (8, 32, 1), 4: (4, 32, 1)}
+
+
+@pytest.mark.parametrize("cfg,layer", [(1, 0), (2, 0), (3, 0), (4, 0), (4, 17), (4, 35)])
 def test_full_size_sampled(oracle_mod, cfg, layer):
     """Full-size workload (one layer of it) in the benchmark's launch
-    configuration; the oracle recomputes the first and last sequence on
-    their own."""
+    configuration: the separate calls, then abs_select_decode (the call the
+    benchmark times, top-K inside the decode launch), which must give the
+    same sel, sel_count, out and lse bit for bit; the oracle recomputes the
+    first and last sequence on their own."""
+    from block_sparse_attention_abs_amd import abs as A
     w = P[cfg]
     x = W.make_layer(w, layer)
     sm = default_scale(w.head_dim)
     print(f"[gpu parity] full size cfg {cfg} layer {layer}: {w.name} bs={x.block_size.tolist()}", flush=True)
     g = GpuLayer(x)
+    plan = g.kv.launch_plan(w.token_budget)
+    if plan["compute_units"] == 256:
+        assert (plan["splits"], plan["pages_per_wg"], plan["pipelined"]) == FULL_SIZE_PLAN[cfg], plan
+        assert plan["fused"] == 1, plan
     r = g.run(w.token_budget, sm)
+    B, Hq, D = x.q.shape
+    cap = g.kv.select_capacity(w.token_budget)
+    sel = torch.full((B, w.num_kv_heads, cap), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((B, w.num_kv_heads), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, Hq, D), dtype=A.torch_dtype(x.dtype), device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    A.select_decode(g.kv, g.cents, g.q, w.token_budget, sm, sel, cnt, out, lse)
+    torch.cuda.synchronize()
+    fsel, fcnt = sel.cpu().numpy(), cnt.cpu().numpy()
+    np.testing.assert_array_equal(fcnt, r.count)
+    for (b, h), k in np.ndenumerate(r.count):
+        np.testing.assert_array_equal(fsel[b, h, :k], r.sel[b, h, :k])
+    np.testing.assert_array_equal(out.float().cpu().numpy(), r.out)
+    np.testing.assert_array_equal(lse.cpu().numpy(), r.lse)
     off = g.kv.centroid_off.cpu().numpy()
     for b in sorted({0, w.batch - 1}):
         xb = dataclasses.replace(x, q=x.q[b:b + 1], page_table=x.page_table[b:b + 1], seq_lens=x.seq_lens[b:b + 1])
@@ -192,9 +228,12 @@ def test_full_size_sampled(oracle_mod, cfg, layer):
         np.testing.assert_array_equal(r.scale[b], ref.quant.scale[0])
         np.testing.assert_array_equal(r.lo[b], ref.quant.lo[0])
         check_selection(oracle_mod, xb, ref.quant, ref.scores, r.sel[b:b + 1], r.count[b:b + 1], w.token_budget)
-        out, lse = oracle_mod.attend(xb.q, x.k_cache, x.v_cache, xb.page_table, xb.seq_lens, x.block_size,
-                                     r.sel[b:b + 1], r.count[b:b + 1], sm, x.dtype)
-        check_attention(r.out[b:b + 1], r.lse[b:b + 1], out, lse, x.dtype)
+        o, l = oracle_mod.attend(xb.q, x.k_cache, x.v_cache, xb.page_table, xb.seq_lens, x.block_size,
+                                 r.sel[b:b + 1], r.count[b:b + 1], sm, x.dtype)
+        mx, mean = check_attention(r.out[b:b + 1], r.lse[b:b + 1], o, l, x.dtype)
+        own = attention_vs_own_selection(r.out[b:b + 1], ref)
+        print(f"[gpu parity] cfg {cfg} layer {layer} seq {b}: max/mean |out - oracle| {mx:.2e}/{mean:.2e}; "
+              f"against the oracle's own selection {own}", flush=True)
     del g
     torch.cuda.empty_cache()
 
