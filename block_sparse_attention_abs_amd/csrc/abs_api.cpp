@@ -500,10 +500,17 @@ abs_status abs_sparse_decode(const abs_paged_kv* kv, const abs_block_map* map, c
     return hip_status(absk::launch_decode(p.g, p.dt, a, static_cast<hipStream_t>(stream)), "sparse_decode");
 }
 
-abs_status abs_select_decode(const abs_paged_kv* kv, const abs_block_map* map, const abs_centroids* cents,
-                             const void* q, int32_t token_budget, float sm_scale, int32_t* sel, int32_t sel_cap,
-                             int32_t* sel_count, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+}  // extern "C"
+
+namespace {
+
+// abs_select_decode on the workspace `workspace` of `workspace_bytes` bytes
+// (validated here), or, with scratch_of_device, on the static scratch of the
+// current device (workspace_bytes is then its size).
+abs_status select_decode_on(const abs_paged_kv* kv, const abs_block_map* map, const abs_centroids* cents,
+                            const void* q, int32_t token_budget, float sm_scale, int32_t* sel, int32_t sel_cap,
+                            int32_t* sel_count, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                            void* stream, void* (*scratch_of_device)()) {
     Plan p;
     if (abs_status st = check_geometry(kv, map, &p)) return st;
     if (abs_status st = require_device(p, true)) return st;
@@ -513,6 +520,13 @@ abs_status abs_select_decode(const abs_paged_kv* kv, const abs_block_map* map, c
     if (!std::isfinite(sm_scale)) return fail(ABS_ERR_INVALID_ARG, "sm_scale is not finite");
     const size_t sbytes = select_bytes(p);
     const absk::DecodeLayout l = decode_layout(p);
+    if (scratch_of_device != nullptr) {
+        if (sbytes + l.bytes > workspace_bytes)
+            return fail(ABS_ERR_WORKSPACE, "this layer needs %zu scratch bytes; the static scratch holds %zu",
+                        sbytes + l.bytes, workspace_bytes);
+        workspace = scratch_of_device();
+        if (workspace == nullptr) return ABS_ERR_HIP;   // the message is set
+    }
     if (workspace == nullptr || workspace_bytes < sbytes + l.bytes)
         return fail(ABS_ERR_WORKSPACE, "select_decode needs %zu workspace bytes, got %zu", sbytes + l.bytes,
                     workspace_bytes);
@@ -533,6 +547,54 @@ abs_status abs_select_decode(const abs_paged_kv* kv, const abs_block_map* map, c
     }
     if (abs_status e = hip_status(absk::launch_select(p.g, p.dt, sa, st), "select_decode (select)")) return e;
     return hip_status(absk::launch_decode(p.g, p.dt, da, st), "select_decode (decode)");
+}
+
+// ---- the static scratch of abs_select_decode_static ------------------------
+//
+// One array per GPU, in device memory for the life of the process.  Its name
+// is only a host-side handle: host code uses the address that
+// hipGetSymbolAddress returns for the current device, taken once per device
+// on the first call there and kept in g_scratch.
+constexpr size_t kStaticScratchBytes = ABS_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+std::atomic<void*> g_scratch[kMaxDevices];
+
+void* scratch_of_current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        fail(ABS_ERR_HIP, "no current device (or device id beyond %d)", kMaxDevices - 1);
+        return nullptr;
+    }
+    void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+    if (ptr != nullptr) return ptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+        (void)hipGetLastError();
+        fail(ABS_ERR_HIP, "hipGetSymbolAddress: %s", hipGetErrorString(e));
+        return nullptr;
+    }
+    g_scratch[dev].store(ptr, std::memory_order_release);   // the same address if two threads race here
+    return ptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+abs_status abs_select_decode(const abs_paged_kv* kv, const abs_block_map* map, const abs_centroids* cents,
+                             const void* q, int32_t token_budget, float sm_scale, int32_t* sel, int32_t sel_cap,
+                             int32_t* sel_count, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    return select_decode_on(kv, map, cents, q, token_budget, sm_scale, sel, sel_cap, sel_count, out, lse, workspace,
+                            workspace_bytes, stream, nullptr);
+}
+
+abs_status abs_select_decode_static(const abs_paged_kv* kv, const abs_block_map* map, const abs_centroids* cents,
+                                    const void* q, int32_t token_budget, float sm_scale, int32_t* sel,
+                                    int32_t sel_cap, int32_t* sel_count, void* out, float* lse, void* stream) {
+    return select_decode_on(kv, map, cents, q, token_budget, sm_scale, sel, sel_cap, sel_count, out, lse, nullptr,
+                            kStaticScratchBytes, stream, scratch_of_current_device);
 }
 
 abs_status abs_describe_launch(const abs_paged_kv* kv, const abs_block_map* map, int32_t token_budget,

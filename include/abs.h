@@ -314,6 +314,27 @@ abs_status abs_select_decode(const abs_paged_kv *kv, const abs_block_map *map, c
                              size_t workspace_bytes, void *stream);
 
 /*
+ * abs_select_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The library keeps one scratch array of
+ * ABS_STATIC_SCRATCH_BYTES in device memory per GPU, for the life of the
+ * process; this call works on the current device's array and allocates
+ * nothing.  Arguments, outputs and results are those of abs_select_decode
+ * (bit for bit); the call clears the state that must start at zero itself.
+ *   ABS_ERR_WORKSPACE, nothing enqueued, when the layer needs more than
+ *   ABS_STATIC_SCRATCH_BYTES (abs_workspace_bytes(ABS_OP_SELECT_DECODE));
+ *   ABS_ERR_HIP if the array's address cannot be obtained on this device.
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller.
+ */
+#define ABS_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+
+abs_status abs_select_decode_static(const abs_paged_kv *kv, const abs_block_map *map, const abs_centroids *cents,
+                                    const void *q, int32_t token_budget, float sm_scale, int32_t *sel,
+                                    int32_t sel_cap, int32_t *sel_count, void *out, float *lse, void *stream);
+
+/*
  * Launch shape of abs_select_decode / abs_sparse_decode for these
  * descriptors and budget on the current device (host only; nothing is
  * enqueued).  The decode splits each (b, h)'s selected pages over `splits`

@@ -25,7 +25,7 @@ def header_functions():
 
 def test_exports_every_declared_call():
     names = header_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     assert sorted(A.EXPORTS) == names
     L = A.lib()
     for n in names:
@@ -272,6 +272,28 @@ def test_launch_plan_of_the_workloads(cfg, splits, ppw, pipelined):
     assert plan["max_blocks"] == max(-(-w.context // int(b)) for b in bs)
     # every head reads budget / 16 pages, and the splits cover them
     assert splits * ppw >= w.token_budget // 16
+
+
+def test_static_scratch_call_rejects_layers_beyond_its_size():
+    """abs_select_decode_static checks the layer's scratch need against
+    ABS_STATIC_SCRATCH_BYTES on the host, before touching any device."""
+    import re as _re
+    m = _re.search(r"#define ABS_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == A.STATIC_SCRATCH_BYTES
+    big = Host(seq_lens=(131072,) * 64, block_size=(16,) * 8, Hq=32, D=128, max_pages=8192)
+    need = A.abs_workspace_bytes(big.kv, big.bmap, 4096, A.ABS_OP_SELECT_DECODE)
+    assert need > A.STATIC_SCRATCH_BYTES
+    cap = A.abs_select_capacity(big.kv, big.bmap, 4096)
+    assert status_of(lambda: A.abs_select_decode_static(big.kv, big.bmap, big.cents, FAKE, 4096, 0.125, FAKE, cap,
+                                                        FAKE, FAKE, None, 0)) == A.ABS_ERR_WORKSPACE
+    assert "static scratch" in A.abs_last_error()
+    h = Host()
+    cap = A.abs_select_capacity(h.kv, h.bmap, 64)
+    I = A.ABS_ERR_INVALID_ARG
+    assert status_of(lambda: A.abs_select_decode_static(h.kv, h.bmap, h.cents, None, 64, 0.125, FAKE, cap, FAKE,
+                                                        FAKE, None, 0)) == I
+    assert status_of(lambda: A.abs_select_decode_static(h.kv, h.bmap, h.cents, FAKE, 64, 0.125, FAKE, cap - 1,
+                                                        FAKE, FAKE, None, 0)) == I
 
 
 def test_reset_and_debug_switch_validation():
