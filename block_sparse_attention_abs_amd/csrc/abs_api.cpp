@@ -123,6 +123,7 @@ abs_status check_geometry(const abs_paged_kv* kv, const abs_block_map* map, Plan
     g.Hkv = kv->num_kv_heads;
     g.D = kv->head_dim;
     g.G = G;
+    g.hkv_magic = absk::div_magic(g.Hkv);
     g.max_pages = kv->max_pages_per_seq;
     g.num_pages = kv->num_pages;
     g.k = kv->k_cache;
@@ -226,8 +227,15 @@ BuildLayout build_layout(const Plan& p) {
 
 int score_stride(const Plan& p) { return (p.max_n + 3) / 4 * 4; }
 
-size_t select_bytes(const Plan& p) {
+int range_stride(const Plan& p) { return (int)ceil_div64(p.max_n, absk::kScoreBlocksPerWg); }
+
+// The select workspace: fp32 score rows, then each 256-block tile's (min, max).
+size_t select_scores_bytes(const Plan& p) {
     return align_up((size_t)p.g.B * p.g.Hkv * score_stride(p) * sizeof(float));
+}
+
+size_t select_bytes(const Plan& p) {
+    return select_scores_bytes(p) + align_up((size_t)p.g.B * p.g.Hkv * range_stride(p) * 2 * sizeof(float));
 }
 
 absk::DecodeLayout decode_layout(const Plan& p) {
@@ -276,6 +284,8 @@ void fill_select_args(const Plan& p, const abs_paged_kv* kv, const abs_block_map
     a->q = q;
     a->scores = reinterpret_cast<float*>(scores);
     a->stride = score_stride(p);
+    a->ranges = scores != nullptr ? reinterpret_cast<float2*>(ws_at(scores, select_scores_bytes(p))) : nullptr;
+    a->range_stride = range_stride(p);
     a->sel = sel;
     a->count = sel_count;
     a->sel_cap = sel_cap;
@@ -318,6 +328,7 @@ void fill_decode_args(const absk::DecodeLayout& l, const void* q, const int32_t*
     a->part_o = reinterpret_cast<float*>(ws_at(ws, l.o));
     a->arrive = ABS_DECODE_FUSED_MERGE ? reinterpret_cast<int32_t*>(ws_at(ws, l.arrive)) : nullptr;
     a->pages_per_wg = l.ppw;
+    a->ppw_magic = absk::div_magic(l.ppw);
     a->chunk = l.chunk;
     a->pipelined = l.pipelined;
     a->splits = l.splits;

@@ -34,11 +34,13 @@ __global__ __launch_bounds__(256) void k_centroid_mean(Geom g, float* __restrict
     constexpr int NW = VEC * Elem<T>::kBytes / 4;         // 32-bit words per lane per row
     constexpr int GROUPS = 256 / kRowLanes;               // 16 blocks in flight
     const int bh = blockIdx.y;
-    const int b = bh / g.Hkv, h = bh - b * g.Hkv;
+    int b, h;
+    split_bh(g, bh, b, h);
     const int L = seq_len(g, b);
-    const int bs = block_size_of(g, h);
-    const int N = ceil_div(L, bs);
-    const int bpt = kBuildTileTokens / bs;                // blocks per tile
+    const int sb = block_shift_of(g, h);
+    const int bs = 1 << sb;
+    const int N = shr_ceil(L, sb);
+    const int bpt = kBuildTileTokens >> sb;               // blocks per tile
     const int j0 = blockIdx.x * bpt;
     if (j0 >= N) return;                                  // uniform: whole workgroup leaves
     const int lane = threadIdx.x & (kRowLanes - 1);
@@ -121,9 +123,10 @@ __global__ __launch_bounds__(kRangeThreads) void k_centroid_range(Geom g, const 
                                                                   float* __restrict__ scale, float* __restrict__ lo) {
     constexpr int S = kRangeThreads / D;
     const int bh = blockIdx.x;
-    const int b = bh / g.Hkv, h = bh - b * g.Hkv;
-    const int bs = block_size_of(g, h);
-    const int nt = ceil_div(ceil_div(seq_len(g, b), bs), kBuildTileTokens / bs);
+    int b, h;
+    split_bh(g, bh, b, h);
+    const int sb = block_shift_of(g, h);
+    const int nt = shr_ceil(shr_ceil(seq_len(g, b), sb), __builtin_ctz(kBuildTileTokens) - sb);
     const int d = threadIdx.x % D, stripe = threadIdx.x / D;
     const float* pn = pmin + (int64_t)bh * tiles * D + d;
     const float* px = pmax + (int64_t)bh * tiles * D + d;
@@ -246,10 +249,11 @@ __global__ __launch_bounds__(256) void k_centroid_quantize(Geom g, const float* 
     constexpr int BITS = fmt_bits(FMT);
     constexpr int64_t RB = row_bytes(D, FMT);
     const int bh = blockIdx.y;
-    const int b = bh / g.Hkv, h = bh - b * g.Hkv;
-    const int bs = block_size_of(g, h);
-    const int N = centroid_rows(g, bh, ceil_div(seq_len(g, b), bs));
-    const int bpt = kBuildTileTokens / bs;
+    int b, h;
+    split_bh(g, bh, b, h);
+    const int sb = block_shift_of(g, h);
+    const int N = centroid_rows(g, bh, shr_ceil(seq_len(g, b), sb));
+    const int bpt = kBuildTileTokens >> sb;
     const int j0 = blockIdx.x * bpt;
     if (j0 >= N) return;
     const int64_t row0 = g.off[bh];
@@ -329,12 +333,15 @@ __global__ __launch_bounds__(256) void k_centroid_update(Geom g, int appended, c
     constexpr int BITS = fmt_bits(FMT);
     constexpr int64_t RB = row_bytes(D, FMT);
     const int bh = blockIdx.x;
-    const int b = bh / g.Hkv, h = bh - b * g.Hkv;
+    int b, h;
+    split_bh(g, bh, b, h);
     const int L = seq_len(g, b);
-    const int bs = block_size_of(g, h);
-    const int ppb = bs / kPage;                           // pages per block
-    const int N = centroid_rows(g, bh, ceil_div(L, bs));
-    const int j_first = (max(1, L - appended) - 1) / bs;
+    const int sb = block_shift_of(g, h);
+    const int bs = 1 << sb;
+    const int sp = sb - 4;                                // log2(pages per block)
+    const int ppb = 1 << sp;                              // pages per block
+    const int N = centroid_rows(g, bh, shr_ceil(L, sb));
+    const int j_first = (max(1, L - appended) - 1) >> sb;
     const int64_t row0 = g.off[bh];
     const int lane = threadIdx.x & (kRowLanes - 1);
     const int grp = threadIdx.x / kRowLanes;
@@ -344,11 +351,11 @@ __global__ __launch_bounds__(256) void k_centroid_update(Geom g, int appended, c
     if (threadIdx.x == 0) s_clamped = 0;
     int clamped = 0;
     // (block, page) items, GROUPS at a time; blocks of a pass are whole
-    const int bpp = max(1, GROUPS / ppb);                 // blocks per pass
+    const int bpp = max(1, GROUPS >> sp);                 // blocks per pass
     for (int jb = j_first; jb < N; jb += bpp) {
         const int nb = min(bpp, N - jb);
         {
-            const int item = grp, j = jb + item / ppb, pg_in = item % ppb;
+            const int item = grp, j = jb + (item >> sp), pg_in = item & (ppb - 1);
             double acc[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e) acc[e] = 0.0;

@@ -121,14 +121,16 @@ __global__ __launch_bounds__(256 * RG, (DecodeOccupancy<T, D, GT, PIPE, MF>::val
                                                           const int32_t* __restrict__ sel, int sel_cap,
                                                           const int32_t* __restrict__ count, float qscale,
                                                           float* __restrict__ part_ml, float* __restrict__ part_o,
-                                                          int splits, int ppw, int32_t* __restrict__ arrive,
+                                                          int splits, int ppw, uint32_t ppw_magic,
+                                                          int32_t* __restrict__ arrive,
                                                           T* __restrict__ out, float* __restrict__ lse) {
     constexpr int VEC = D / kRowLanes;
     constexpr int NW = VEC * Elem<T>::kBytes / 4;
     constexpr float NEG = -__builtin_inff();
     const int split = blockIdx.x;
     const int bh = blockIdx.y;
-    const int b = bh / g.Hkv, h = bh - b * g.Hkv;
+    int b, h;
+    split_bh(g, bh, b, h);
     const int row = (threadIdx.x & 255) / kRowLanes;
     const int rg = threadIdx.x >> 8;                     // row group
     const int lane = threadIdx.x & (kRowLanes - 1);
@@ -147,15 +149,15 @@ __global__ __launch_bounds__(256 * RG, (DecodeOccupancy<T, D, GT, PIPE, MF>::val
     // follows selection entry -> logical page -> physical page for page p0 + i
     // (the selection row is read speculatively up to sel_cap, before the
     // sequence length and the count arrive); readlane then broadcasts them.
-    const int spb = block_size_of(g, h) / kPage;      // pages per block (stride): 1, 2 or 4
-    const int sh = __builtin_ctz(spb);
+    const int sh = block_shift_of(g, h) - 4;          // log2(pages per block)
+    const int spb = 1 << sh;                           // pages per block (stride): 1, 2 or 4
     const int p0 = split * ppw;                        // ppw <= 64
     const int gp = p0 + wl;
     const bool in_row = wl < ppw && gp < sel_cap * spb;
     const int sv = sel[(int64_t)bh * sel_cap + min(gp >> sh, sel_cap - 1)];   // unconditional, clamped
     const int L = seq_len(g, b);
-    const int npages = ceil_div(L, kPage);
-    const int N = ceil_div(L, spb * kPage);
+    const int npages = shr_ceil(L, 4);
+    const int N = shr_ceil(L, sh + 4);
     const int K = min(max(count[bh], 0), sel_cap);
     const int total = min(K * spb, splits * ppw);      // selected pages of (b, h)
     int ph = -1, lp = 0;
@@ -375,7 +377,7 @@ __global__ __launch_bounds__(256 * RG, (DecodeOccupancy<T, D, GT, PIPE, MF>::val
     // in the selected range but all of its pages are empty.
     const bool fused = arrive != nullptr;
     const bool holds = p0 < total;                      // active implies holds
-    const int nact = ceil_div(total, ppw);              // workgroups holding pages of (b, h)
+    const int nact = fast_div(total + ppw - 1, ppw, ppw_magic);   // workgroups holding pages of (b, h)
     if (holds) {
         for (int idx = 2 * (int)threadIdx.x; idx < GT * D; idx += 2 * (int)blockDim.x) {
             const int gg = idx / D, d = idx - gg * D;
@@ -495,7 +497,7 @@ __global__ __launch_bounds__(256 * RG, (DecodeOccupancy<T, D, GT, PIPE, MF>::val
 template <int GT, int NW>
 __device__ __forceinline__ void ws_decode(const Geom& g, const uint16_t* __restrict__ q, int sv, int K, int sel_cap,
                                           float qscale, float* __restrict__ part_ml, float* __restrict__ part_o,
-                                          int splits, int ppw, int32_t* __restrict__ arrive,
+                                          int splits, int ppw, uint32_t ppw_magic, int32_t* __restrict__ arrive,
                                           uint16_t* __restrict__ out, float* __restrict__ lse) {
     using T = uint16_t;
     constexpr int D = 128;
@@ -505,19 +507,20 @@ __device__ __forceinline__ void ws_decode(const Geom& g, const uint16_t* __restr
     constexpr float NEG = -__builtin_inff();
     const int split = blockIdx.x;
     const int bh = blockIdx.y;
-    const int b = bh / g.Hkv, h = bh - b * g.Hkv;
+    int b, h;
+    split_bh(g, bh, b, h);
     const int wave = threadIdx.x / 64;
     const int wl = threadIdx.x & 63;
     const bool worker = NW == 4 || wave < 4;
 
-    const int spb = block_size_of(g, h) / kPage;      // pages per block (stride): 1, 2 or 4
-    const int sh = __builtin_ctz(spb);
+    const int sh = block_shift_of(g, h) - 4;          // log2(pages per block)
+    const int spb = 1 << sh;                           // pages per block (stride): 1, 2 or 4
     const int p0 = split * ppw;                        // ppw <= 64
     const int gp = p0 + wl;
     const bool in_row = wl < ppw && gp < sel_cap * spb;
     const int L = seq_len(g, b);
-    const int npages = ceil_div(L, kPage);
-    const int N = ceil_div(L, spb * kPage);
+    const int npages = shr_ceil(L, 4);
+    const int N = shr_ceil(L, sh + 4);
     const int total = min(K * spb, splits * ppw);      // selected pages of (b, h)
     int ph = -1, lp = 0;
     if (in_row) {
@@ -653,7 +656,7 @@ __device__ __forceinline__ void ws_decode(const Geom& g, const uint16_t* __restr
     // in the selected range but all of its pages are empty.
     const bool fused = arrive != nullptr;
     const bool holds = p0 < total;                      // active implies holds
-    const int nact = ceil_div(total, ppw);              // workgroups holding pages of (b, h)
+    const int nact = fast_div(total + ppw - 1, ppw, ppw_magic);   // workgroups holding pages of (b, h)
     if (holds) {
         for (int idx = 2 * (int)threadIdx.x; idx < GT * D; idx += 2 * (int)blockDim.x) {
             const int gg = idx / D, d = idx - gg * D;
@@ -761,14 +764,17 @@ __global__ __launch_bounds__(256, 2) void k_sparse_decode_ws(Geom g, const uint1
                                                              const int32_t* __restrict__ sel, int sel_cap,
                                                              const int32_t* __restrict__ count, float qscale,
                                                              float* __restrict__ part_ml, float* __restrict__ part_o,
-                                                             int splits, int ppw, int32_t* __restrict__ arrive,
+                                                             int splits, int ppw, uint32_t ppw_magic,
+                                                             int32_t* __restrict__ arrive,
                                                              uint16_t* __restrict__ out, float* __restrict__ lse) {
     const int bh = blockIdx.y;
-    const int sh = __builtin_ctz(block_size_of(g, bh % g.Hkv) / kPage);
+    int b, h;
+    split_bh(g, bh, b, h);
+    const int sh = block_shift_of(g, h) - 4;
     const int gp = blockIdx.x * ppw + (int)(threadIdx.x & 63);
     const int sv = sel[(int64_t)bh * sel_cap + min(gp >> sh, sel_cap - 1)];   // unconditional, clamped
     const int K = min(max(count[bh], 0), sel_cap);
-    ws_decode<GT, 4>(g, q, sv, K, sel_cap, qscale, part_ml, part_o, splits, ppw, arrive, out, lse);
+    ws_decode<GT, 4>(g, q, sv, K, sel_cap, qscale, part_ml, part_o, splits, ppw, ppw_magic, arrive, out, lse);
 }
 
 // Top-K and decode in one launch (abs_select_decode): every split workgroup
@@ -779,15 +785,20 @@ __global__ __launch_bounds__(256, 2) void k_sparse_decode_ws(Geom g, const uint1
 // the same selection from the same row.
 template <int GT, int KPT>
 __global__ __launch_bounds__(512) void k_select_decode_ws(Geom g, const float* __restrict__ scores, int stride,
+                                                          const float2* __restrict__ ranges, int range_stride,
                                                           int max_len, int budget, int32_t* __restrict__ sel,
                                                           int sel_cap, int32_t* __restrict__ count,
                                                           const uint16_t* __restrict__ q, float qscale,
                                                           float* __restrict__ part_ml, float* __restrict__ part_o,
-                                                          int splits, int ppw, int32_t* __restrict__ arrive,
+                                                          int splits, int ppw, uint32_t ppw_magic,
+                                                          int32_t* __restrict__ arrive,
                                                           uint16_t* __restrict__ out, float* __restrict__ lse) {
     const int split = blockIdx.x;
     const int bh = blockIdx.y;
-    const int sh = __builtin_ctz(block_size_of(g, bh % g.Hkv) / kPage);
+    int b, h;
+    split_bh(g, bh, b, h);
+    const int sb = block_shift_of(g, h);
+    const int sh = sb - 4;
     const int first = (split * ppw) >> sh;            // selection positions first .. first + 63 (ppw <= 64)
     __shared__ int32_t s_blk[kMaxPagesPerWg];
     int32_t* row_out = sel + (int64_t)bh * sel_cap;
@@ -799,20 +810,21 @@ __global__ __launch_bounds__(512) void k_select_decode_ws(Geom g, const float* _
     // keys per thread for this head's longest row (up to KPT, the layer's):
     // heads with larger blocks finish their top-K sooner
     const float* srow = scores + (int64_t)bh * stride;
-    const int nh = ceil_div(max_len, block_size_of(g, bh % g.Hkv));
+    const float2* rrow = ranges + (int64_t)bh * range_stride;
+    const int nh = shr_ceil(max_len, sb);
     int K;
     if (KPT > 4 && nh <= kFusedThreads * 4)
-        K = topk_rows<kFusedThreads, 4>(g, bh, srow, stride, max_len, budget, emit);
+        K = topk_rows<kFusedThreads, 4>(g, bh, srow, stride, rrow, max_len, budget, emit);
     else if (KPT > 8 && nh <= kFusedThreads * 8)
-        K = topk_rows<kFusedThreads, (KPT > 8 ? 8 : KPT)>(g, bh, srow, stride, max_len, budget, emit);
+        K = topk_rows<kFusedThreads, (KPT > 8 ? 8 : KPT)>(g, bh, srow, stride, rrow, max_len, budget, emit);
     else
-        K = topk_rows<kFusedThreads, KPT>(g, bh, srow, stride, max_len, budget, emit);
+        K = topk_rows<kFusedThreads, KPT>(g, bh, srow, stride, rrow, max_len, budget, emit);
     if (split == 0 && threadIdx.x == 0) count[bh] = K;
     __syncthreads();
     const int gp = split * ppw + (int)(threadIdx.x & 63);
     const int sv = s_blk[min(max((gp >> sh) - first, 0), kMaxPagesPerWg - 1)];   // positions >= K: unused
     ws_decode<GT, kFusedThreads / 64>(g, q, sv, min(K, sel_cap), sel_cap, qscale, part_ml, part_o, splits, ppw,
-                                      arrive, out, lse);
+                                      ppw_magic, arrive, out, lse);
 }
 
 // One workgroup per (b, query head): merge the partials of the splits that
@@ -882,7 +894,7 @@ void launch_split(dim3 grid, const Geom& g, const DecodeArgs& a, float qscale, h
     constexpr int kThreads = 256 * RG;
     hipLaunchKernelGGL((k_sparse_decode<T, D, GT, CH, PIPE, MF, RG>), grid, dim3(kThreads), 0, s, g,
                        reinterpret_cast<const T*>(a.q), a.sel, a.sel_cap, a.count, qscale, a.part_ml, a.part_o,
-                       a.splits, a.pages_per_wg, a.arrive, reinterpret_cast<T*>(a.out), a.lse);
+                       a.splits, a.pages_per_wg, a.ppw_magic, a.arrive, reinterpret_cast<T*>(a.out), a.lse);
 }
 
 template <typename T, int D, int GT>
@@ -902,7 +914,8 @@ hipError_t decode_gt(const Geom& g, const DecodeArgs& a, hipStream_t s) {
         if constexpr (kWaveSplit)
             hipLaunchKernelGGL((k_sparse_decode_ws<GT>), grid, dim3(256), 0, s, g,
                                reinterpret_cast<const uint16_t*>(a.q), a.sel, a.sel_cap, a.count, qscale, a.part_ml,
-                               a.part_o, a.splits, a.pages_per_wg, a.arrive, reinterpret_cast<uint16_t*>(a.out), a.lse);
+                               a.part_o, a.splits, a.pages_per_wg, a.ppw_magic, a.arrive,
+                               reinterpret_cast<uint16_t*>(a.out), a.lse);
     } else if (a.pipelined && kPipeFits<T, D, GT>) {
         if constexpr (kPipeFits<T, D, GT>) launch_split<T, D, GT, 8, true, kMatrix, kRowGroups>(grid, g, a, qscale, s);
     } else if ((a.chunk == 8 || a.pipelined) && !kWide) {
@@ -957,9 +970,9 @@ namespace {
 template <int GT, int KPT>
 void launch_fused(const Geom& g, const SelectArgs& s, const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((k_select_decode_ws<GT, KPT>), dim3(a.splits, g.B * g.Hkv), dim3(kFusedThreads), 0, st, g, s.scores,
-                       s.stride, s.max_len, s.budget, s.sel, s.sel_cap, s.count,
+                       s.stride, s.ranges, s.range_stride, s.max_len, s.budget, s.sel, s.sel_cap, s.count,
                        reinterpret_cast<const uint16_t*>(a.q), a.sm_scale * kLog2e, a.part_ml, a.part_o, a.splits,
-                       a.pages_per_wg, a.arrive, reinterpret_cast<uint16_t*>(a.out), a.lse);
+                       a.pages_per_wg, a.ppw_magic, a.arrive, reinterpret_cast<uint16_t*>(a.out), a.lse);
 }
 
 template <int GT>

@@ -15,6 +15,7 @@ namespace absk {
 constexpr int kMaxKvHeads = 64;
 struct Geom {
     int B, Hq, Hkv, D, G, max_pages;
+    uint32_t hkv_magic;   // div_magic(Hkv): b = bh / Hkv without a division
     int max_len;          // the longest L_b on the host: every buffer is sized from it
     int64_t num_pages;
     const void* k;
@@ -37,10 +38,34 @@ __device__ __forceinline__ int centroid_rows(const Geom& g, int bh, int N) {
     return (int)min((int64_t)N, g.off[bh + 1] - g.off[bh]);
 }
 
-__device__ __forceinline__ int block_size_of(const Geom& g, int h) {
-    const uint64_t w = h < 32 ? g.bs_log2[0] : g.bs_log2[1];
-    return 16 << (int)((w >> (2 * (h & 31))) & 3u);
+// Division by a small runtime divisor d (1..64) without a division: with
+// magic = ceil(2^32 / d), floor(n / d) = (n * magic) >> 32 for 0 <= n < 2^26
+// (the rounding of the magic, n * (magic - 2^32 / d) < n * d / 2^32, stays
+// below 1/d, the smallest gap between n/d and the next integer).  d = 1 has
+// magic 0 and is taken apart.
+__host__ __device__ constexpr uint32_t div_magic(int d) {
+    return d <= 1 ? 0u : (uint32_t)(((uint64_t)1 << 32) / (uint64_t)d + (((uint64_t)1 << 32) % (uint64_t)d != 0));
 }
+__device__ __forceinline__ int fast_div(int n, int d, uint32_t magic) {
+    return d == 1 ? n : (int)__umulhi((uint32_t)n, magic);
+}
+
+// (b, h) of a flat index bh = b * Hkv + h.
+__device__ __forceinline__ void split_bh(const Geom& g, int bh, int& b, int& h) {
+    b = fast_div(bh, g.Hkv, g.hkv_magic);
+    h = bh - b * g.Hkv;
+}
+
+// Block sizes are 16 << {0, 1, 2}: log2 of head h's block size.
+__device__ __forceinline__ int block_shift_of(const Geom& g, int h) {
+    const uint64_t w = h < 32 ? g.bs_log2[0] : g.bs_log2[1];
+    return 4 + (int)((w >> (2 * (h & 31))) & 3u);
+}
+
+__device__ __forceinline__ int block_size_of(const Geom& g, int h) { return 1 << block_shift_of(g, h); }
+
+// ceil(x / 2^s) for x >= 0.
+__device__ __forceinline__ int shr_ceil(int x, int s) { return (x + (1 << s) - 1) >> s; }
 
 enum class DType { F32 = 0, BF16 = 1 };
 
@@ -92,7 +117,7 @@ constexpr int kMaxBlocksPerHead = 65536;   // top-K keeps N_{b,h} keys in regist
 // head needs for the longest sequence, B): x is mapped to (head, tile)
 // through the per-head cumulative tile counts in HeadTiles, and only the
 // workgroups past a shorter sequence's blocks have nothing to do.
-constexpr int kScoreBlocksPerWg = 256;
+constexpr int kScoreBlocksPerWg = 256;             // 2^8: the top-K shifts by 8 to count tiles
 constexpr int kMaxScoreTiles = 512;
 struct ScoreTiles {
     uint32_t t[kMaxScoreTiles];
@@ -109,6 +134,8 @@ struct SelectArgs {
     const void* q;
     float* scores;    // [B*Hkv][stride]
     int stride;       // max N_{b,h} rounded up to a multiple of 4
+    float2* ranges;   // [B*Hkv][range_stride]: (min, max) score of each 256-block tile
+    int range_stride; // tiles of the longest head
     int32_t* sel;
     int32_t* count;
     int sel_cap;
@@ -138,6 +165,7 @@ struct DecodeArgs {
     float* part_o;    // [B*Hq][splits][D]
     int32_t* arrive;  // [B*Hkv] arrival counters, zero between calls; null: separate merge launch
     int pages_per_wg; // <= kMaxPagesPerWg, a multiple of chunk
+    uint32_t ppw_magic;   // div_magic(pages_per_wg)
     int chunk;        // pages held in registers at a time: 1, 2, 4 or 8
     bool pipelined;   // two chunks in flight (chunk 8, pages_per_wg a multiple of 16)
     int splits;

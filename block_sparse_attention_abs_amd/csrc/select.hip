@@ -37,8 +37,8 @@ namespace {
 template <typename T, int D, int GT, int BITS>
 __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restrict__ codes,
                                            const float* __restrict__ scale, const float* __restrict__ lo,
-                                           const T* __restrict__ q, float* __restrict__ scores, int stride, int bh,
-                                           int tile) {
+                                           const T* __restrict__ q, float* __restrict__ scores, int stride,
+                                           float2* __restrict__ ranges, int range_stride, int bh, int tile) {
     constexpr int NT = ABS_SCORE_NT;
     constexpr int CPL = 128 / BITS;           // channels per lane (16 B of codes)
     constexpr int LPB = D / CPL;              // lanes per block row
@@ -47,9 +47,10 @@ __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restr
     constexpr int RB = D * BITS / 8;          // bytes per row
     constexpr int PER = 32 / BITS;            // channels per 32-bit word
     static_assert(NT >= D, "one thread per channel folds the query");
-    const int b = bh / g.Hkv, h = bh - b * g.Hkv;
+    int b, h;
+    split_bh(g, bh, b, h);
     const int64_t row0 = g.off[bh];
-    const int N = centroid_rows(g, bh, ceil_div(seq_len(g, b), block_size_of(g, h)));
+    const int N = centroid_rows(g, bh, shr_ceil(seq_len(g, b), block_shift_of(g, h)));
     const int j0 = tile * kScoreBlocksPerWg;
     const int sub = threadIdx.x % LPB;
     const int grp = threadIdx.x / LPB;
@@ -115,6 +116,7 @@ __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restr
         wr[n] = w[sub * CS + n];
         if constexpr (BITS != 16) c0 += z[sub * CS + n];
     }
+    float tmn = __builtin_inff(), tmx = -__builtin_inff();   // the tile's range of stored scores
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
         const uint32_t wd[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
@@ -133,6 +135,26 @@ __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restr
         const double sum = lanes_sum_f64<LPB>(acc[0] + acc[1]);
         const int j = j0 + r * GPW + grp;
         if (j < N && sub == 0) scores[(int64_t)bh * stride + j] = (float)sum;
+        tmn = j < N ? fminf(tmn, (float)sum) : tmn;
+        tmx = j < N ? fmaxf(tmx, (float)sum) : tmx;
+    }
+    // (min, max) over the tile's stored scores, for the top-K's binning
+    // (a tile past the row's end writes the empty range)
+    __shared__ float s_rng[2][NT / 64];
+    tmx = wave_max(tmx);
+    tmn = -wave_max(-tmn);
+    if ((threadIdx.x & 63) == 0) {
+        s_rng[0][threadIdx.x >> 6] = tmn;
+        s_rng[1][threadIdx.x >> 6] = tmx;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int w = 1; w < NT / 64; ++w) {
+            tmn = fminf(tmn, s_rng[0][w]);
+            tmx = fmaxf(tmx, s_rng[1][w]);
+        }
+        ranges[(int64_t)bh * range_stride + tile] = make_float2(tmn, tmx);
     }
 }
 
@@ -149,6 +171,7 @@ template <typename T, int D, int GT, int BITS>
 __global__ __launch_bounds__(ABS_SCORE_NT) void k_score_seq(Geom g, const uint8_t* __restrict__ codes,
                                                    const float* __restrict__ scale, const float* __restrict__ lo,
                                                    const T* __restrict__ q, float* __restrict__ scores, int stride,
+                                                   float2* __restrict__ ranges, int range_stride,
                                                    const HeadTiles ht, int32_t* __restrict__ zc, int nz) {
     const uint32_t x = blockIdx.x;
     int hl = 0, hh = g.Hkv;                          // ht.cum[hl] <= x < ht.cum[hh]
@@ -157,8 +180,8 @@ __global__ __launch_bounds__(ABS_SCORE_NT) void k_score_seq(Geom g, const uint8_
         if (ht.cum[mid] <= x) hl = mid;
         else hh = mid;
     }
-    score_tile<T, D, GT, BITS>(g, codes, scale, lo, q, scores, stride, (int)blockIdx.y * g.Hkv + hl,
-                               (int)(x - ht.cum[hl]));
+    score_tile<T, D, GT, BITS>(g, codes, scale, lo, q, scores, stride, ranges, range_stride,
+                               (int)blockIdx.y * g.Hkv + hl, (int)(x - ht.cum[hl]));
     if (x == 0 && blockIdx.y == 0) zero_ints(zc, nz);
 }
 
@@ -166,9 +189,11 @@ template <typename T, int D, int GT, int BITS>
 __global__ __launch_bounds__(ABS_SCORE_NT) void k_score_list(Geom g, const uint8_t* __restrict__ codes,
                                                     const float* __restrict__ scale, const float* __restrict__ lo,
                                                     const T* __restrict__ q, float* __restrict__ scores, int stride,
+                                                    float2* __restrict__ ranges, int range_stride,
                                                     const ScoreTiles tl, int32_t* __restrict__ zc, int nz) {
     const uint32_t e = tl.t[blockIdx.x];
-    score_tile<T, D, GT, BITS>(g, codes, scale, lo, q, scores, stride, (int)(e >> 8), (int)(e & 255u));
+    score_tile<T, D, GT, BITS>(g, codes, scale, lo, q, scores, stride, ranges, range_stride, (int)(e >> 8),
+                               (int)(e & 255u));
     if (blockIdx.x == 0) zero_ints(zc, nz);
 }
 
@@ -178,12 +203,14 @@ __global__ __launch_bounds__(ABS_SCORE_NT) void k_score_list(Geom g, const uint8
 #endif
 
 template <int NT, int KPT>
-__global__ __launch_bounds__(NT) void k_topk(Geom g, const float* __restrict__ scores, int stride, int max_len,
+__global__ __launch_bounds__(NT) void k_topk(Geom g, const float* __restrict__ scores, int stride,
+                                             const float2* __restrict__ ranges, int range_stride, int max_len,
                                              int budget, int32_t* __restrict__ sel, int sel_cap,
                                              int32_t* __restrict__ count) {
     const int bh = blockIdx.x;
     int32_t* out = sel + (int64_t)bh * sel_cap;
-    const int K = topk_rows<NT, KPT>(g, bh, scores + (int64_t)bh * stride, stride, max_len, budget,
+    const int K = topk_rows<NT, KPT>(g, bh, scores + (int64_t)bh * stride, stride,
+                                     ranges + (int64_t)bh * range_stride, max_len, budget,
                                      [&](uint32_t p, int32_t j) {
                                          if (p < (uint32_t)sel_cap) out[p] = j;
                                      });
@@ -198,7 +225,8 @@ void launch_score(const Geom& g, const SelectArgs& a, hipStream_t s) {
         for (int i = 0; i < a.ntiles; ++i) tl.t[i] = a.tiles_host[i];
 #define ABS_SCORE(GT_)                                                                                    \
     hipLaunchKernelGGL((k_score_list<T, D, GT_, BITS>), dim3(a.ntiles), dim3(ABS_SCORE_NT), 0, s, g, a.codes, \
-                       a.scale, a.lo, q, a.scores, a.stride, tl, a.zero_counters, a.n_zero)
+                       a.scale, a.lo, q, a.scores, a.stride, a.ranges, a.range_stride, tl, a.zero_counters, \
+                       a.n_zero)
         if (g.G <= 1) ABS_SCORE(1);
         else if (g.G <= 2) ABS_SCORE(2);
         else if (g.G <= 4) ABS_SCORE(4);
@@ -208,7 +236,7 @@ void launch_score(const Geom& g, const SelectArgs& a, hipStream_t s) {
         const dim3 sgrid(a.head_tiles.cum[g.Hkv], g.B);
 #define ABS_SCORE(GT_)                                                                                       \
     hipLaunchKernelGGL((k_score_seq<T, D, GT_, BITS>), sgrid, dim3(ABS_SCORE_NT), 0, s, g, a.codes, a.scale, a.lo, \
-                       q, a.scores, a.stride, a.head_tiles, a.zero_counters, a.n_zero)
+                       q, a.scores, a.stride, a.ranges, a.range_stride, a.head_tiles, a.zero_counters, a.n_zero)
         if (g.G <= 1) ABS_SCORE(1);
         else if (g.G <= 2) ABS_SCORE(2);
         else if (g.G <= 4) ABS_SCORE(4);
@@ -226,7 +254,8 @@ hipError_t select_impl(const Geom& g, const SelectArgs& a, bool with_topk, hipSt
     if (!with_topk) return hipGetLastError();
     const dim3 tgrid(g.B * g.Hkv);
 #define ABS_TOPK(NT_, KPT_)                                                                                  \
-    hipLaunchKernelGGL((k_topk<NT_, KPT_>), tgrid, dim3(NT_), 0, s, g, a.scores, a.stride, a.max_len, a.budget, \
+    hipLaunchKernelGGL((k_topk<NT_, KPT_>), tgrid, dim3(NT_), 0, s, g, a.scores, a.stride, a.ranges,            \
+                       a.range_stride, a.max_len, a.budget,                                                \
                        a.sel, a.sel_cap, a.count)
     // ABS_TOPK_NT threads, each holding up to 32 keys; 1024 x 64 beyond that
     constexpr int NT = ABS_TOPK_NT;
