@@ -60,13 +60,13 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0
 METRIC = "sparse decode attn queries/s per layer at 32K/128K ctx; achieved HBM GB/s vs peak"
 
-# HBM bytes per launch of the split kernel from rocprofv3 FETCH_SIZE and
-# WRITE_SIZE, each scaled by the same counter's reading for a plain copy of
-# known size (see profiles/), keyed by (workload, context, block map) and by
-# a hash of the kernel sources they were taken with; any other source
+# HBM bytes per launch of the kernel the roofline describes (the fused
+# top-K + split decode launch, k_select_decode_ws) from rocprofv3 FETCH_SIZE
+# and WRITE_SIZE, each scaled by the same counter's reading for a plain copy
+# of known size (see profiles/), keyed by (workload, context, block map) and
+# by a hash of the kernel sources they were taken with; any other source
 # reports null.
 TRAFFIC = {
-    ("llama8b-128k-b4-bf16", 131072, "drawn", "aa9aff67d5232a7d"): 68849732,
 }
 KERNEL_SOURCES = ("decode.hip", "device.hpp", "launch.hpp", "decode_layout.hpp", "topk.hpp")   # kernel + its launch layout
 
@@ -262,7 +262,28 @@ def main():
         torch.cuda.synchronize()
         return g
 
+    # the two halves of abs_select_decode on their own (the page's per-stage
+    # split): abs_estimate, and abs_topk_decode -- the top-K + split decode
+    # launch the roofline describes -- each layer copy on its own workspace,
+    # filled by abs_estimate for that copy
+    ws_stage = [A.workspace(ws_sd.numel(), dev) for _ in range(R)]
+
+    def estimate_call(i, st):
+        r = i % R
+        A.abs_estimate(layers[r].kv, layers[r].bmap, cents[r].desc, int(qs[r].data_ptr()), budget,
+                       int(ws_stage[r].data_ptr()), ws_stage[r].numel(), st)
+
+    def topk_decode_call(i, st):
+        r = i % R
+        A.abs_topk_decode(layers[r].kv, layers[r].bmap, int(qs[r].data_ptr()), budget, sm, int(sel.data_ptr()), cap,
+                          int(cnt.data_ptr()), int(out.data_ptr()), int(lse.data_ptr()), int(ws_stage[r].data_ptr()),
+                          ws_stage[r].numel(), st)
+
+    for i in range(R):
+        estimate_call(i, sh)
+    torch.cuda.synchronize()
     g_step, g_sel, g_dec = capture(step), capture(select_call), capture(decode_call)
+    g_est, g_td = capture(estimate_call), capture(topk_decode_call)
     g_fused, g_sep = capture(fused_step), capture(separate_step)
     torch.cuda.synchronize()
 
@@ -293,6 +314,8 @@ def main():
     sreps = max(1, min(reps, 32))
     sel_us = np.array([timed(g_sel, sreps) / (sreps * R) * 1e3 for _ in range(5)])
     dec_us = np.array([timed(g_dec, sreps) / (sreps * R) * 1e3 for _ in range(5)])
+    est_us = np.array([timed(g_est, sreps) / (sreps * R) * 1e3 for _ in range(5)])
+    td_us = np.array([timed(g_td, sreps) / (sreps * R) * 1e3 for _ in range(5)])
     # both step forms, timed the same way, alternating
     form_us = {"fused": [], "separate": []}
     for _ in range(5):
@@ -322,7 +345,13 @@ def main():
 
     ab = algorithmic_bytes(x, budget, lambda L, bs: min(L, max(1, budget // bs) * bs), code_bits)
     dec_avg = float(np.median(dec_us))
-    achieved = ab["decode"] / (dec_avg * 1e-6) / 1e9
+    td_avg = float(np.median(td_us))
+    plan = base.launch_plan(budget)
+    # the dominant kernel of the timed step: the top-K + split decode launch
+    # (abs_topk_decode) when the layer is served by it, else the split decode
+    fused = bool(plan["fused"]) and not args.separate
+    kern_us = td_avg if fused else dec_avg
+    achieved = ab["decode"] / (kern_us * 1e-6) / 1e9
     queries_per_s = B / (ms_per_step * 1e-3)
 
     copy_gbs = measured_copy_gbs(torch, dev)
@@ -331,7 +360,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x, budget, sm, args.cpu_seconds)
 
-    traffic = TRAFFIC.get((w.name, int(w.context), args.block_map, kernel_source_hash()))
+    traffic = TRAFFIC.get((w.name, int(w.context), args.block_map, kernel_source_hash())) if fused else None
     rec = {
         "metric": METRIC,
         "value": round(queries_per_s, 1),
@@ -349,18 +378,24 @@ def main():
                    "kv_heads": w.num_kv_heads, "head_dim": D, "token_budget": budget, "page_size": 16,
                    "block_sizes": x.block_size.tolist(), "block_map": args.block_map, "centroid_format": fmt,
                    "kv_replicas": None if args.layers else R, "layers": args.layers or 1},
-        "roofline": {"bound": "hbm", "kernel": "k_sparse_decode_ws (abs_sparse_decode: split, merge in the same launch)",
+        "roofline": {"bound": "hbm",
+                     "kernel": ("k_select_decode_ws (abs_topk_decode: top-K, split decode and merge in one launch)"
+                                if fused else "k_sparse_decode_ws (abs_sparse_decode: split, merge in the same launch)"),
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes": ab["decode"], "avg_us": round(dec_avg, 3),
+                     "algorithmic_bytes": ab["decode"], "avg_us": round(kern_us, 3),
                      "measured_copy_gbs": round(copy_gbs, 1),
-                     "frac_of_measured_copy": round(achieved / copy_gbs, 4)},
+                     "frac_of_measured_copy": round(achieved / copy_gbs, 4),
+                     "decode_only": {"kernel": "k_sparse_decode_ws (abs_sparse_decode)", "avg_us": round(dec_avg, 3),
+                                     "frac": round(ab["decode"] / (dec_avg * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}},
         "cpu_baseline": cpu,
         "step": {"algorithmic_bytes": ab["step"], "hbm_gbs": round(ab["step"] / (ms_per_step * 1e-3) / 1e9, 1),
                  "hbm_frac": round(ab["step"] / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                  "step_call": "abs_score_select + abs_sparse_decode" if args.separate else "abs_select_decode",
                  "select_decode_step_us": round(float(np.median(form_us["fused"])), 3),
                  "separate_calls_step_us": round(float(np.median(form_us["separate"])), 3),
+                 "estimate_us": round(float(np.median(est_us)), 3), "topk_decode_us": round(td_avg, 3),
+                 "launch_plan": plan,
                  "score_select_us": round(float(np.median(sel_us)), 3), "sparse_decode_us": round(dec_avg, 3),
                  "sparse_decode_us_min_max": [round(float(dec_us.min()), 3), round(float(dec_us.max()), 3)],
                  "step_us_p10_p50_p90": [round(float(np.percentile(per_rep, q)), 3) for q in (10, 50, 90)],

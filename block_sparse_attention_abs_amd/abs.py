@@ -30,7 +30,7 @@ CENTROID_FORMATS = {"int4": 0, "int4_sym": 1, "int8": 2, "int4_tensor": 3, "bf16
 EXPORTS = ("abs_status_str", "abs_last_error", "abs_total_blocks", "abs_centroid_offsets",
            "abs_centroid_offsets_capacity", "abs_centroid_row_bytes", "abs_select_capacity", "abs_workspace_bytes", "abs_build_centroids",
            "abs_update_centroids", "abs_score_select", "abs_sparse_decode", "abs_select_decode",
-           "abs_select_decode_static", "abs_describe_launch", "abs_reset_workspace", "abs_set_debug_checks",
+           "abs_estimate", "abs_topk_decode", "abs_select_decode_static", "abs_describe_launch", "abs_reset_workspace", "abs_set_debug_checks",
            "abs_head_recall", "abs_assign_block_sizes")
 
 
@@ -102,6 +102,10 @@ def lib():
         L.abs_sparse_decode.argtypes = [KV, MAP, P, P, i32, P, i32, C.c_float, P, P, P, C.c_size_t, P]
         L.abs_select_decode.restype = st
         L.abs_select_decode.argtypes = [KV, MAP, CEN, P, i32, C.c_float, P, i32, P, P, P, P, C.c_size_t, P]
+        L.abs_estimate.restype = st
+        L.abs_estimate.argtypes = [KV, MAP, CEN, P, i32, P, C.c_size_t, P]
+        L.abs_topk_decode.restype = st
+        L.abs_topk_decode.argtypes = [KV, MAP, P, i32, C.c_float, P, i32, P, P, P, P, C.c_size_t, P]
         L.abs_select_decode_static.restype = st
         L.abs_select_decode_static.argtypes = [KV, MAP, CEN, P, i32, C.c_float, P, i32, P, P, P, P]
         L.abs_describe_launch.restype = st
@@ -202,6 +206,18 @@ def abs_select_decode(kv, bmap, cents, q_ptr: int, token_budget: int, sm_scale: 
     _check(lib().abs_select_decode(C.byref(kv), C.byref(bmap), C.byref(cents), q_ptr, token_budget, sm_scale,
                                    sel_ptr, sel_cap, count_ptr, out_ptr, lse_ptr, ws_ptr, ws_bytes, stream),
            "abs_select_decode")
+
+
+def abs_estimate(kv, bmap, cents, q_ptr: int, token_budget: int, ws_ptr: int, ws_bytes: int, stream: int) -> None:
+    _check(lib().abs_estimate(C.byref(kv), C.byref(bmap), C.byref(cents) if cents is not None else None, q_ptr,
+                              token_budget, ws_ptr, ws_bytes, stream), "abs_estimate")
+
+
+def abs_topk_decode(kv, bmap, q_ptr: int, token_budget: int, sm_scale: float, sel_ptr: int, sel_cap: int,
+                    count_ptr: int, out_ptr: int, lse_ptr: Optional[int], ws_ptr: int, ws_bytes: int,
+                    stream: int) -> None:
+    _check(lib().abs_topk_decode(C.byref(kv), C.byref(bmap), q_ptr, token_budget, sm_scale, sel_ptr, sel_cap,
+                                 count_ptr, out_ptr, lse_ptr, ws_ptr, ws_bytes, stream), "abs_topk_decode")
 
 
 STATIC_SCRATCH_BYTES = 16 << 20   # ABS_STATIC_SCRATCH_BYTES

@@ -515,20 +515,36 @@ abs_status abs_sparse_decode(const abs_paged_kv* kv, const abs_block_map* map, c
 
 namespace {
 
-// abs_select_decode on the workspace `workspace` of `workspace_bytes` bytes
-// (validated here), or, with scratch_of_device, on the static scratch of the
-// current device (workspace_bytes is then its size).
+// The stages of abs_select_decode: Estimation alone (abs_estimate), Top-K and
+// Attention on the scores already in the workspace (abs_topk_decode), or all
+// three.
+enum class Stages { All, Estimate, TopkDecode };
+
+// abs_select_decode's stages on the workspace `workspace` of
+// `workspace_bytes` bytes (validated here), or, with scratch_of_device, on
+// the static scratch of the current device (workspace_bytes is then its
+// size).
 abs_status select_decode_on(const abs_paged_kv* kv, const abs_block_map* map, const abs_centroids* cents,
                             const void* q, int32_t token_budget, float sm_scale, int32_t* sel, int32_t sel_cap,
                             int32_t* sel_count, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                            void* stream, void* (*scratch_of_device)()) {
+                            void* stream, void* (*scratch_of_device)(), Stages stages) {
+    const bool estimate = stages != Stages::TopkDecode, decode = stages != Stages::Estimate;
     Plan p;
     if (abs_status st = check_geometry(kv, map, &p)) return st;
-    if (abs_status st = require_device(p, true)) return st;
+    if (abs_status st = require_device(p, decode)) return st;
     if (abs_status st = plan_budget(kv, map, token_budget, &p)) return st;
-    if (abs_status st = check_select(p, cents, q, sel, sel_cap, sel_count)) return st;
-    if (out == nullptr) return fail(ABS_ERR_INVALID_ARG, "null out");
-    if (!std::isfinite(sm_scale)) return fail(ABS_ERR_INVALID_ARG, "sm_scale is not finite");
+    if (estimate) {
+        if (abs_status st = check_centroids(cents)) return st;
+    }
+    if (q == nullptr) return fail(ABS_ERR_INVALID_ARG, "null q");
+    if (decode) {
+        if (sel == nullptr || sel_count == nullptr || out == nullptr)
+            return fail(ABS_ERR_INVALID_ARG, "null sel, sel_count or out");
+        if (sel_cap < p.sel_cap) return fail(ABS_ERR_INVALID_ARG, "sel_cap %d < required %d", sel_cap, p.sel_cap);
+        if (!std::isfinite(sm_scale)) return fail(ABS_ERR_INVALID_ARG, "sm_scale is not finite");
+    }
+    if (p.max_n > absk::kMaxBlocksPerHead)
+        return fail(ABS_ERR_UNSUPPORTED, "%d blocks in one head (max %d)", p.max_n, absk::kMaxBlocksPerHead);
     const size_t sbytes = select_bytes(p);
     const absk::DecodeLayout l = decode_layout(p);
     if (scratch_of_device != nullptr) {
@@ -541,22 +557,26 @@ abs_status select_decode_on(const abs_paged_kv* kv, const abs_block_map* map, co
     if (workspace == nullptr || workspace_bytes < sbytes + l.bytes)
         return fail(ABS_ERR_WORKSPACE, "select_decode needs %zu workspace bytes, got %zu", sbytes + l.bytes,
                     workspace_bytes);
+    const abs_centroids none{};
     absk::SelectArgs sa;
     uint32_t tiles[absk::kMaxScoreTiles];
-    fill_select_args(p, kv, map, cents, q, token_budget, sel, sel_cap, sel_count, workspace, tiles, &sa);
+    fill_select_args(p, kv, map, estimate ? cents : &none, q, token_budget, sel, sel_cap, sel_count, workspace, tiles,
+                     &sa);
     absk::DecodeArgs da;
     fill_decode_args(l, q, sel, sel_cap, sel_count, sm_scale, out, lse, ws_at(workspace, sbytes), &da);
-    // the first launch zero-fills the decode's arrival counters, so the
+    // the score launch zero-fills the decode's arrival counters, so the
     // decode region needs no zero-filling by the caller
     sa.zero_counters = da.arrive;
     sa.n_zero = da.arrive != nullptr ? p.g.B * p.g.Hkv : 0;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     if (abs_status e = debug_check(p, kv, map, st)) return e;
-    if (absk::select_decode_fusable(p.g, p.dt, sa, da)) {
+    if (estimate) {
         if (abs_status e = hip_status(absk::launch_scores(p.g, p.dt, sa, st), "select_decode (scores)")) return e;
-        return hip_status(absk::launch_select_decode(p.g, p.dt, sa, da, st), "select_decode");
     }
-    if (abs_status e = hip_status(absk::launch_select(p.g, p.dt, sa, st), "select_decode (select)")) return e;
+    if (!decode) return ok();
+    if (absk::select_decode_fusable(p.g, p.dt, sa, da))
+        return hip_status(absk::launch_select_decode(p.g, p.dt, sa, da, st), "select_decode");
+    if (abs_status e = hip_status(absk::launch_topk(p.g, sa, st), "select_decode (top-K)")) return e;
     return hip_status(absk::launch_decode(p.g, p.dt, da, st), "select_decode (decode)");
 }
 
@@ -598,14 +618,27 @@ abs_status abs_select_decode(const abs_paged_kv* kv, const abs_block_map* map, c
                              int32_t* sel_count, void* out, float* lse, void* workspace, size_t workspace_bytes,
                              void* stream) {
     return select_decode_on(kv, map, cents, q, token_budget, sm_scale, sel, sel_cap, sel_count, out, lse, workspace,
-                            workspace_bytes, stream, nullptr);
+                            workspace_bytes, stream, nullptr, Stages::All);
+}
+
+abs_status abs_estimate(const abs_paged_kv* kv, const abs_block_map* map, const abs_centroids* cents, const void* q,
+                        int32_t token_budget, void* workspace, size_t workspace_bytes, void* stream) {
+    return select_decode_on(kv, map, cents, q, token_budget, 1.0f, nullptr, 0, nullptr, nullptr, nullptr, workspace,
+                            workspace_bytes, stream, nullptr, Stages::Estimate);
+}
+
+abs_status abs_topk_decode(const abs_paged_kv* kv, const abs_block_map* map, const void* q, int32_t token_budget,
+                           float sm_scale, int32_t* sel, int32_t sel_cap, int32_t* sel_count, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    return select_decode_on(kv, map, nullptr, q, token_budget, sm_scale, sel, sel_cap, sel_count, out, lse,
+                            workspace, workspace_bytes, stream, nullptr, Stages::TopkDecode);
 }
 
 abs_status abs_select_decode_static(const abs_paged_kv* kv, const abs_block_map* map, const abs_centroids* cents,
                                     const void* q, int32_t token_budget, float sm_scale, int32_t* sel,
                                     int32_t sel_cap, int32_t* sel_count, void* out, float* lse, void* stream) {
     return select_decode_on(kv, map, cents, q, token_budget, sm_scale, sel, sel_cap, sel_count, out, lse, nullptr,
-                            kStaticScratchBytes, stream, scratch_of_current_device);
+                            kStaticScratchBytes, stream, scratch_of_current_device, Stages::All);
 }
 
 abs_status abs_describe_launch(const abs_paged_kv* kv, const abs_block_map* map, int32_t token_budget,

@@ -182,6 +182,7 @@ hipError_t launch_decode(const Geom& g, DType dt, const DecodeArgs& a, hipStream
 constexpr int kFusedThreads = 512;                 // the fused launch's workgroup: the top-K launch's width
 constexpr int kFusedTopkMaxN = kFusedThreads * 32;
 hipError_t launch_scores(const Geom& g, DType dt, const SelectArgs& a, hipStream_t s);
+hipError_t launch_topk(const Geom& g, const SelectArgs& a, hipStream_t s);   // the top-K launch alone
 bool select_decode_fusable(const Geom& g, DType dt, const SelectArgs& s, const DecodeArgs& a);
 hipError_t launch_select_decode(const Geom& g, DType dt, const SelectArgs& s, const DecodeArgs& a, hipStream_t st);
 

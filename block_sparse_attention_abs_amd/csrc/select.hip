@@ -245,13 +245,7 @@ void launch_score(const Geom& g, const SelectArgs& a, hipStream_t s) {
     }
 }
 
-template <typename T, int D>
-hipError_t select_impl(const Geom& g, const SelectArgs& a, bool with_topk, hipStream_t s) {
-    const int bits = fmt_bits(a.fmt);
-    if (bits == 8) launch_score<T, D, 8>(g, a, s);
-    else if (bits == 16) launch_score<T, D, 16>(g, a, s);
-    else launch_score<T, D, 4>(g, a, s);
-    if (!with_topk) return hipGetLastError();
+hipError_t topk_impl(const Geom& g, const SelectArgs& a, hipStream_t s) {
     const dim3 tgrid(g.B * g.Hkv);
 #define ABS_TOPK(NT_, KPT_)                                                                                  \
     hipLaunchKernelGGL((k_topk<NT_, KPT_>), tgrid, dim3(NT_), 0, s, g, a.scores, a.stride, a.ranges,            \
@@ -271,6 +265,17 @@ hipError_t select_impl(const Geom& g, const SelectArgs& a, bool with_topk, hipSt
     return hipGetLastError();
 }
 
+template <typename T, int D>
+hipError_t select_impl(const Geom& g, const SelectArgs& a, bool with_topk, hipStream_t s) {
+    const int bits = fmt_bits(a.fmt);
+    if (bits == 8) launch_score<T, D, 8>(g, a, s);
+    else if (bits == 16) launch_score<T, D, 16>(g, a, s);
+    else launch_score<T, D, 4>(g, a, s);
+    if (!with_topk) return hipGetLastError();
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    return topk_impl(g, a, s);
+}
+
 }  // namespace
 
 hipError_t launch_select(const Geom& g, DType dt, const SelectArgs& a, hipStream_t s) {
@@ -278,6 +283,8 @@ hipError_t launch_select(const Geom& g, DType dt, const SelectArgs& a, hipStream
         return g.D == 128 ? select_impl<uint16_t, 128>(g, a, true, s) : select_impl<uint16_t, 64>(g, a, true, s);
     return g.D == 128 ? select_impl<float, 128>(g, a, true, s) : select_impl<float, 64>(g, a, true, s);
 }
+
+hipError_t launch_topk(const Geom& g, const SelectArgs& a, hipStream_t s) { return topk_impl(g, a, s); }
 
 hipError_t launch_scores(const Geom& g, DType dt, const SelectArgs& a, hipStream_t s) {
     if (dt == DType::BF16)

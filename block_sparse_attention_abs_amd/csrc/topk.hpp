@@ -191,7 +191,7 @@ __device__ __forceinline__ int topk_rows(const Geom& g, int bh, const float* __r
         int slot[KPT];
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
-            slot[e] = e < nv ? min(kBins - 1, max(0, (int)fmaf(f[e], inv, c0))) + 1 : 0;
+            slot[e] = e < nv ? (int)fminf(fmaxf(fmaf(f[e], inv, c0), 0.0f), (float)(kBins - 1)) + 1 : 0;
             atomicAdd(&hist[slot[e]], 1u);
         }
         __syncthreads();

@@ -314,6 +314,29 @@ abs_status abs_select_decode(const abs_paged_kv *kv, const abs_block_map *map, c
                              size_t workspace_bytes, void *stream);
 
 /*
+ * abs_select_decode in two calls, one per side of the page's per-stage
+ * latency split (the figure after Figure 13: Estimation, then Top-K and
+ * Attention).  abs_estimate computes every block's score (the estimation of
+ * abs_score_select) into the select region of an abs_select_decode
+ * workspace; abs_topk_decode then runs the top-K and the sparse attention
+ * from those scores.  The two calls on one workspace, in this order on one
+ * stream, enqueue exactly the launches of abs_select_decode and give the
+ * same results bit for bit; in between, the workspace holds the scores of
+ * this layer and query (abs_topk_decode on any other contents gives
+ * undefined results).  Arguments as abs_select_decode; abs_estimate zero-fills
+ * the decode's arrival counters, so neither call needs a zero-filled
+ * workspace.
+ */
+abs_status abs_estimate(const abs_paged_kv *kv, const abs_block_map *map, const abs_centroids *cents,
+                        const void *q, int32_t token_budget, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+abs_status abs_topk_decode(const abs_paged_kv *kv, const abs_block_map *map, const void *q,
+                           int32_t token_budget, float sm_scale, int32_t *sel, int32_t sel_cap,
+                           int32_t *sel_count, void *out, float *lse, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/*
  * abs_select_decode without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  The library keeps one scratch array of

@@ -25,7 +25,7 @@ def header_functions():
 
 def test_exports_every_declared_call():
     names = header_functions()
-    assert len(names) == 19
+    assert len(names) == 21
     assert sorted(A.EXPORTS) == names
     L = A.lib()
     for n in names:
@@ -294,6 +294,31 @@ def test_static_scratch_call_rejects_layers_beyond_its_size():
                                                         FAKE, None, 0)) == I
     assert status_of(lambda: A.abs_select_decode_static(h.kv, h.bmap, h.cents, FAKE, 64, 0.125, FAKE, cap - 1,
                                                         FAKE, FAKE, None, 0)) == I
+
+
+def test_stage_calls_validation():
+    """abs_estimate needs the centroid store and q; abs_topk_decode needs q,
+    sel, sel_count, out, a large enough sel_cap and a finite sm_scale; both
+    the select + decode workspace."""
+    h = Host()
+    need = A.abs_workspace_bytes(h.kv, h.bmap, 64, A.ABS_OP_SELECT_DECODE)
+    cap = A.abs_select_capacity(h.kv, h.bmap, 64)
+    I, W = A.ABS_ERR_INVALID_ARG, A.ABS_ERR_WORKSPACE
+    assert status_of(lambda: A.abs_estimate(h.kv, h.bmap, None, FAKE, 64, FAKE, need, 0)) == I
+    assert status_of(lambda: A.abs_estimate(h.kv, h.bmap, h.cents, None, 64, FAKE, need, 0)) == I
+    assert status_of(lambda: A.abs_estimate(h.kv, h.bmap, h.cents, FAKE, 64, FAKE, need - 1, 0)) == W
+    assert status_of(lambda: A.abs_estimate(h.kv, h.bmap, h.cents, FAKE, 0, FAKE, need, 0)) == I
+    assert status_of(lambda: A.abs_topk_decode(h.kv, h.bmap, FAKE, 64, 0.125, FAKE, cap - 1, FAKE, FAKE, None, FAKE,
+                                               need, 0)) == I
+    assert status_of(lambda: A.abs_topk_decode(h.kv, h.bmap, FAKE, 64, 0.125, FAKE, cap, FAKE, None, None, FAKE,
+                                               need, 0)) == I
+    assert status_of(lambda: A.abs_topk_decode(h.kv, h.bmap, FAKE, 64, float("nan"), FAKE, cap, FAKE, FAKE, None,
+                                               FAKE, need, 0)) == I
+    assert status_of(lambda: A.abs_topk_decode(h.kv, h.bmap, FAKE, 64, 0.125, FAKE, cap, FAKE, FAKE, None, FAKE,
+                                               need - 1, 0)) == W
+    h.kv.v_cache = None
+    assert status_of(lambda: A.abs_topk_decode(h.kv, h.bmap, FAKE, 64, 0.125, FAKE, cap, FAKE, FAKE, None, FAKE,
+                                               need, 0)) == I
 
 
 def test_reset_and_debug_switch_validation():

@@ -105,7 +105,9 @@ def test_fused_equals_separate_calls_and_oracle(oracle_mod, case):
 
 @pytest.mark.parametrize("name,context,K,n10,n5", [("few-below", 4096, 32, 10, 50), ("edge-64", 4096, 32, 10, 64),
                                                     ("edge-65", 4096, 32, 10, 65), ("crowded", 4096, 32, 10, 200),
-                                                    ("overflow", 16384, 32, 0, 600)])
+                                                    ("overflow", 16384, 32, 0, 600),
+                                                    ("wide-crowded", 65536, 32, 10, 200),
+                                                    ("wide-overflow", 65536, 32, 0, 600)])
 def test_fused_ties(name, context, K, n10, n5):
     """Runs of equal scores at the threshold (the construction of
     test_gpu_topk_ties): the in-decode top-K takes the same ranked path,
@@ -161,3 +163,31 @@ def test_fused_in_a_graph_replays_like_eager():
         assert torch.equal(out, eager[2]) and torch.equal(lse, eager[3]) and torch.equal(cnt, eager[1])
         for (b, h), k in np.ndenumerate(eager[1].cpu().numpy()):
             assert torch.equal(sel[b, h, :k], eager[0][b, h, :k])
+
+
+@pytest.mark.parametrize("case", ["b2-16k", "b1-128k", "ragged-4k", "f32"])
+def test_estimate_then_topk_decode_equals_select_decode(case):
+    """abs_estimate + abs_topk_decode (the two halves of the per-stage split)
+    on one workspace make the launches of abs_select_decode: sel, sel_count,
+    out and lse bit for bit, on a fused layer and on layers that take the
+    separate launches; a workspace filled with stale bytes needs no reset."""
+    x = _case(case)
+    budget = x.workload.token_budget
+    sm = default_scale(x.q.shape[2])
+    g = GpuLayer(x)
+    g.build()
+    ws = A.workspace(g.kv.workspace_bytes(budget, A.ABS_OP_SELECT_DECODE))
+    want = _fused(g, budget, sm, ws)
+    B, Hq, D = x.q.shape
+    cap = g.kv.select_capacity(budget)
+    stale = torch.full((ws.numel(),), 0x7F, dtype=torch.uint8, device="cuda")
+    sel = torch.full((B, x.k_cache.shape[1], cap), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((B, x.k_cache.shape[1]), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, Hq, D), dtype=A.torch_dtype(x.dtype), device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    st = A.current_stream()
+    A.abs_estimate(g.kv.kv, g.kv.bmap, g.cents.desc, g.q.data_ptr(), budget, stale.data_ptr(), stale.numel(), st)
+    A.abs_topk_decode(g.kv.kv, g.kv.bmap, g.q.data_ptr(), budget, sm, sel.data_ptr(), cap, cnt.data_ptr(),
+                      out.data_ptr(), lse.data_ptr(), stale.data_ptr(), stale.numel(), st)
+    torch.cuda.synchronize()
+    _same((sel.cpu().numpy(), cnt.cpu().numpy(), to_host_f32(out), lse.cpu().numpy()), want)

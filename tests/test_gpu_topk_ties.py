@@ -26,7 +26,11 @@ CASES = [("few-below", 4096, 32, 10, 50),     # threshold bin = the a=5 group: 5
          ("edge-64", 4096, 32, 10, 64),       # 64 candidates: the most one wavefront ranks
          ("edge-65", 4096, 32, 10, 65),       # 65: ranked through LDS by the candidates' threads
          ("crowded", 4096, 32, 10, 200),      # 200 candidates
-         ("overflow", 16384, 32, 0, 600)]     # more than the candidate list holds: radix select
+         ("overflow", 16384, 32, 0, 600),     # more than the candidate list holds: radix select
+         # 4096 blocks per head (8 keys per thread): the same three paths
+         ("wide-few", 65536, 32, 10, 50),
+         ("wide-crowded", 65536, 32, 10, 200),
+         ("wide-overflow", 65536, 32, 0, 600)]
 
 
 def _layer(context, K, n10, n5, dtype, seed):
