@@ -783,8 +783,8 @@ __global__ __launch_bounds__(256, 2) void k_sparse_decode_ws(Geom g, const uint1
 // at the positions its pages cover, and decodes them with wavefronts 0-3;
 // split 0 also writes sel and sel_count.  The workgroups of a head compute
 // the same selection from the same row.
-template <int GT, int KPT>
-__global__ __launch_bounds__(512) void k_select_decode_ws(Geom g, const float* __restrict__ scores, int stride,
+template <int NT, int GT, int KPT>
+__global__ __launch_bounds__(NT) void k_select_decode_ws(Geom g, const float* __restrict__ scores, int stride,
                                                           const float2* __restrict__ ranges, int range_stride,
                                                           int max_len, int budget, int32_t* __restrict__ sel,
                                                           int sel_cap, int32_t* __restrict__ count,
@@ -813,17 +813,18 @@ __global__ __launch_bounds__(512) void k_select_decode_ws(Geom g, const float* _
     const float2* rrow = ranges + (int64_t)bh * range_stride;
     const int nh = shr_ceil(max_len, sb);
     int K;
-    if (KPT > 4 && nh <= kFusedThreads * 4)
-        K = topk_rows<kFusedThreads, 4>(g, bh, srow, stride, rrow, max_len, budget, emit);
-    else if (KPT > 8 && nh <= kFusedThreads * 8)
-        K = topk_rows<kFusedThreads, (KPT > 8 ? 8 : KPT)>(g, bh, srow, stride, rrow, max_len, budget, emit);
+    constexpr int K4 = KPT >= 16 ? KPT / 4 : KPT, K2 = KPT >= 8 ? KPT / 2 : KPT;
+    if (KPT > K4 && nh <= NT * K4)
+        K = topk_rows<NT, K4>(g, bh, srow, stride, rrow, max_len, budget, emit);
+    else if (KPT > K2 && nh <= NT * K2)
+        K = topk_rows<NT, K2>(g, bh, srow, stride, rrow, max_len, budget, emit);
     else
-        K = topk_rows<kFusedThreads, KPT>(g, bh, srow, stride, rrow, max_len, budget, emit);
+        K = topk_rows<NT, KPT>(g, bh, srow, stride, rrow, max_len, budget, emit);
     if (split == 0 && threadIdx.x == 0) count[bh] = K;
     __syncthreads();
     const int gp = split * ppw + (int)(threadIdx.x & 63);
     const int sv = s_blk[min(max((gp >> sh) - first, 0), kMaxPagesPerWg - 1)];   // positions >= K: unused
-    ws_decode<GT, kFusedThreads / 64>(g, q, sv, min(K, sel_cap), sel_cap, qscale, part_ml, part_o, splits, ppw,
+    ws_decode<GT, NT / 64>(g, q, sv, min(K, sel_cap), sel_cap, qscale, part_ml, part_o, splits, ppw,
                                       ppw_magic, arrive, out, lse);
 }
 
@@ -967,20 +968,26 @@ bool select_decode_fusable(const Geom& g, DType dt, const SelectArgs& s, const D
 
 namespace {
 
-template <int GT, int KPT>
+template <int NT, int GT, int KPT>
 void launch_fused(const Geom& g, const SelectArgs& s, const DecodeArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((k_select_decode_ws<GT, KPT>), dim3(a.splits, g.B * g.Hkv), dim3(kFusedThreads), 0, st, g, s.scores,
+    hipLaunchKernelGGL((k_select_decode_ws<NT, GT, KPT>), dim3(a.splits, g.B * g.Hkv), dim3(NT), 0, st, g, s.scores,
                        s.stride, s.ranges, s.range_stride, s.max_len, s.budget, s.sel, s.sel_cap, s.count,
                        reinterpret_cast<const uint16_t*>(a.q), a.sm_scale * kLog2e, a.part_ml, a.part_o, a.splits,
                        a.pages_per_wg, a.ppw_magic, a.arrive, reinterpret_cast<uint16_t*>(a.out), a.lse);
 }
 
+// Heads of at most kFusedSmallMaxN blocks: 256 threads (the decode's
+// wavefronts alone), measured faster there (-0.4 to -0.8 us per step at
+// 32K x 1, 32K x 16 and 64K x 8); larger heads: 512 threads, whose top-K the
+// eight wavefronts share (1.2 us faster at 128K x 4, where one head has 8192
+// blocks).
 template <int GT>
 void launch_fused_gt(const Geom& g, const SelectArgs& s, const DecodeArgs& a, hipStream_t st) {
-    if (s.max_n <= kFusedThreads * 4) launch_fused<GT, 4>(g, s, a, st);
-    else if (s.max_n <= kFusedThreads * 8) launch_fused<GT, 8>(g, s, a, st);
-    else if (s.max_n <= kFusedThreads * 16) launch_fused<GT, 16>(g, s, a, st);
-    else launch_fused<GT, 32>(g, s, a, st);
+    if (s.max_n <= 256 * 4) launch_fused<256, GT, 4>(g, s, a, st);
+    else if (s.max_n <= 256 * 8) launch_fused<256, GT, 8>(g, s, a, st);
+    else if (s.max_n <= kFusedSmallMaxN) launch_fused<256, GT, 16>(g, s, a, st);
+    else if (s.max_n <= kFusedThreads * 16) launch_fused<kFusedThreads, GT, 16>(g, s, a, st);
+    else launch_fused<kFusedThreads, GT, 32>(g, s, a, st);
 }
 
 }  // namespace

@@ -179,7 +179,11 @@ hipError_t launch_decode(const Geom& g, DType dt, const DecodeArgs& a, hipStream
 // abs_select_decode: the score launch alone (launch_scores), then one launch
 // that runs the top-K inside the split decode (launch_select_decode), when
 // select_decode_fusable(); otherwise launch_select and launch_decode.
-constexpr int kFusedThreads = 512;                 // the fused launch's workgroup: the top-K launch's width
+// The fused launch's workgroup: 256 threads (the decode's four wavefronts)
+// when every head has at most kFusedSmallMaxN blocks, else 512 (eight
+// wavefronts share the top-K of larger heads; four of them decode).
+constexpr int kFusedThreads = 512;
+constexpr int kFusedSmallMaxN = 256 * 16;
 constexpr int kFusedTopkMaxN = kFusedThreads * 32;
 hipError_t launch_scores(const Geom& g, DType dt, const SelectArgs& a, hipStream_t s);
 hipError_t launch_topk(const Geom& g, const SelectArgs& a, hipStream_t s);   // the top-K launch alone
