@@ -175,6 +175,7 @@ def main():
                                               xr.dtype, dev))
             qs.append(A.upload(xr.q, dev, xr.dtype))
             del xr
+            print(f"[bench] layer {r + 1}/{R} uploaded ({time.time() - t0:.1f}s)", file=sys.stderr, flush=True)
         else:
             layers.append(A.PagedKV(base.k_cache.clone(), base.v_cache.clone(), base.page_table, base.seq_lens,
                                     base.seq_lens_host, base.block_size, base.block_size_host, base.centroid_off,

@@ -93,10 +93,10 @@ __device__ __forceinline__ void rank_in_wave(const float* s_val, const int32_t* 
 //      degenerate range takes an 8-bit radix select over the keys instead;
 //   4. keep the keys above b*, and those in b* ranked up to the threshold;
 //      a block scan gives the kept indices' positions in ascending order.
-// Every per-key step works on bit masks without branches (padding keys go to
-// a sink slot below the scanned bins), and the kept keys are emitted by a
-// loop over the set bits of the keep mask, so the cost per thread grows with
-// KPT by a few instructions per key.
+// Every per-key step works on bit masks without branches (padding keys take
+// a slot below the scanned bins and count into spill slots past them), and
+// the kept keys are emitted by a loop over the set bits of the keep mask, so
+// the cost per thread grows with KPT by a few instructions per key.
 template <int NT, int KPT, class Emit>
 __device__ __forceinline__ int topk_rows(const Geom& g, int bh, const float* __restrict__ row, int stride,
                                          const float2* __restrict__ ranges, int max_len, int budget, Emit&& emit) {
@@ -139,14 +139,14 @@ __device__ __forceinline__ int topk_rows(const Geom& g, int bh, const float* __r
 
     const int L = seq_len(g, b);                      // issued with the loads above
 
-    __shared__ uint32_t hist[kBins + 1];              // slot 0: sink of padding keys; bin i -> slot i + 1
+    __shared__ uint32_t hist[kBins + 1 + 64];         // bin i -> slot i + 1; then one padding spill slot per lane
     __shared__ uint32_t s_wave[3][NW];                // one per scan: no barrier between reuses
     __shared__ float s_cand_val[kCandCap];
     __shared__ int32_t s_cand_idx[kCandCap];
     __shared__ uint32_t s_bin, s_above, s_ncand;
     __shared__ float s_tau_f;
     __shared__ int32_t s_tau_idx;
-    for (int i = threadIdx.x; i <= kBins; i += NT) hist[i] = 0u;
+    for (int i = threadIdx.x; i <= kBins + 64; i += NT) hist[i] = 0u;
     if (threadIdx.x == 0) s_ncand = 0u;
     __syncthreads();                                  // (the loads above are still in flight)
 
@@ -156,8 +156,9 @@ __device__ __forceinline__ int topk_rows(const Geom& g, int bh, const float* __r
         for (int j = threadIdx.x; j < N; j += NT) emit((uint32_t)j, (int32_t)j);
         return K;
     }
-    // padding keys (e >= nv, at most one partial thread) become -inf: below
-    // every score (finite), so no later comparison needs to test e < nv
+    // padding keys (e >= nv: the tail of one thread, and every key of the
+    // threads past the row) become -inf: below every score (finite), so no
+    // later comparison needs to test e < nv
     const int nv = min(max(N - base, 0), KPT);
     if (nv < KPT) {
 #pragma unroll
@@ -186,13 +187,16 @@ __device__ __forceinline__ int topk_rows(const Geom& g, int bh, const float* __r
     bool resolved = false;
     if (binned) {
         // slot of a key: monotone non-decreasing in the score (one fma then a
-        // truncation); padding keys go to the sink slot 0
+        // truncation); padding keys take slot 0, below every bin, and count
+        // into their lane's own spill slot past the bins: no branch, and no
+        // LDS address taking the atomics of whole wavefronts of padding
+        // (those serialize, 64 cycles per instruction)
         const float c0 = -mn * inv;
         int slot[KPT];
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
             slot[e] = e < nv ? (int)fminf(fmaxf(fmaf(f[e], inv, c0), 0.0f), (float)(kBins - 1)) + 1 : 0;
-            atomicAdd(&hist[slot[e]], 1u);
+            atomicAdd(&hist[e < nv ? slot[e] : kBins + 1 + lane], 1u);
         }
         __syncthreads();
         // thread t sums the bins of slots kBins - t*BPT ... downwards; scan from the top
