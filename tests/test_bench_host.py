@@ -59,3 +59,52 @@ def test_traffic_key_covers_every_decode_source():
     assert srcs <= set(bench.KERNEL_SOURCES), srcs - set(bench.KERNEL_SOURCES)
     h = bench.kernel_source_hash()
     assert re.fullmatch(r"[0-9a-f]{16}", h)
+
+
+def _counter_csv(path, rows):
+    import csv
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for r in rows:
+            w.writerow(r)
+
+
+def test_traffic_summary_scales_by_the_copy_and_counts_requests(tmp_path, capsys):
+    # counter files of a made-up command: a copy of 1 MiB (three dispatches)
+    # and two dispatches of a kernel; FETCH_SIZE reads half a copy's bytes
+    from block_sparse_attention_abs_amd import traffic
+    copy, kern = "__amd_rocclr_copyBuffer", "void absk::k_demo<4>(int)"
+    mib = 1 << 20
+    _counter_csv(tmp_path / "f.csv", [(1, copy, "FETCH_SIZE", 512), (2, copy, "FETCH_SIZE", 512),
+                                      (3, copy, "FETCH_SIZE", 512), (4, kern, "FETCH_SIZE", 100),
+                                      (5, kern, "FETCH_SIZE", 300)])
+    _counter_csv(tmp_path / "w.csv", [(1, copy, "WRITE_SIZE", 1024), (2, copy, "WRITE_SIZE", 1024),
+                                      (3, copy, "WRITE_SIZE", 1024), (4, kern, "WRITE_SIZE", 10),
+                                      (5, kern, "WRITE_SIZE", 30)])
+    req = []
+    for d in (1, 2, 3):
+        req += [(d, copy, "TCC_EA0_RDREQ_32B", 0), (d, copy, "TCC_EA0_RDREQ_64B", 0),
+                (d, copy, "TCC_EA0_RDREQ_128B", mib // 128), (d, copy, "TCC_EA0_RDREQ", mib // 128)]
+    # the kernel's two dispatches: 10 x 32 B + 20 x 64 B + 1000 x 128 B, and 3x that
+    for d, k in ((4, 1), (5, 3)):
+        req += [(d, kern, "TCC_EA0_RDREQ_32B", 10 * k), (d, kern, "TCC_EA0_RDREQ_64B", 20 * k),
+                (d, kern, "TCC_EA0_RDREQ_128B", 1000 * k), (d, kern, "TCC_EA0_RDREQ", 1030 * k)]
+    _counter_csv(tmp_path / "r.csv", req)
+    import sys as _sys
+    argv = _sys.argv
+    _sys.argv = ["traffic", "bytes", str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "--copy-bytes", str(mib),
+                 "--rdreq", str(tmp_path / "r.csv")]
+    try:
+        traffic.main()
+    finally:
+        _sys.argv = argv
+    out = capsys.readouterr().out
+    assert "scale 2.0000 (read), 1.0000 (write)" in out
+    assert f"by read requests (32/64/128 B): {mib} B (1.0000" in out
+    row = [l for l in out.splitlines() if l.startswith("| k_demo<4>")][0].split("|")
+    cells = [c.strip() for c in row[1:-1]]
+    # mean FETCH 200 KiB x 2 = 409600 B read; mean WRITE 20 KiB = 20480 B written
+    assert cells[1] == "2" and cells[4] == "409600" and cells[5] == "20480" and cells[6] == "430080"
+    # request bytes: mean over the two dispatches of (320 + 1280 + 128000) x k, k = 1 and 3
+    assert cells[7] == str(2 * (320 + 1280 + 128000))
