@@ -495,7 +495,7 @@ __global__ __launch_bounds__(256 * RG, (DecodeOccupancy<T, D, GT, PIPE, MF>::val
 // clamped into the row) of a head with K selected blocks; NW wavefronts in
 // the workgroup, of which 0-3 do the work.
 template <int GT, int NW>
-__device__ __forceinline__ void ws_decode(const Geom& g, const uint16_t* __restrict__ q, int sv, int K, int sel_cap,
+__device__ __forceinline__ void ws_decode(const Geom& g, const uint16_t* __restrict__ q, int L, int sv, int K, int sel_cap,
                                           float qscale, float* __restrict__ part_ml, float* __restrict__ part_o,
                                           int splits, int ppw, uint32_t ppw_magic, int32_t* __restrict__ arrive,
                                           uint16_t* __restrict__ out, float* __restrict__ lse) {
@@ -518,7 +518,6 @@ __device__ __forceinline__ void ws_decode(const Geom& g, const uint16_t* __restr
     const int p0 = split * ppw;                        // ppw <= 64
     const int gp = p0 + wl;
     const bool in_row = wl < ppw && gp < sel_cap * spb;
-    const int L = seq_len(g, b);
     const int npages = shr_ceil(L, 4);
     const int N = shr_ceil(L, sh + 4);
     const int total = min(K * spb, splits * ppw);      // selected pages of (b, h)
@@ -774,7 +773,8 @@ __global__ __launch_bounds__(256, 2) void k_sparse_decode_ws(Geom g, const uint1
     const int gp = blockIdx.x * ppw + (int)(threadIdx.x & 63);
     const int sv = sel[(int64_t)bh * sel_cap + min(gp >> sh, sel_cap - 1)];   // unconditional, clamped
     const int K = min(max(count[bh], 0), sel_cap);
-    ws_decode<GT, 4>(g, q, sv, K, sel_cap, qscale, part_ml, part_o, splits, ppw, ppw_magic, arrive, out, lse);
+    ws_decode<GT, 4>(g, q, seq_len(g, b), sv, K, sel_cap, qscale, part_ml, part_o, splits, ppw, ppw_magic, arrive,
+                     out, lse);
 }
 
 // Top-K and decode in one launch (abs_select_decode): every split workgroup
@@ -812,20 +812,20 @@ __global__ __launch_bounds__(NT) void k_select_decode_ws(Geom g, const float* __
     const float* srow = scores + (int64_t)bh * stride;
     const float2* rrow = ranges + (int64_t)bh * range_stride;
     const int nh = shr_ceil(max_len, sb);
-    int K;
+    int K, L;
     constexpr int K4 = KPT >= 16 ? KPT / 4 : KPT, K2 = KPT >= 8 ? KPT / 2 : KPT;
     if (KPT > K4 && nh <= NT * K4)
-        K = topk_rows<NT, K4>(g, bh, srow, stride, rrow, max_len, budget, emit);
+        K = topk_rows<NT, K4>(g, bh, srow, stride, rrow, max_len, budget, emit, L);
     else if (KPT > K2 && nh <= NT * K2)
-        K = topk_rows<NT, K2>(g, bh, srow, stride, rrow, max_len, budget, emit);
+        K = topk_rows<NT, K2>(g, bh, srow, stride, rrow, max_len, budget, emit, L);
     else
-        K = topk_rows<NT, KPT>(g, bh, srow, stride, rrow, max_len, budget, emit);
+        K = topk_rows<NT, KPT>(g, bh, srow, stride, rrow, max_len, budget, emit, L);
     if (split == 0 && threadIdx.x == 0) count[bh] = K;
     __syncthreads();
     const int gp = split * ppw + (int)(threadIdx.x & 63);
     const int sv = s_blk[min(max((gp >> sh) - first, 0), kMaxPagesPerWg - 1)];   // positions >= K: unused
-    ws_decode<GT, NT / 64>(g, q, sv, min(K, sel_cap), sel_cap, qscale, part_ml, part_o, splits, ppw,
-                                      ppw_magic, arrive, out, lse);
+    ws_decode<GT, NT / 64>(g, q, L, sv, min(K, sel_cap), sel_cap, qscale, part_ml, part_o, splits, ppw,
+                           ppw_magic, arrive, out, lse);
 }
 
 // One workgroup per (b, query head): merge the partials of the splits that

@@ -113,6 +113,7 @@ struct Elem<float> {
     template <int NW>
     __device__ static __forceinline__ float get(const Words<NW>& w, int e) { return __uint_as_float(w.w[e]); }
     __device__ static __forceinline__ float load1(const float* p) { return *p; }
+    __device__ static __forceinline__ float cvt(float v) { return v; }
     __device__ static __forceinline__ void store1(float* p, float v) { *p = v; }
 };
 
@@ -124,6 +125,7 @@ struct Elem<uint16_t> {  // bf16 bit patterns
         return (e & 1) ? bf16_hi(w.w[e >> 1]) : bf16_lo(w.w[e >> 1]);
     }
     __device__ static __forceinline__ float load1(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
+    __device__ static __forceinline__ float cvt(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
     __device__ static __forceinline__ void store1(uint16_t* p, float v) { *p = (uint16_t)f32_to_bf16(v); }
 };
 

@@ -31,6 +31,23 @@ struct Geom {
 // (which sized every buffer and grid) cannot index past them.
 __device__ __forceinline__ int seq_len(const Geom& g, int b) { return min(max(g.seq_lens[b], 1), g.max_len); }
 
+// The same length read by a vector load, for kernels with a workgroup
+// barrier before its first use: a barrier waits for every scalar load in
+// flight, a vector load only where its value is used.  seq_len_issue()
+// issues the load (the offset is an opaque zero in a vector register, so
+// the load cannot be made scalar), seq_len_use() takes the value, uniform;
+// its empty volatile statement keeps the wait for the load after any
+// barrier that precedes the call.
+__device__ __forceinline__ int seq_len_issue(const Geom& g, int b) {
+    int zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+    return g.seq_lens[b + zero];
+}
+__device__ __forceinline__ int seq_len_use(const Geom& g, int issued) {
+    asm volatile("" : "+v"(issued));
+    return min(max(__builtin_amdgcn_readfirstlane(issued), 1), g.max_len);
+}
+
 // Centroid rows of (b, h) = bh that the kernels touch: its N blocks, capped
 // by the rows the offsets give it (so that a device length that disagrees
 // with the host's cannot index past the centroid store).
@@ -42,12 +59,14 @@ __device__ __forceinline__ int centroid_rows(const Geom& g, int bh, int N) {
 // magic = ceil(2^32 / d), floor(n / d) = (n * magic) >> 32 for 0 <= n < 2^26
 // (the rounding of the magic, n * (magic - 2^32 / d) < n * d / 2^32, stays
 // below 1/d, the smallest gap between n/d and the next integer).  d = 1 has
-// magic 0 and is taken apart.
+// magic 0: the product vanishes and n is added back by a select, not a
+// branch (a branch here splits the kernel's entry block, and the kernel
+// argument loads after it then wait for a second round trip).
 __host__ __device__ constexpr uint32_t div_magic(int d) {
     return d <= 1 ? 0u : (uint32_t)(((uint64_t)1 << 32) / (uint64_t)d + (((uint64_t)1 << 32) % (uint64_t)d != 0));
 }
 __device__ __forceinline__ int fast_div(int n, int d, uint32_t magic) {
-    return d == 1 ? n : (int)__umulhi((uint32_t)n, magic);
+    return (int)(__umulhi((uint32_t)n, magic) + (d == 1 ? (uint32_t)n : 0u));
 }
 
 // (b, h) of a flat index bh = b * Hkv + h.

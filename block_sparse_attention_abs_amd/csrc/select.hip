@@ -49,26 +49,38 @@ __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restr
     static_assert(NT >= D, "one thread per channel folds the query");
     int b, h;
     split_bh(g, bh, b, h);
-    const int64_t row0 = g.off[bh];
-    const int N = centroid_rows(g, bh, shr_ceil(seq_len(g, b), block_shift_of(g, h)));
     const int j0 = tile * kScoreBlocksPerWg;
     const int sub = threadIdx.x % LPB;
     const int grp = threadIdx.x / LPB;
 
     // Every load below is unconditional (offsets clamped), so all of them are
-    // in flight together and none waits on a branch; the query group, scale
-    // and lo go first, so that the fold below waits only for them.  A tile
-    // past the end of a shorter sequence (j0 >= N, in the per-sequence grid)
-    // runs through and stores nothing.
+    // in flight together and none waits on a branch.  First the row's bounds
+    // (centroid offsets and length) by vector loads, then the query group,
+    // scale and lo, which need only (b, h) and so go out at once, then the
+    // code rows, which wait for the bounds only (scalar loads of the bounds
+    // would put a round trip before every load, and barriers wait for them).
+    // A tile past the end of a shorter sequence (j0 >= N, in the per-sequence
+    // grid) runs through and stores nothing.
+    int zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+    const int64_t off0 = g.off[bh + zero], off1 = g.off[bh + 1 + zero];
+    const int len = g.seq_lens[b + zero];
     const int dch = min((int)threadIdx.x, D - 1);    // this thread's channel (threads < D)
-    float qv[GT], sc = 0.0f, zp = 0.0f;
+    T qraw[GT];                                       // converted after the code loads are out
+    float sc = 0.0f, zp = 0.0f;
 #pragma unroll
-    for (int gg = 0; gg < GT; ++gg)
-        qv[gg] = Elem<T>::load1(q + ((int64_t)b * g.Hq + h * g.G + min(gg, g.G - 1)) * D + dch);
+    for (int gg = 0; gg < GT; ++gg) qraw[gg] = q[((int64_t)b * g.Hq + h * g.G + min(gg, g.G - 1)) * D + dch];
     if constexpr (BITS != 16) {
         sc = scale[(int64_t)bh * D + dch];
         zp = lo[(int64_t)bh * D + dch];
     }
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t row0 = (int64_t)__builtin_amdgcn_readfirstlane((int)off0) |
+                         ((int64_t)__builtin_amdgcn_readfirstlane((int)(off0 >> 32)) << 32);
+    const int64_t rows = ((int64_t)__builtin_amdgcn_readfirstlane((int)off1) |
+                          ((int64_t)__builtin_amdgcn_readfirstlane((int)(off1 >> 32)) << 32)) - row0;
+    const int L = min(max(__builtin_amdgcn_readfirstlane(len), 1), g.max_len);
+    const int N = (int)min((int64_t)shr_ceil(L, block_shift_of(g, h)), rows);   // as centroid_rows()
     // RPL block rows per lane group, GPW consecutive rows per step (contiguous
     // runs); a row at or beyond N reads row N - 1 again (N >= 1) and is not
     // stored
@@ -99,7 +111,7 @@ __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restr
         for (int gg = 0; gg < GT; ++gg) {
             uint32_t keep = gg < g.G ? ~0u : 0u;
             asm volatile("" : "+v"(keep));
-            qbar += (double)__uint_as_float(__float_as_uint(qv[gg]) & keep);
+            qbar += (double)__uint_as_float(__float_as_uint(Elem<T>::cvt(qraw[gg])) & keep);
         }
         const int slot = threadIdx.x + threadIdx.x / CPL;
         w[slot] = BITS == 16 ? qbar : qbar * (double)sc;
@@ -209,11 +221,12 @@ __global__ __launch_bounds__(NT) void k_topk(Geom g, const float* __restrict__ s
                                              int32_t* __restrict__ count) {
     const int bh = blockIdx.x;
     int32_t* out = sel + (int64_t)bh * sel_cap;
+    int L;
     const int K = topk_rows<NT, KPT>(g, bh, scores + (int64_t)bh * stride, stride,
                                      ranges + (int64_t)bh * range_stride, max_len, budget,
                                      [&](uint32_t p, int32_t j) {
                                          if (p < (uint32_t)sel_cap) out[p] = j;
-                                     });
+                                     }, L);
     if (threadIdx.x == 0) count[bh] = K;
 }
 

@@ -99,17 +99,19 @@ __device__ __forceinline__ void rank_in_wave(const float* s_val, const int32_t* 
 // the cost per thread grows with KPT by a few instructions per key.
 template <int NT, int KPT, class Emit>
 __device__ __forceinline__ int topk_rows(const Geom& g, int bh, const float* __restrict__ row, int stride,
-                                         const float2* __restrict__ ranges, int max_len, int budget, Emit&& emit) {
+                                         const float2* __restrict__ ranges, int max_len, int budget, Emit&& emit,
+                                         int& L) {
     using Mask = KeyMask<KPT>;
     constexpr int NW = NT / 64;
     int b, h;
     split_bh(g, bh, b, h);
     const int sb = block_shift_of(g, h);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int len_issued = seq_len_issue(g, b);       // first: its wait does not take the loads below
 
     // Thread t owns indices [t*KPT, t*KPT + nv).  Its scores and the tile
     // ranges are loaded before the row length is known (that takes a read of
-    // seq_lens), so the reads overlap.  The loads are unconditional, their
+    // seq_lens, issued first), so the reads overlap.  The loads are unconditional, their
     // offsets clamped to the head's longest row (keys: rounded up to a
     // multiple of 4, at least N, at most the stride): a clamped slot is at or
     // beyond N and never used.
@@ -137,7 +139,6 @@ __device__ __forceinline__ int topk_rows(const Geom& g, int bh, const float* __r
 #pragma unroll
     for (int k = 0; k < RL; ++k) rr[k] = ranges[min(lane + 64 * k, tiles_max - 1)];
 
-    const int L = seq_len(g, b);                      // issued with the loads above
 
     __shared__ uint32_t hist[kBins + 1 + 64];         // bin i -> slot i + 1; then one padding spill slot per lane
     __shared__ uint32_t s_wave[3][NW];                // one per scan: no barrier between reuses
@@ -150,6 +151,7 @@ __device__ __forceinline__ int topk_rows(const Geom& g, int bh, const float* __r
     if (threadIdx.x == 0) s_ncand = 0u;
     __syncthreads();                                  // (the loads above are still in flight)
 
+    L = seq_len_use(g, len_issued);
     const int N = shr_ceil(L, sb);
     const int K = min(N, max(1, budget >> sb));
     if (K >= N) {
