@@ -65,8 +65,8 @@ __device__ __forceinline__ int centroid_rows(const Geom& g, int bh, int N) {
 __host__ __device__ constexpr uint32_t div_magic(int d) {
     return d <= 1 ? 0u : (uint32_t)(((uint64_t)1 << 32) / (uint64_t)d + (((uint64_t)1 << 32) % (uint64_t)d != 0));
 }
-__device__ __forceinline__ int fast_div(int n, int d, uint32_t magic) {
-    return (int)(__umulhi((uint32_t)n, magic) + (d == 1 ? (uint32_t)n : 0u));
+__host__ __device__ __forceinline__ constexpr int fast_div(int n, int d, uint32_t magic) {
+    return (int)((uint32_t)(((uint64_t)(uint32_t)n * magic) >> 32) + (d == 1 ? (uint32_t)n : 0u));
 }
 
 // (b, h) of a flat index bh = b * Hkv + h.

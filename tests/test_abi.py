@@ -384,3 +384,21 @@ def test_host_calls_from_plain_c(tmp_path):
     assert int(got["status_capacity"][0]) == A.ABS_ERR_INVALID_ARG
     assert int(got["status_budget"][0]) == A.ABS_ERR_INVALID_ARG
     assert got["last_error_nonempty"] == ["1"]
+
+
+def test_division_without_division_is_exact(tmp_path):
+    """The kernels divide flat indices by Hkv and by the pages per workgroup
+    with a multiply by a magic number (div_magic / fast_div, launch.hpp);
+    tests/c/div_magic.cpp checks it against integer division for every
+    divisor 1..64 and every dividend below 2^26, on the host."""
+    import shutil
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not found")
+    exe = tmp_path / "div_magic"
+    subprocess.run([hipcc, "-O2", "-std=c++17", "--offload-arch=gfx950", "-I",
+                    os.path.join(ROOT, "block_sparse_attention_abs_amd", "csrc"),
+                    os.path.join(ROOT, "tests", "c", "div_magic.cpp"), "-o", str(exe)], check=True,
+                   capture_output=True, timeout=600)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
