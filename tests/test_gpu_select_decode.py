@@ -5,8 +5,9 @@ The fused launch runs the same selection (the top-K launch's code, 512
 threads per head) and the same decode arithmetic on the same pages, so sel,
 sel_count, out and lse must equal the separate calls' bit for bit.
 Layers the fused launch does not serve (fp32, head_dim 64, 8-head groups,
-16384 blocks in every head) run the separate launches and must give the
-same results too.  Against the oracle: the selection rule and the attention
+16384 blocks in every head, and small layers whose split decode holds
+fewer than 8 pages per workgroup) run the separate launches and must give
+the same results too; each case asserts which form it gets.  Against the oracle: the selection rule and the attention
 tolerances of gpu_pipeline.
 """
 import numpy as np
@@ -35,7 +36,13 @@ def _case(name):
         return W.make_layer(P[1].scaled(context=65536, fixed_block_sizes=(16,) * 8))
     if name == "gqa2":
         return W.make_layer(P[1].scaled(num_q_heads=16, batch=2, context=6000), seq_lens=[6000, 2500])
-    if name == "budget-covers":                # K = N: every block selected
+    if name == "gqa1":                         # one query head per KV head
+        return W.make_layer(P[1].scaled(num_q_heads=8, batch=2, context=5000), seq_lens=[5000, 1800])
+    if name == "b1-128k-mixed":                # 512 threads; heads of 8192, 4096 and 2048 blocks: 16, 8 and 4 keys
+        return W.make_layer(P[3].scaled(batch=1, fixed_block_sizes=(16, 32, 64, 32, 64, 16, 32, 64)))
+    if name == "dense-short":                  # fused; the short sequence has K = N (every block selected)
+        return W.make_layer(P[2].scaled(batch=2, context=16384), seq_lens=[16384, 500])
+    if name == "budget-covers":                # K = N: every block selected (a small layer: separate launches)
         return W.make_layer(P[1].scaled(batch=2, context=1000, token_budget=4096), seq_lens=[1000, 333])
     # not served by the fused launch
     if name == "f32":
@@ -49,8 +56,10 @@ def _case(name):
     raise KeyError(name)
 
 
-CASES = ["b2-16k", "ragged-4k", "b1-128k", "b1-256k", "b1-64k-bs16", "gqa2", "budget-covers", "f32", "d64",
-         "gqa8", "b1-256k-bs16"]
+CASES = ["b2-16k", "ragged-4k", "b1-128k", "b1-256k", "b1-64k-bs16", "gqa2", "gqa1", "b1-128k-mixed",
+         "dense-short", "budget-covers", "f32", "d64", "gqa8", "b1-256k-bs16"]
+# layers abs_select_decode runs as the separate launches (on a device of 256 compute units)
+SEPARATE = {"ragged-4k", "budget-covers", "f32", "d64", "gqa8", "b1-256k-bs16"}
 
 
 def _fused(g, budget, sm, ws):
@@ -84,6 +93,9 @@ def test_fused_equals_separate_calls_and_oracle(oracle_mod, case):
     print(f"[gpu select_decode] {case}: B={x.q.shape[0]} Hq={x.q.shape[1]} Hkv={x.k_cache.shape[1]} "
           f"D={x.q.shape[2]} lens={x.seq_lens.tolist()} bs={x.block_size.tolist()} {x.dtype}", flush=True)
     g = GpuLayer(x)
+    plan = g.kv.launch_plan(budget)
+    if plan["compute_units"] == 256:               # the launch choice depends on the device's CU count
+        assert plan["fused"] == (0 if case in SEPARATE else 1), plan
     g.build()
     sel, cnt = g.select(budget)
     out, lse = g.decode(sel, cnt, budget, sm)
@@ -103,21 +115,29 @@ def test_fused_equals_separate_calls_and_oracle(oracle_mod, case):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("name,context,K,n10,n5", [("few-below", 4096, 32, 10, 50), ("edge-64", 4096, 32, 10, 64),
-                                                    ("edge-65", 4096, 32, 10, 65), ("crowded", 4096, 32, 10, 200),
-                                                    ("overflow", 16384, 32, 0, 600),
-                                                    ("wide-crowded", 65536, 32, 10, 200),
-                                                    ("wide-overflow", 65536, 32, 0, 600)])
+@pytest.mark.parametrize("name,context,K,n10,n5", [("few-below", 16384, 128, 100, 50),
+                                                    ("edge-64", 16384, 128, 100, 64),
+                                                    ("edge-65", 16384, 128, 100, 65),
+                                                    ("crowded", 16384, 128, 100, 200),
+                                                    ("overflow", 16384, 128, 0, 600),
+                                                    ("wide-crowded", 65536, 128, 100, 200),
+                                                    ("wide-overflow", 65536, 128, 0, 600)])
 def test_fused_ties(name, context, K, n10, n5):
     """Runs of equal scores at the threshold (the construction of
-    test_gpu_topk_ties): the in-decode top-K takes the same ranked path,
-    crowded-bin path or radix path as the top-K launch."""
+    test_gpu_topk_ties, with K = 128 so that each head's 128 pages give the
+    split decode 8 per workgroup and the layer takes the fused launch): the
+    in-decode top-K takes the same ranked path (at most 64 tied
+    candidates), LDS ranking (65-512) or radix path (more) as the top-K
+    launch."""
     from test_gpu_topk_ties import _layer
     x, groups = _layer(context, K, n10, n5, "bf16", seed=context + n5)
     budget = 16 * K
     sm = default_scale(x.q.shape[2])
     print(f"[gpu select_decode] ties {name}", flush=True)
     g = GpuLayer(x)
+    plan = g.kv.launch_plan(budget)
+    if plan["compute_units"] == 256:
+        assert plan["fused"] == 1, plan
     g.build()
     sel, cnt = g.select(budget)
     out, lse = g.decode(sel, cnt, budget, sm)
@@ -131,11 +151,18 @@ def test_fused_ties(name, context, K, n10, n5):
         np.testing.assert_array_equal(fused[0][b, h, :K], want)
 
 
-def test_fused_in_a_graph_replays_like_eager():
-    x = _case("ragged-4k")
+@pytest.mark.parametrize("case", ["gqa2", "ragged-4k"])
+def test_fused_in_a_graph_replays_like_eager(case):
+    """abs_select_decode captured in a HIP graph (the fused launch for gqa2,
+    the separate launches for the small ragged layer) and replayed: every
+    replay equals the eager call."""
+    x = _case(case)
     budget = x.workload.token_budget
     sm = default_scale(x.q.shape[2])
     g = GpuLayer(x)
+    plan = g.kv.launch_plan(budget)
+    if plan["compute_units"] == 256:
+        assert plan["fused"] == (0 if case in SEPARATE else 1), plan
     g.build()
     B, Hq, D = x.q.shape
     cap = g.kv.select_capacity(budget)
