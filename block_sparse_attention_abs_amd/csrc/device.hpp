@@ -229,6 +229,10 @@ __device__ __forceinline__ float rows4_min(float v) {
 // Whole-wavefront max (every lane gets it): DPP within rows, row swaps across.
 __device__ __forceinline__ float wave_max(float v) { return rows4_max(row16_max(v)); }
 
+// Max over each half of the wavefront (lanes 0-31, 32-63): the rows, then
+// the swap of rows 0<->1 and 2<->3.
+__device__ __forceinline__ float half32_max(float v) { return swap16_other_plus(row16_max(v), true); }
+
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);   // out-of-row lanes read 0

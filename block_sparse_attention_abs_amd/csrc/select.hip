@@ -102,6 +102,10 @@ __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restr
     // INT4 and conflict)
     constexpr int CS = CPL + 1;
     __shared__ double w[NT + NT / CPL], z[NT + NT / CPL];
+    constexpr int KRS = 36;                          // words per run of integer weights (32 + padding: 16-byte
+                                                     // aligned, and the runs of a row's lanes in different banks)
+    __shared__ __align__(16) uint32_t kq[BITS == 4 ? (D / 32) * KRS : 1];
+    __shared__ int kE[BITS == 4 ? D / 32 : 1];
     {
         // the group's G heads count, the padding slots (G < GT) add +0; the
         // mask is opaque to the optimizer, which would otherwise move a
@@ -116,6 +120,36 @@ __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restr
         const int slot = threadIdx.x + threadIdx.x / CPL;
         w[slot] = BITS == 16 ? qbar : qbar * (double)sc;
         z[slot] = BITS == 16 ? 0.0 : qbar * (double)zp;
+        if constexpr (BITS == 4) {
+            // 4-bit codes: each run of 32 channels (the channels one lane of
+            // a row reads) gets a scale 2^E from its largest |w_d| (a max over
+            // the run's 32 threads), and each weight becomes an integer k_d =
+            // rint(w_d / 2^E), |k_d| <= 2^30, stored as four signed base-256
+            // digits, so that sum_d code_d k_d is exact in int32 dot products
+            // of four 8-bit pairs (v_dot4_i32_i8).  Each weight then carries
+            // |w_d - k_d 2^E| <= 2^-30 max_run |w|, a score at most 128 x 15 x
+            // 2^-30 max_d |w_d| <= 2.4e-7 M (M = sum_d |qbar_d| max(|lo_d|,
+            // |hi_d|) >= 15 max_d |w_d| / 2), and equal codes give equal sums.
+            const double wv = qbar * (double)sc;
+            int ev = 0;
+            (void)frexp(wv, &ev);                    // |wv| < 2^ev
+            const float emax = half32_max(wv != 0.0 ? (float)ev : -4096.0f);
+            const int E = (int)emax - 30;
+            const int k = (int)rint(ldexp(wv, -E));
+            const int d0 = ((k + 128) & 255) - 128, k1 = (k - d0) / 256;
+            const int d1 = ((k1 + 128) & 255) - 128, k2 = (k1 - d1) / 256;
+            const int d2 = ((k2 + 128) & 255) - 128, d3 = (k2 - d2) / 256;   // |d3| <= 65
+            if ((int)threadIdx.x < D) {
+                const int c = threadIdx.x & 31, run = threadIdx.x >> 5;
+                // word ((8-channel group) * 2 + parity) * 4 + digit of the run; byte = position in the group's pair
+                int8_t* dst = reinterpret_cast<int8_t*>(kq + run * KRS + ((c >> 3) * 2 + (c & 1)) * 4) + ((c & 7) >> 1);
+                dst[0] = (int8_t)d0;
+                dst[4] = (int8_t)d1;
+                dst[8] = (int8_t)d2;
+                dst[12] = (int8_t)d3;
+                if (c == 0) kE[run] = E;
+            }
+        }
     }
     __syncthreads();
 
@@ -125,26 +159,53 @@ __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restr
     double wr[CPL], c0 = 0.0;
 #pragma unroll
     for (int n = 0; n < CPL; ++n) {
-        wr[n] = w[sub * CS + n];
+        if constexpr (BITS != 4) wr[n] = w[sub * CS + n];
         if constexpr (BITS != 16) c0 += z[sub * CS + n];
+    }
+    uint32_t kw[32];                                 // 4-bit codes: this lane's run of integer weights
+    int E = 0;
+    if constexpr (BITS == 4) {
+#pragma unroll
+        for (int n = 0; n < 32; ++n) kw[n] = kq[sub * KRS + n];
+        E = kE[sub];
     }
     float tmn = __builtin_inff(), tmx = -__builtin_inff();   // the tile's range of stored scores
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
         const uint32_t wd[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
-        double acc[2] = {c0, 0.0};
+        double part;
+        if constexpr (BITS == 4) {
+            // digit sums: |s_L| <= 32 x 15 x 128; sum_L s_L 256^L is sum code k exactly (< 2^40)
+            int sd[4] = {0, 0, 0, 0};
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i) {
+                const int ev = (int)(wd[i] & 0x0F0F0F0Fu);          // channels 8i + 0, 2, 4, 6 (one per byte)
+                const int od = (int)((wd[i] >> 4) & 0x0F0F0F0Fu);   // channels 8i + 1, 3, 5, 7
 #pragma unroll
-            for (int n = 0; n < PER; ++n) {
-                double x;
-                if constexpr (BITS == 16)
-                    x = (double)__uint_as_float(n == 0 ? wd[i] << 16 : wd[i] & 0xFFFF0000u);
-                else
-                    x = (double)((wd[i] >> (BITS * n)) & ((1u << BITS) - 1u));
-                acc[i >> 1] = fma(wr[i * PER + n], x, acc[i >> 1]);
+                for (int L = 0; L < 4; ++L) {
+                    sd[L] = __builtin_amdgcn_sdot4(ev, (int)kw[(2 * i) * 4 + L], sd[L], false);
+                    sd[L] = __builtin_amdgcn_sdot4(od, (int)kw[(2 * i + 1) * 4 + L], sd[L], false);
+                }
             }
-        const double sum = lanes_sum_f64<LPB>(acc[0] + acc[1]);
+            const int64_t sum_k = (int64_t)sd[0] + (int64_t)sd[1] * 256 + (int64_t)sd[2] * 65536 +
+                                  (int64_t)sd[3] * 16777216;
+            part = c0 + ldexp((double)sum_k, E);
+        } else {
+            double acc[2] = {c0, 0.0};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int n = 0; n < PER; ++n) {
+                    double x;
+                    if constexpr (BITS == 16)
+                        x = (double)__uint_as_float(n == 0 ? wd[i] << 16 : wd[i] & 0xFFFF0000u);
+                    else
+                        x = (double)((wd[i] >> (BITS * n)) & ((1u << BITS) - 1u));
+                    acc[i >> 1] = fma(wr[i * PER + n], x, acc[i >> 1]);
+                }
+            part = acc[0] + acc[1];
+        }
+        const double sum = lanes_sum_f64<LPB>(part);
         const int j = j0 + r * GPW + grp;
         if (j < N && sub == 0) scores[(int64_t)bh * stride + j] = (float)sum;
         tmn = j < N ? fminf(tmn, (float)sum) : tmn;
