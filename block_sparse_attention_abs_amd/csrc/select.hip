@@ -9,14 +9,16 @@
 //         per-channel dequantization once per workgroup:
 //             w_d = qbar_d * scale_d,   c0 = sum_d qbar_d * lo_d,
 //             score_j = c0 + sum_d w_d * code_{j,d}
-//         (fp64 inside, stored as fp32 in a [b*Hkv+h][stride] scratch with
-//         16-byte aligned rows).  The lanes of one block row load 16 bytes
+//         (stored as fp32 in a [b*Hkv+h][stride] scratch with 16-byte
+//         aligned rows; fp64 inside for the 8-bit and bf16 formats, exact
+//         integer sums of the codes against 30-bit rounded weights for the
+//         4-bit formats, see the fold).  The lanes of one block row load 16 bytes
 //         of codes each (head_dim/32 lanes for INT4, head_dim/16 for INT8,
 //         head_dim/8 for bf16 centroids, whose w_d is qbar_d and c0 = 0),
 //         so one load instruction reads a contiguous 1 KiB run per
-//         wavefront.  Every load is unconditional (offsets clamped), the
-//         query, scale and lo first, then all of a lane's code rows, so
-//         the fold waits only for the former.
+//         wavefront.  Every load is unconditional (offsets clamped): the
+//         row's bounds, the query, scale and lo, then all of a lane's code
+//         rows, so the fold waits only for the query, scale and lo.
 // top-K:  one workgroup per (b, h) running topk_rows (topk.hpp): a value
 //         histogram, the exact rank of the threshold bin's candidates (or a
 //         radix select when that bin is crowded), the kept indices written
