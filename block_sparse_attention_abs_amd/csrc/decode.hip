@@ -961,8 +961,16 @@ hipError_t launch_decode(const Geom& g, DType dt, const DecodeArgs& a, hipStream
 bool select_decode_fusable(const Geom& g, DType dt, const SelectArgs& s, const DecodeArgs& a) {
     const bool served = ABS_DECODE_WAVES && ABS_DECODE_MATRIX && dt == DType::BF16 && g.D == 128 && g.G <= 4 &&
                         (a.pipelined || a.chunk == 8) && a.arrive != nullptr && s.max_n <= kFusedTopkMaxN;
-    const bool faster = s.total_blocks <= (int64_t)6144 * g.B * g.Hkv &&
-                        (s.max_n <= 4096 || (int64_t)a.splits * g.B * g.Hkv <= a.compute_units);
+    // measured faster than the separate launches: heads of at most 4096
+    // blocks; heads of at most 8192 with the split grid within two
+    // workgroups per compute unit (128K x 16, and every head at 16-token
+    // blocks at 128K: 1-2 us faster; 128K x 32, four per unit: no gain);
+    // longer heads (a 16384-block head) with the grid within the compute
+    // units and at most 6144 blocks per head on average (256K x 4 with one
+    // 16-token head: 2 us faster; every head at 16384 blocks: no gain)
+    const int64_t grid = (int64_t)a.splits * g.B * g.Hkv;
+    const bool faster = s.max_n <= 4096 || (s.max_n <= 8192 && grid <= 2 * (int64_t)a.compute_units) ||
+                        (grid <= a.compute_units && s.total_blocks <= (int64_t)6144 * g.B * g.Hkv);
     return served && faster;
 }
 

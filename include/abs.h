@@ -300,10 +300,13 @@ abs_status abs_sparse_decode(const abs_paged_kv *kv, const abs_block_map *map, c
  * writes sel and sel_count).  sel, sel_count, out and lse are written as the
  * two calls write them, with the same values (the same arithmetic).  The
  * fused launch serves bf16 caches with head_dim 128 and up to 4 query heads
- * per KV head, where it measured faster than the separate launches: at most
- * 6144 blocks per head on average, and either at most 4096 in every head or
- * a split grid within the device's compute units (up to 16384 per head).
- * Other layers run the two calls' launches, with the same results.
+ * per KV head (and a split decode of at least 8 pages per workgroup), where
+ * it measured faster than the separate launches: heads of at most 4096
+ * blocks; heads of at most 8192 blocks with a split grid of at most two
+ * workgroups per compute unit of the device; heads of up to 16384 blocks
+ * with the grid within the compute units and at most 6144 blocks per head
+ * on average.  Other layers run the two calls' launches, with the same
+ * results.
  *   Arguments: as abs_score_select and abs_sparse_decode (token_budget is
  *   both the selection budget and the decode's).
  *   workspace: >= abs_workspace_bytes(ABS_OP_SELECT_DECODE) bytes: the select
