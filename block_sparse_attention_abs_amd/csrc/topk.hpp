@@ -93,10 +93,11 @@ __device__ __forceinline__ void rank_in_wave(const float* s_val, const int32_t* 
 //      degenerate range takes an 8-bit radix select over the keys instead;
 //   4. keep the keys above b*, and those in b* ranked up to the threshold;
 //      a block scan gives the kept indices' positions in ascending order.
-// Every per-key step works on bit masks without branches (padding keys take
-// a slot below the scanned bins and count into spill slots past them), and
-// the kept keys are emitted by a loop over the set bits of the keep mask, so
-// the cost per thread grows with KPT by a few instructions per key.
+// Every per-key step works on bit masks without data-dependent branches
+// (padding keys take a slot below the scanned bins and count into spill
+// slots past them), and the kept keys are emitted by a loop over the set
+// bits of the keep mask, so the cost per thread grows with KPT by a few
+// instructions per key.
 template <int NT, int KPT, class Emit>
 __device__ __forceinline__ int topk_rows(const Geom& g, int bh, const float* __restrict__ row, int stride,
                                          const float2* __restrict__ ranges, int max_len, int budget, Emit&& emit,
@@ -188,17 +189,27 @@ __device__ __forceinline__ int topk_rows(const Geom& g, int bh, const float* __r
     Mask keep = 0;
     bool resolved = false;
     if (binned) {
-        // slot of a key: monotone non-decreasing in the score (one fma then a
-        // truncation); padding keys take slot 0, below every bin, and count
-        // into their lane's own spill slot past the bins: no branch, and no
-        // LDS address taking the atomics of whole wavefronts of padding
-        // (those serialize, 64 cycles per instruction)
-        const float c0 = -mn * inv;
+        // slot of a key: clamp(f inv + 1 - mn inv, 1, kBins) truncated, one
+        // fma then a truncation, monotone non-decreasing in the score (the
+        // bin offset 1 folded into the constant).  A wavefront with padding
+        // keys gives them slot 0, below every bin, and counts them into each
+        // lane's own spill slot past the bins (one LDS address taking the
+        // atomics of whole wavefronts of padding would serialize them, 64
+        // cycles per instruction); the others skip those selects.
+        const float c1 = 1.0f - mn * inv;
         int slot[KPT];
+        if (__builtin_amdgcn_ballot_w64(nv < KPT) == 0) {       // every key of this wavefront is valid
 #pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-            slot[e] = e < nv ? (int)fminf(fmaxf(fmaf(f[e], inv, c0), 0.0f), (float)(kBins - 1)) + 1 : 0;
-            atomicAdd(&hist[e < nv ? slot[e] : kBins + 1 + lane], 1u);
+            for (int e = 0; e < KPT; ++e) {
+                slot[e] = (int)fminf(fmaxf(fmaf(f[e], inv, c1), 1.0f), (float)kBins);
+                atomicAdd(&hist[slot[e]], 1u);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) {
+                slot[e] = e < nv ? (int)fminf(fmaxf(fmaf(f[e], inv, c1), 1.0f), (float)kBins) : 0;
+                atomicAdd(&hist[e < nv ? slot[e] : kBins + 1 + lane], 1u);
+            }
         }
         __syncthreads();
         // thread t sums the bins of slots kBins - t*BPT ... downwards; scan from the top
