@@ -63,11 +63,11 @@ METRIC = "sparse decode attn queries/s per layer at 32K/128K ctx; achieved HBM G
 # HBM bytes per launch of the kernel the roofline describes (the fused
 # top-K + split decode launch, k_select_decode_ws) from rocprofv3 FETCH_SIZE
 # and WRITE_SIZE, each scaled by the same counter's reading for a plain copy
-# of known size (see profiles/), keyed by (workload, context, block map) and
-# by a hash of the kernel sources they were taken with; any other source
-# reports null.
+# of known size (see profiles/), keyed by (workload, batch, context, block
+# map) and by a hash of the kernel sources they were taken with; any other
+# shape or source reports null.
 TRAFFIC = {
-    ("llama8b-128k-b4-bf16", 131072, "drawn", "46924a33e5cd2da4"): 71994652,
+    ("llama8b-128k-b4-bf16", 4, 131072, "drawn", "7c6b11818c19adf0"): 72013762,
 }
 KERNEL_SOURCES = ("decode.hip", "device.hpp", "launch.hpp", "decode_layout.hpp", "topk.hpp")   # kernel + its launch layout
 
@@ -362,7 +362,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x, budget, sm, args.cpu_seconds)
 
-    traffic = TRAFFIC.get((w.name, int(w.context), args.block_map, kernel_source_hash())) if fused else None
+    traffic = TRAFFIC.get((w.name, B, int(w.context), args.block_map, kernel_source_hash())) if fused else None
     rec = {
         "metric": METRIC,
         "value": round(queries_per_s, 1),

@@ -61,6 +61,18 @@ def test_traffic_key_covers_every_decode_source():
     assert re.fullmatch(r"[0-9a-f]{16}", h)
 
 
+def test_traffic_figures_name_the_shape_they_were_measured_on():
+    # a figure is looked up by (workload, batch, context, block map, source
+    # hash): a run at another batch or context must not find it
+    from block_sparse_attention_abs_amd.workload import PRESETS
+    names = {w.name for w in PRESETS}
+    for key, nbytes in bench.TRAFFIC.items():
+        name, batch, context, block_map, h = key
+        assert name in names and isinstance(batch, int) and batch > 0 and isinstance(context, int)
+        assert block_map in ("drawn", "16", "32", "64") and re.fullmatch(r"[0-9a-f]{16}", h)
+        assert nbytes > 0
+
+
 def _counter_csv(path, rows):
     import csv
     with open(path, "w", newline="") as f:
