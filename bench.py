@@ -357,6 +357,7 @@ def main():
     queries_per_s = B / (ms_per_step * 1e-3)
 
     copy_gbs = measured_copy_gbs(torch, dev)
+    gather = gather_ceiling(A, torch, x, layers, fused_step, sel, cnt, sh, capture, timed, sreps, R)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -388,6 +389,8 @@ def main():
                      "algorithmic_bytes": ab["decode"], "avg_us": round(kern_us, 3),
                      "measured_copy_gbs": round(copy_gbs, 1),
                      "frac_of_measured_copy": round(achieved / copy_gbs, 4),
+                     "gather_ceiling": gather,
+                     "frac_of_gather_ceiling": round(achieved / gather["gbs"], 4) if gather else None,
                      "decode_only": {"kernel": "k_sparse_decode_ws (abs_sparse_decode)", "avg_us": round(dec_avg, 3),
                                      "frac": round(ab["decode"] / (dec_avg * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}},
         "cpu_baseline": cpu,
@@ -478,6 +481,79 @@ def naive_per_size(A, torch, x, layers, q, budget, sm, fmt, R, capture, timed, s
     del groups
     torch.cuda.empty_cache()
     return res
+
+
+def selected_tiles(page_table, seq_lens, block_size, tile, sel, cnt, k_base, v_base):
+    """Device addresses of the K and V tiles ([16][head_dim] of one page and
+    KV head, `tile` bytes) of every selected page, in the decode's order: by
+    (sequence, head), then selection position, then page, K before V; also
+    the byte offsets and which are K."""
+    B, Hkv = cnt.shape
+    offs = []
+    for b in range(B):
+        L = int(seq_lens[b])
+        for h in range(Hkv):
+            bs = int(block_size[h])
+            for j in sel[b, h, :cnt[b, h]]:
+                t0, t1 = int(j) * bs, min((int(j) + 1) * bs, L)
+                for pg in range(t0 // 16, (t1 + 15) // 16):
+                    o = (int(page_table[b, pg]) * Hkv + h) * tile
+                    offs.append((o, True))
+                    offs.append((o, False))
+    o = np.array([a for a, _ in offs], dtype=np.uint64)
+    is_k = np.array([k for _, k in offs], dtype=bool)
+    return np.where(is_k, np.uint64(k_base) + o, np.uint64(v_base) + o), o, is_k
+
+
+def gather_ceiling(A, torch, x, layers, fused_step, sel, cnt, sh, capture, timed, sreps, R):
+    """The rate at which the GPU gathers the K/V tiles a decode step selects,
+    with none of the decode's arithmetic (abs_gather_tiles, the decode's
+    non-temporal loads): for each layer copy its own selection's tiles, one
+    launch per copy in a graph as for the kernels, the best over launch
+    shapes (workgroups x tiles in flight per wavefront).  Layer 0's words
+    are checked against the host arrays (XOR).  None where the tiles are not
+    4 KiB (bf16, head_dim 128)."""
+    D = x.k_cache.shape[3]
+    if x.dtype != "bf16" or D != 128:
+        return None
+    addrs = []
+    for r in range(R):
+        fused_step(r, sh)
+        torch.cuda.synchronize()
+        Lr = layers[r]
+        a, o, is_k = selected_tiles(Lr.page_table.cpu().numpy(), Lr.seq_lens_host, Lr.block_size_host, 4096,
+                                    sel.cpu().numpy(), cnt.cpu().numpy(), Lr.k_cache.data_ptr(),
+                                    Lr.v_cache.data_ptr())
+        if r == 0:
+            want = 0
+            for cache, m in ((x.k_cache, is_k), (x.v_cache, ~is_k)):
+                words = cache.reshape(-1).view(np.uint32)
+                idx = (o[m] // 4)[:, None] + np.arange(1024, dtype=np.uint64)[None, :]
+                want ^= int(np.bitwise_xor.reduce(words[idx].ravel()))
+            n0 = len(a)
+        addrs.append(torch.from_numpy(a.view(np.int64)).to(sel.device))
+    n = len(addrs[0])
+    if any(len(t) != n for t in addrs):
+        return None
+    best = None
+    for wgs in (256, 512, 1024, 2048):
+        out = torch.zeros((wgs,), dtype=torch.int32, device=sel.device)
+        for u in (1, 2, 4, 8):
+            def call(i, st, wgs=wgs, u=u, out=out):
+                A.abs_gather_tiles(int(addrs[i % R].data_ptr()), n, 4096, wgs, u, int(out.data_ptr()), st)
+            call(0, sh)
+            torch.cuda.synchronize()
+            got = int(np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32)))
+            if got != want:
+                raise SystemExit(f"gather probe read wrong words (workgroups {wgs}, in flight {u})")
+            g = capture(call)
+            us = float(np.median([timed(g, sreps) / (sreps * R) * 1e3 for _ in range(5)]))
+            gbs = n * 4096 / (us * 1e-6) / 1e9
+            if best is None or gbs > best["gbs"]:
+                best = {"gbs": round(gbs, 1), "avg_us": round(us, 3), "workgroups": wgs, "in_flight": u,
+                        "tiles": n, "bytes": n * 4096, "checked_tiles": n0}
+            del g
+    return best
 
 
 def measured_copy_gbs(torch, dev, nbytes=1 << 30, reps=5):

@@ -31,7 +31,7 @@ EXPORTS = ("abs_status_str", "abs_last_error", "abs_total_blocks", "abs_centroid
            "abs_centroid_offsets_capacity", "abs_centroid_row_bytes", "abs_select_capacity", "abs_workspace_bytes", "abs_build_centroids",
            "abs_update_centroids", "abs_score_select", "abs_sparse_decode", "abs_select_decode",
            "abs_estimate", "abs_topk_decode", "abs_select_decode_static", "abs_describe_launch", "abs_reset_workspace", "abs_set_debug_checks",
-           "abs_head_recall", "abs_assign_block_sizes")
+           "abs_head_recall", "abs_assign_block_sizes", "abs_gather_tiles")
 
 
 class abs_paged_kv(C.Structure):
@@ -118,6 +118,8 @@ def lib():
         L.abs_head_recall.argtypes = [KV, P, P, P, P]
         L.abs_assign_block_sizes.restype = st
         L.abs_assign_block_sizes.argtypes = [i32, P, C.c_float, P]
+        L.abs_gather_tiles.restype = st
+        L.abs_gather_tiles.argtypes = [P, i32, i32, i32, i32, P, P]
         _lib = L
     return _lib
 
@@ -248,6 +250,12 @@ def abs_set_debug_checks(enable: bool) -> bool:
 
 def abs_head_recall(kv, lse_sel_ptr: int, lse_full_ptr: int, recall_ptr: int, stream: int) -> None:
     _check(lib().abs_head_recall(C.byref(kv), lse_sel_ptr, lse_full_ptr, recall_ptr, stream), "abs_head_recall")
+
+
+def abs_gather_tiles(tile_addr_ptr: int, num_tiles: int, tile_bytes: int, workgroups: int, in_flight: int,
+                     xor_out_ptr: int, stream: int) -> None:
+    _check(lib().abs_gather_tiles(tile_addr_ptr, num_tiles, tile_bytes, workgroups, in_flight, xor_out_ptr, stream),
+           "abs_gather_tiles")
 
 
 def abs_assign_block_sizes(recall_host: np.ndarray, threshold: float) -> np.ndarray:

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libabs.so")
-SOURCES = ["centroid.hip", "select.hip", "decode.hip", "calibrate.hip", "abs_api.cpp"]
+SOURCES = ["centroid.hip", "select.hip", "decode.hip", "calibrate.hip", "gather.hip", "abs_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -705,6 +705,20 @@ abs_status abs_head_recall(const abs_paged_kv* kv, const float* lse_sel, const f
                       "head_recall");
 }
 
+abs_status abs_gather_tiles(const uint64_t* tile_addr, int32_t num_tiles, int32_t tile_bytes, int32_t workgroups,
+                            int32_t in_flight, uint32_t* xor_out, void* stream) {
+    if (tile_addr == nullptr || xor_out == nullptr) return fail(ABS_ERR_INVALID_ARG, "null tile_addr or xor_out");
+    if (tile_bytes != 4096) return fail(ABS_ERR_INVALID_ARG, "tile_bytes %d: only 4096 is supported", tile_bytes);
+    if (num_tiles < 1) return fail(ABS_ERR_INVALID_ARG, "num_tiles %d < 1", num_tiles);
+    if (workgroups < 1 || workgroups > 65535)
+        return fail(ABS_ERR_INVALID_ARG, "workgroups %d outside [1, 65535]", workgroups);
+    if (in_flight != 1 && in_flight != 2 && in_flight != 4 && in_flight != 8)
+        return fail(ABS_ERR_INVALID_ARG, "in_flight %d not 1, 2, 4 or 8", in_flight);
+    return hip_status(absk::launch_gather_tiles(tile_addr, num_tiles, workgroups, in_flight, xor_out,
+                                                static_cast<hipStream_t>(stream)),
+                      "gather_tiles");
+}
+
 abs_status abs_assign_block_sizes(int32_t num_kv_heads, const float* recall_host, float threshold,
                                   int32_t* block_size_host) {
     if (num_kv_heads < 1) return fail(ABS_ERR_INVALID_ARG, "num_kv_heads %d < 1", num_kv_heads);

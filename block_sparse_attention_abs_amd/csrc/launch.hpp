@@ -216,4 +216,9 @@ hipError_t launch_zero(int32_t* p, int n, hipStream_t s);
 hipError_t launch_head_recall(int B, int Hq, int Hkv, const float* lse_sel, const float* lse_full, float* recall,
                               hipStream_t s);
 
+// Measurement: n tiles of 4 KiB at the device addresses addr, read as the
+// decode reads its K/V tiles; out[g] = XOR of the words workgroup g read.
+hipError_t launch_gather_tiles(const uint64_t* addr, int n, int workgroups, int in_flight, uint32_t* out,
+                               hipStream_t s);
+
 }  // namespace absk

@@ -77,10 +77,13 @@ __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restr
         zp = lo[(int64_t)bh * D + dch];
     }
     __builtin_amdgcn_sched_barrier(0);
-    const int64_t row0 = (int64_t)__builtin_amdgcn_readfirstlane((int)off0) |
-                         ((int64_t)__builtin_amdgcn_readfirstlane((int)(off0 >> 32)) << 32);
-    const int64_t rows = ((int64_t)__builtin_amdgcn_readfirstlane((int)off1) |
-                          ((int64_t)__builtin_amdgcn_readfirstlane((int)(off1 >> 32)) << 32)) - row0;
+    // 64-bit offsets through scalar registers, each half as unsigned (readfirstlane
+    // returns int: a sign-extended low half would fill the high half with ones)
+    const int64_t row0 = (int64_t)((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)off0) |
+                                   ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(off0 >> 32)) << 32));
+    const int64_t rows = (int64_t)((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)off1) |
+                                   ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(off1 >> 32)) << 32)) -
+                         row0;
     const int L = min(max(__builtin_amdgcn_readfirstlane(len), 1), g.max_len);
     const int N = (int)min((int64_t)shr_ceil(L, block_shift_of(g, h)), rows);   // as centroid_rows()
     // RPL block rows per lane group, GPW consecutive rows per step (contiguous

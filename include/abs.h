@@ -442,6 +442,29 @@ abs_status abs_head_recall(const abs_paged_kv *kv, const float *lse_sel, const f
 abs_status abs_assign_block_sizes(int32_t num_kv_heads, const float *recall_host, float threshold,
                                   int32_t *block_size_host);
 
+/*
+ * Measurement, not part of the decode step: the K/V gather of the split
+ * decode (its page loop reads, for each selected page of a head, the
+ * page's K and V tiles of [page_size][head_dim] storage elements) with none
+ * of its arithmetic, for timing the decode's page loop against the rate at
+ * which the GPU gathers the same bytes.
+ *
+ * Reads num_tiles tiles of tile_bytes bytes at the device addresses
+ * tile_addr[0 .. num_tiles) (device u64 array; each address 16-byte
+ * aligned) with the decode's non-temporal 16-byte loads: workgroups
+ * workgroups of 256 threads, each wavefront a contiguous run of
+ * ceil(num_tiles / (4 * workgroups)) tiles of the list, in_flight tiles
+ * (1, 2, 4 or 8) in flight at a time.  xor_out (device u32 [workgroups]):
+ * entry g = the XOR of every 32-bit word of the tiles workgroup g read, so
+ * the XOR of all entries is the XOR of all words of all listed tiles
+ * (a tile listed twice cancels).  tile_bytes must be 4096 (bf16,
+ * head_dim 128, 16-token pages); num_tiles >= 1; 1 <= workgroups <= 65535;
+ * otherwise ABS_ERR_INVALID_ARG.  One launch, no workspace, asynchronous on
+ * `stream`.
+ */
+abs_status abs_gather_tiles(const uint64_t *tile_addr, int32_t num_tiles, int32_t tile_bytes, int32_t workgroups,
+                            int32_t in_flight, uint32_t *xor_out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

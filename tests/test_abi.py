@@ -25,7 +25,7 @@ def header_functions():
 
 def test_exports_every_declared_call():
     names = header_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     assert sorted(A.EXPORTS) == names
     L = A.lib()
     for n in names:
@@ -402,3 +402,20 @@ def test_division_without_division_is_exact(tmp_path):
                    capture_output=True, timeout=600)
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
+
+
+@pytest.mark.parametrize("args", [
+    (0, 10, 4096, 4, 2, 1),          # null tile_addr
+    (1, 10, 4096, 4, 2, 0),          # null xor_out
+    (1, 10, 2048, 4, 2, 1),          # tile size other than 4096
+    (1, 0, 4096, 4, 2, 1),           # no tiles
+    (1, 10, 4096, 0, 2, 1),          # no workgroups
+    (1, 10, 4096, 65536, 2, 1),      # too many workgroups
+    (1, 10, 4096, 4, 3, 1),          # in_flight not 1, 2, 4 or 8
+])
+def test_gather_probe_rejects_bad_arguments(args):
+    """abs_gather_tiles checks its arguments on the host before any launch
+    (the pointers here are never dereferenced: each call fails first)."""
+    addr, n, tile_bytes, wgs, in_flight, out = args
+    st = status_of(lambda: A.abs_gather_tiles(addr, n, tile_bytes, wgs, in_flight, out, 0))
+    assert st == A.ABS_ERR_INVALID_ARG

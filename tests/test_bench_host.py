@@ -120,3 +120,21 @@ def test_traffic_summary_scales_by_the_copy_and_counts_requests(tmp_path, capsys
     assert cells[1] == "2" and cells[4] == "409600" and cells[5] == "20480" and cells[6] == "430080"
     # request bytes: mean over the two dispatches of (320 + 1280 + 128000) x k, k = 1 and 3
     assert cells[7] == str(2 * (320 + 1280 + 128000))
+
+
+def test_selected_tiles_follow_the_page_table():
+    """The gather reference's tile list: for each selected block, the pages
+    its tokens cover (the last one cut at L), each page's K tile then V tile
+    at ((page id x Hkv + head) x tile bytes) from the cache bases."""
+    page_table = np.array([[5, 2, 7, -1]], dtype=np.int32)
+    seq_lens = np.array([40], dtype=np.int32)                  # 3 pages, the last holding 8 tokens
+    block_size = np.array([16, 32], dtype=np.int32)            # two KV heads
+    sel = np.array([[[1, 2], [0, -1]]], dtype=np.int32)
+    cnt = np.array([[2, 1]], dtype=np.int32)
+    a, o, is_k = bench.selected_tiles(page_table, seq_lens, block_size, 4096, sel, cnt, 1_000_000, 2_000_000)
+    # head 0 (16-token blocks): block 1 -> page 1 (id 2), block 2 -> tokens 32..39 -> page 2 (id 7);
+    # head 1 (32-token blocks): block 0 -> pages 0, 1 (ids 5, 2)
+    want_o = [(2 * 2 + 0) * 4096, (7 * 2 + 0) * 4096, (5 * 2 + 1) * 4096, (2 * 2 + 1) * 4096]
+    assert o.tolist() == [x for v in want_o for x in (v, v)]
+    assert is_k.tolist() == [True, False] * 4
+    assert a.tolist() == [(1_000_000 if k else 2_000_000) + v for v, k in zip(o.tolist(), is_k.tolist())]
