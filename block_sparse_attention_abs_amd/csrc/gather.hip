@@ -39,22 +39,23 @@ __global__ __launch_bounds__(256) void k_gather_tiles(const uint64_t* __restrict
             u32x4 v[U][kLoadsPerTile];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int k = min(i + u, cnt - 1);                    // a repeated tile past the run is not counted
-                // both halves as unsigned: readlane returns int, and a sign-extended
-                // low half would set every bit of the high half
-                const uint64_t t = (uint64_t)(uint32_t)__builtin_amdgcn_readlane(a_lo, k) |
-                                   ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(a_hi, k) << 32);
-                const u32x4* p = reinterpret_cast<const u32x4*>(t) + lane;
+                if (i + u < cnt) {                                    // the run's last slots load nothing
+                    // both halves as unsigned: readlane returns int, and a sign-extended
+                    // low half would set every bit of the high half
+                    const uint64_t t = (uint64_t)(uint32_t)__builtin_amdgcn_readlane(a_lo, i + u) |
+                                       ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(a_hi, i + u) << 32);
+                    const u32x4* p = reinterpret_cast<const u32x4*>(t) + lane;
 #pragma unroll
-                for (int s = 0; s < kLoadsPerTile; ++s) v[u][s] = __builtin_nontemporal_load(p + s * 64);
+                    for (int s = 0; s < kLoadsPerTile; ++s) v[u][s] = __builtin_nontemporal_load(p + s * 64);
+                } else {
+#pragma unroll
+                    for (int s = 0; s < kLoadsPerTile; ++s) v[u][s] = u32x4{0u, 0u, 0u, 0u};
+                }
             }
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                uint32_t x = 0;
+            for (int u = 0; u < U; ++u)
 #pragma unroll
-                for (int s = 0; s < kLoadsPerTile; ++s) x ^= v[u][s].x ^ v[u][s].y ^ v[u][s].z ^ v[u][s].w;
-                acc ^= i + u < cnt ? x : 0u;
-            }
+                for (int s = 0; s < kLoadsPerTile; ++s) acc ^= v[u][s].x ^ v[u][s].y ^ v[u][s].z ^ v[u][s].w;
         }
     }
 #pragma unroll
