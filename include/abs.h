@@ -42,7 +42,17 @@
 extern "C" {
 #endif
 
-typedef enum abs_status {
+/* Every enum of this interface is a 32-bit integer.  Compiled as C++ its
+ * underlying type is int32_t, so that any value a C caller passes (an
+ * out-of-range op or status included) is a value of the type, which the
+ * calls can check and reject; compiled as C it is the usual enum. */
+#ifdef __cplusplus
+#define ABS_ENUM(name) enum name : int32_t
+#else
+#define ABS_ENUM(name) enum name
+#endif
+
+typedef ABS_ENUM(abs_status) {
     ABS_OK = 0,
     ABS_ERR_INVALID_ARG = 1,  /* null pointer, bad dimension, too-small capacity */
     ABS_ERR_UNSUPPORTED = 2,  /* valid but not built: head_dim, page size, block size, group size, N */
@@ -50,12 +60,12 @@ typedef enum abs_status {
     ABS_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
 } abs_status;
 
-typedef enum abs_dtype {
+typedef ABS_ENUM(abs_dtype) {
     ABS_F32 = 0,   /* IEEE binary32 */
     ABS_BF16 = 1   /* bfloat16 (upper half of binary32) */
 } abs_dtype;
 
-typedef enum abs_op {
+typedef ABS_ENUM(abs_op) {
     ABS_OP_BUILD = 0,    /* abs_build_centroids */
     ABS_OP_SELECT = 1,   /* abs_score_select */
     ABS_OP_DECODE = 2,   /* abs_sparse_decode */
@@ -136,7 +146,7 @@ typedef struct abs_block_map {
  * Every step that decides a code is an fp32 operation; a scale of 0 gives
  * code 0 (ABS_CENT_INT4_SYM: q = 0).
  */
-typedef enum abs_centroid_format {
+typedef ABS_ENUM(abs_centroid_format) {
     ABS_CENT_INT4 = 0,
     ABS_CENT_INT4_SYM = 1,
     ABS_CENT_INT8 = 2,
