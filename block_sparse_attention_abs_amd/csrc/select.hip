@@ -10,9 +10,9 @@
 //             w_d = qbar_d * scale_d,   c0 = sum_d qbar_d * lo_d,
 //             score_j = c0 + sum_d w_d * code_{j,d}
 //         (stored as fp32 in a [b*Hkv+h][stride] scratch with 16-byte
-//         aligned rows; fp64 inside for the 8-bit and bf16 formats, exact
-//         integer sums of the codes against 30-bit rounded weights for the
-//         4-bit formats, see the fold).  The lanes of one block row load 16 bytes
+//         aligned rows; exact integer sums of the codes against 30-bit
+//         rounded weights for the 4- and 8-bit formats, see the fold, and
+//         fp64 for bf16 centroids).  The lanes of one block row load 16 bytes
 //         of codes each (head_dim/32 lanes for INT4, head_dim/16 for INT8,
 //         head_dim/8 for bf16 centroids, whose w_d is qbar_d and c0 = 0),
 //         so one load instruction reads a contiguous 1 KiB run per
@@ -107,10 +107,15 @@ __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restr
     // INT4 and conflict)
     constexpr int CS = CPL + 1;
     __shared__ double w[NT + NT / CPL], z[NT + NT / CPL];
-    constexpr int KRS = 36;                          // words per run of integer weights (32 + padding: 16-byte
-                                                     // aligned, and the runs of a row's lanes in different banks)
-    __shared__ __align__(16) uint32_t kq[BITS == 4 ? (D / 32) * KRS : 1];
-    __shared__ int kE[BITS == 4 ? D / 32 : 1];
+    // integer weights (4- and 8-bit codes): one run per lane's channels (32
+    // for 4-bit codes, 16 for 8-bit), NKW words of digits each, KRS words
+    // apart (padding: 16-byte aligned, and the runs of a row's lanes in
+    // different banks)
+    constexpr bool INT = BITS == 4 || BITS == 8;
+    constexpr int NKW = BITS == 4 ? 32 : 16;
+    constexpr int KRS = BITS == 4 ? 36 : 20;
+    __shared__ __align__(16) uint32_t kq[INT ? (D / CPL) * KRS : 1];
+    __shared__ int kE[INT ? D / CPL : 1];
     {
         // the group's G heads count, the padding slots (G < GT) add +0; the
         // mask is opaque to the optimizer, which would otherwise move a
@@ -125,29 +130,36 @@ __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restr
         const int slot = threadIdx.x + threadIdx.x / CPL;
         w[slot] = BITS == 16 ? qbar : qbar * (double)sc;
         z[slot] = BITS == 16 ? 0.0 : qbar * (double)zp;
-        if constexpr (BITS == 4) {
-            // 4-bit codes: each run of 32 channels (the channels one lane of
-            // a row reads) gets a scale 2^E from its largest |w_d| (a max over
-            // the run's 32 threads), and each weight becomes an integer k_d =
+        if constexpr (INT) {
+            // 4- and 8-bit codes: each run of channels one lane of a row reads
+            // (32 or 16) gets a scale 2^E from its largest |w_d| (a max over
+            // the run's threads), and each weight becomes an integer k_d =
             // rint(w_d / 2^E), |k_d| <= 2^30, stored as four signed base-256
             // digits, so that sum_d code_d k_d is exact in int32 dot products
-            // of four 8-bit pairs (v_dot4_i32_i8).  Each weight then carries
-            // |w_d - k_d 2^E| <= 2^-30 max_run |w|, a score at most 128 x 15 x
-            // 2^-30 max_d |w_d| <= 2.4e-7 M (M = sum_d |qbar_d| max(|lo_d|,
-            // |hi_d|) >= 15 max_d |w_d| / 2), and equal codes give equal sums.
+            // of four 8-bit pairs (v_dot4_i32_i8; 8-bit codes enter as code -
+            // 128, and 128 sum_d k_d is added back).  Each weight then carries
+            // |w_d - k_d 2^E| <= 2^-30 max_run |w|, a score at most 128 x
+            // (2^BITS - 1) x 2^-30 max_d |w_d| <= 2.4e-7 M (M = sum_d |qbar_d|
+            // max(|lo_d|, |hi_d|) >= (2^BITS - 1) max_d |w_d| / 2), and equal
+            // codes give equal sums.
             const double wv = qbar * (double)sc;
             int ev = 0;
             (void)frexp(wv, &ev);                    // |wv| < 2^ev
-            const float emax = half32_max(wv != 0.0 ? (float)ev : -4096.0f);
+            const float ef = wv != 0.0 ? (float)ev : -4096.0f;
+            const float emax = BITS == 4 ? half32_max(ef) : row16_max(ef);
             const int E = (int)emax - 30;
             const int k = (int)rint(ldexp(wv, -E));
             const int d0 = ((k + 128) & 255) - 128, k1 = (k - d0) / 256;
             const int d1 = ((k1 + 128) & 255) - 128, k2 = (k1 - d1) / 256;
             const int d2 = ((k2 + 128) & 255) - 128, d3 = (k2 - d2) / 256;   // |d3| <= 65
             if ((int)threadIdx.x < D) {
-                const int c = threadIdx.x & 31, run = threadIdx.x >> 5;
-                // word ((8-channel group) * 2 + parity) * 4 + digit of the run; byte = position in the group's pair
-                int8_t* dst = reinterpret_cast<int8_t*>(kq + run * KRS + ((c >> 3) * 2 + (c & 1)) * 4) + ((c & 7) >> 1);
+                const int c = threadIdx.x % CPL, run = threadIdx.x / CPL;
+                // 4-bit: word ((8-channel group) * 2 + parity) * 4 + digit of the run, byte = position in the
+                // group's pair (a word of codes holds the group's even channels in its low nibbles, the odd
+                // ones in its high nibbles); 8-bit: word (4-channel group) * 4 + digit, byte = position in
+                // the group
+                int8_t* dst = reinterpret_cast<int8_t*>(kq + run * KRS) +
+                              (BITS == 4 ? ((c >> 3) * 2 + (c & 1)) * 16 + ((c & 7) >> 1) : (c >> 2) * 16 + (c & 3));
                 dst[0] = (int8_t)d0;
                 dst[4] = (int8_t)d1;
                 dst[8] = (int8_t)d2;
@@ -164,15 +176,26 @@ __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restr
     double wr[CPL], c0 = 0.0;
 #pragma unroll
     for (int n = 0; n < CPL; ++n) {
-        if constexpr (BITS != 4) wr[n] = w[sub * CS + n];
+        if constexpr (BITS == 16) wr[n] = w[sub * CS + n];
         if constexpr (BITS != 16) c0 += z[sub * CS + n];
     }
-    uint32_t kw[32];                                 // 4-bit codes: this lane's run of integer weights
+    uint32_t kw[NKW];                                // 4- and 8-bit codes: this lane's run of integer weights
     int E = 0;
-    if constexpr (BITS == 4) {
+    int64_t bias = 0;                                // 8-bit codes: 128 sum_d k_d over the run (codes enter as code - 128)
+    if constexpr (INT) {
 #pragma unroll
-        for (int n = 0; n < 32; ++n) kw[n] = kq[sub * KRS + n];
+        for (int n = 0; n < NKW; ++n) kw[n] = kq[sub * KRS + n];
         E = kE[sub];
+    }
+    if constexpr (BITS == 8) {
+#pragma unroll
+        for (int L = 0; L < 4; ++L) {
+            int s = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s = __builtin_amdgcn_sdot4((int)kw[i * 4 + L], 0x01010101, s, false);
+            bias += (int64_t)s << (8 * L);
+        }
+        bias *= 128;
     }
     float tmn = __builtin_inff(), tmx = -__builtin_inff();   // the tile's range of stored scores
 #pragma unroll
@@ -194,6 +217,18 @@ __device__ __forceinline__ void score_tile(const Geom& g, const uint8_t* __restr
             }
             const int64_t sum_k = (int64_t)sd[0] + (int64_t)sd[1] * 256 + (int64_t)sd[2] * 65536 +
                                   (int64_t)sd[3] * 16777216;
+            part = c0 + ldexp((double)sum_k, E);
+        } else if constexpr (BITS == 8) {
+            // digit sums: |s_L| <= 16 x 128 x 128; sum_L s_L 256^L + 128 sum_d k_d is sum code k exactly
+            int sd[4] = {0, 0, 0, 0};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int cv = (int)(wd[i] ^ 0x80808080u);           // channels 4i .. 4i + 3 as code - 128
+#pragma unroll
+                for (int L = 0; L < 4; ++L) sd[L] = __builtin_amdgcn_sdot4(cv, (int)kw[i * 4 + L], sd[L], false);
+            }
+            const int64_t sum_k = (int64_t)sd[0] + (int64_t)sd[1] * 256 + (int64_t)sd[2] * 65536 +
+                                  (int64_t)sd[3] * 16777216 + bias;
             part = c0 + ldexp((double)sum_k, E);
         } else {
             double acc[2] = {c0, 0.0};

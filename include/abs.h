@@ -257,12 +257,12 @@ abs_status abs_update_centroids(const abs_paged_kv *kv, const abs_block_map *map
  * qbar = sum of the query heads h*G .. h*G+G-1 (G = num_q_heads /
  * num_kv_heads), score_j = qbar . (code_j * scale + lo) (ABS_CENT_BF16:
  * qbar . centroid_j), rounded to fp32; keep the K_{b,h} best blocks ranked
- * by (score desc, index asc).  The 8-bit and bf16 formats are evaluated in
- * fp64; the 4-bit formats as exact integer sums of code x weight after each
+ * by (score desc, index asc).  bf16 centroids are evaluated in fp64; the
+ * 4- and 8-bit formats as exact integer sums of code x weight after each
  * weight qbar_d * scale_d is rounded to a 30-bit multiple of a power of two
- * (one per 32 channels), which moves a score by at most 2.4e-7 M, M =
- * sum_d |qbar_d| max(|lo_d|, |hi_d|) (a bound on every |score|).  Equal
- * centroids give equal scores.
+ * (one per 32 channels for 4-bit codes, per 16 for 8-bit), which moves a
+ * score by at most 2.4e-7 M, M = sum_d |qbar_d| max(|lo_d|, |hi_d|) (a
+ * bound on every |score|).  Equal centroids give equal scores.
  *   q: device [num_seqs][num_q_heads][head_dim] in kv_dtype.
  *   sel: device int32 [num_seqs][num_kv_heads][sel_cap]; row (b, h) gets its
  *       K_{b,h} block indices in ascending order; slots past K are not written.

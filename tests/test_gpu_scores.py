@@ -3,15 +3,15 @@ the oracle's fp64 scores on the same centroid codes.
 
 abs_estimate leaves the score rows at the start of the select region of its
 workspace: fp32, one row per (b, h) in b-major order, each row as long as
-the layer's largest block count rounded up to a multiple of 4.  For 4-bit
-codes the kernel sums code x weight exactly in integers after rounding each
-weight to a 30-bit integer multiple of a power of two (at most 2^-30 of the
-largest weight of its 32-channel run off), so a score is at most
-128 x 15 x 2^-30 max_d |w_d| <= 2.4e-7 M off before it is stored, M =
-sum_d |qbar_d| max(|lo_d|, |hi_d|) (R16's bound on every |score|); the 8-bit
-and bf16 formats are summed in fp64.  Storing the row in fp32 adds half an
-ulp.  The bound checked: |gpu - oracle| <= 2.4e-7 M + 2^-24 |oracle| +
-1e-12 M.
+the layer's largest block count rounded up to a multiple of 4.  For 4- and
+8-bit codes the kernel sums code x weight exactly in integers after rounding
+each weight to a 30-bit integer multiple of a power of two (at most 2^-30 of
+the largest weight of its run of 32 or 16 channels off), so a score is at
+most 128 x (2^bits - 1) x 2^-30 max_d |w_d| <= 2.4e-7 M off before it is
+stored, M = sum_d |qbar_d| max(|lo_d|, |hi_d|) >= (2^bits - 1) max_d |w_d| / 2
+(R16's bound on every |score|); bf16 centroids are summed in fp64.  Storing
+the row in fp32 adds half an ulp.  The bound checked: |gpu - oracle| <=
+2.4e-7 M + 2^-24 |oracle| + 1e-12 M.
 """
 import numpy as np
 import pytest
