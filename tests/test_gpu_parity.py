@@ -194,15 +194,41 @@ def test_full_size_sampled(oracle_mod, cfg, layer):
     benchmark times, top-K inside the decode launch), which must give the
     same sel, sel_count, out and lse bit for bit; the oracle recomputes the
     first and last sequence on their own."""
-    from block_sparse_attention_abs_amd import abs as A
     w = P[cfg]
     x = W.make_layer(w, layer)
-    sm = default_scale(w.head_dim)
     print(f"[gpu parity] full size cfg {cfg} layer {layer}: {w.name} bs={x.block_size.tolist()}", flush=True)
+    _full_size_check(oracle_mod, w, x, f"cfg {cfg} layer {layer}", FULL_SIZE_PLAN[cfg])
+
+
+def test_fused_past_4gib_of_cache(oracle_mod):
+    """128K x 16 with 8192 spare pages in the pool: the K and V caches are
+    4.25 GiB each, and the shuffled page table puts selected pages past the
+    4 GiB mark (byte offsets above 2^32).  The layer takes the fused launch
+    at two split workgroups per compute unit (4 splits of 64 pages, 512
+    workgroups); checked as the full-size workloads are."""
+    w = P[3].scaled(batch=16)
+    x = W.make_layer(w, extra_pages=8192)
+    print(f"[gpu parity] 128K x 16 over 4 GiB: pool {x.k_cache.shape[0]} pages, "
+          f"{x.k_cache.nbytes / 2**30:.2f} GiB per cache", flush=True)
+    sel, cnt = _full_size_check(oracle_mod, w, x, "128K x 16 over 4 GiB", (4, 64, 1))
+    Hkv = w.num_kv_heads
+    top = 0
+    for (b, h), k in np.ndenumerate(cnt):
+        bs = int(x.block_size[h])
+        for j in sel[b, h, :k]:
+            end = min((int(j) + 1) * bs, int(x.seq_lens[b]))           # the block's tokens: j bs .. end - 1
+            for pg in range(int(j) * bs // 16, (end + 15) // 16):
+                top = max(top, (int(x.page_table[b, pg]) * Hkv + h + 1) * 16 * w.head_dim * 2)
+    assert top > 2**32, top
+
+
+def _full_size_check(oracle_mod, w, x, label, want_plan):
+    from block_sparse_attention_abs_amd import abs as A
+    sm = default_scale(w.head_dim)
     g = GpuLayer(x)
     plan = g.kv.launch_plan(w.token_budget)
     if plan["compute_units"] == 256:
-        assert (plan["splits"], plan["pages_per_wg"], plan["pipelined"]) == FULL_SIZE_PLAN[cfg], plan
+        assert (plan["splits"], plan["pages_per_wg"], plan["pipelined"]) == want_plan, plan
         assert plan["fused"] == 1, plan
     r = g.run(w.token_budget, sm)
     B, Hq, D = x.q.shape
@@ -232,10 +258,11 @@ def test_full_size_sampled(oracle_mod, cfg, layer):
                                  r.sel[b:b + 1], r.count[b:b + 1], sm, x.dtype)
         mx, mean = check_attention(r.out[b:b + 1], r.lse[b:b + 1], o, l, x.dtype)
         own = attention_vs_own_selection(r.out[b:b + 1], ref)
-        print(f"[gpu parity] cfg {cfg} layer {layer} seq {b}: max/mean |out - oracle| {mx:.2e}/{mean:.2e}; "
+        print(f"[gpu parity] {label} seq {b}: max/mean |out - oracle| {mx:.2e}/{mean:.2e}; "
               f"against the oracle's own selection {own}", flush=True)
     del g
     torch.cuda.empty_cache()
+    return r.sel, r.count
 
 
 def test_decode_repeats_bit_identical():
