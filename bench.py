@@ -535,7 +535,7 @@ def gather_ceiling(A, torch, x, layers, fused_step, sel, cnt, sh, capture, timed
     n = len(addrs[0])
     if any(len(t) != n for t in addrs):
         return None
-    best = None
+    best, shapes = None, []
     for wgs in (256, 512, 1024, 2048):
         out = torch.zeros((wgs,), dtype=torch.int32, device=sel.device)
         for u in (1, 2, 4, 8):
@@ -549,10 +549,12 @@ def gather_ceiling(A, torch, x, layers, fused_step, sel, cnt, sh, capture, timed
             g = capture(call)
             us = float(np.median([timed(g, sreps) / (sreps * R) * 1e3 for _ in range(5)]))
             gbs = n * 4096 / (us * 1e-6) / 1e9
+            shapes.append([wgs, u, round(gbs, 1)])
             if best is None or gbs > best["gbs"]:
                 best = {"gbs": round(gbs, 1), "avg_us": round(us, 3), "workgroups": wgs, "in_flight": u,
                         "tiles": n, "bytes": n * 4096, "checked_tiles": n0}
             del g
+    best["shapes"] = shapes              # [workgroups, tiles in flight, GB/s] of every launch shape tried
     return best
 
 
