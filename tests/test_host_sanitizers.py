@@ -22,6 +22,7 @@ from block_sparse_attention_abs_amd import build as B  # noqa: E402
 HOST_SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
             "-Xarch_host", "-fno-omit-frame-pointer"]
 ENV = {"ASAN_OPTIONS": "detect_leaks=0:halt_on_error=1", "UBSAN_OPTIONS": "print_stacktrace=1:halt_on_error=1"}
+CLANG = "/opt/rocm/llvm/bin/clang"
 
 
 def _runtime():
@@ -31,8 +32,8 @@ def _runtime():
 
 @pytest.fixture(scope="module")
 def san_lib(tmp_path_factory):
-    if not os.path.exists(B.HIPCC) or _runtime() is None:
-        pytest.skip("hipcc or the clang sanitizer runtime not found")
+    if not os.path.exists(B.HIPCC) or not os.path.exists(CLANG) or _runtime() is None:
+        pytest.skip("hipcc, clang or the clang sanitizer runtime not found")
     d = tmp_path_factory.mktemp("san")
     flags = [f for f in B.FLAGS if f != "-O3"] + ["-O1", "-g", *HOST_SAN]
     procs, objs = [], []
@@ -62,7 +63,7 @@ def _env(extra):
 def test_c_host_calls_under_sanitizers(san_lib, tmp_path):
     exe = str(tmp_path / "host_calls")
     lib_dir = os.path.dirname(san_lib)
-    subprocess.run(["/opt/rocm/llvm/bin/clang", "-std=c11", "-Wall", "-Werror", "-g",
+    subprocess.run([CLANG, "-std=c11", "-Wall", "-Werror", "-g",
                     "-fsanitize=address,undefined", "-shared-libasan", "-I", os.path.join(ROOT, "include"),
                     os.path.join(ROOT, "tests", "c", "host_calls.c"), "-L", lib_dir, "-labs",
                     f"-Wl,-rpath,{lib_dir}", "-o", exe], check=True, timeout=300)
