@@ -1,8 +1,10 @@
 """Seeded random layers through the whole path on the GPU (C ABI), against
-the oracle: random batch, heads, group size, head_dim, dtype, block-size map,
-ragged lengths (partial pages and blocks), budget and centroid format.  Each
-case checks the codes bit for bit, the selection under the tie-band rule and
-the attention on the GPU's selection (rules of gpu_pipeline.py)."""
+the oracle: random batch, heads, group size (1 to 8, slots padded), head_dim,
+dtype, block-size map, ragged lengths (partial pages and blocks), budget and
+centroid format.  Each case checks the codes bit for bit, the selection under
+the tie-band rule and the attention on the GPU's selection (rules of
+gpu_pipeline.py), and abs_select_decode against the separate calls bit for
+bit (the fused launch where the layer takes it)."""
 import numpy as np
 import pytest
 import torch
@@ -18,7 +20,7 @@ FORMATS = ["int4", "int4_sym", "int8", "int4_tensor", "bf16"]
 def _case(seed):
     r = np.random.default_rng(1000 + seed)
     Hkv = int(r.choice([1, 2, 3, 4, 8]))
-    G = int(r.choice([1, 2, 4, 8]))
+    G = int(r.choice([1, 2, 3, 4, 5, 6, 7, 8]))
     D = int(r.choice([64, 128]))
     dtype = str(r.choice(["f32", "bf16"]))
     B = int(r.integers(1, 6))
@@ -32,7 +34,7 @@ def _case(seed):
     return W.make_layer(w, seq_lens=lens, extra_pages=int(r.integers(0, 4))), budget, fmt
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(40))
 def test_random_layer(oracle_mod, seed):
     x, budget, fmt = _case(seed)
     B, Hq, D = x.q.shape
@@ -50,7 +52,18 @@ def test_random_layer(oracle_mod, seed):
     out = torch.empty((B, Hq, D), dtype=A.torch_dtype(x.dtype), device="cuda")
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
     A.sparse_decode(kv, q, sel, cnt, budget, sm, out, lse)
+    fsel = torch.full((B, Hkv, cap), -1, dtype=torch.int32, device="cuda")
+    fcnt = torch.zeros((B, Hkv), dtype=torch.int32, device="cuda")
+    fout = torch.empty((B, Hq, D), dtype=A.torch_dtype(x.dtype), device="cuda")
+    flse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    A.select_decode(kv, cents, q, budget, sm, fsel, fcnt, fout, flse)
     torch.cuda.synchronize()
+    np.testing.assert_array_equal(fcnt.cpu().numpy(), cnt.cpu().numpy())
+    fs, ss = fsel.cpu().numpy(), sel.cpu().numpy()
+    for (b, h), k in np.ndenumerate(cnt.cpu().numpy()):
+        np.testing.assert_array_equal(fs[b, h, :k], ss[b, h, :k])
+    np.testing.assert_array_equal(fout.float().cpu().numpy(), out.float().cpu().numpy())
+    np.testing.assert_array_equal(flse.cpu().numpy(), lse.cpu().numpy())
 
     c = oracle_mod.centroids(x.k_cache, x.page_table, x.seq_lens, x.block_size, x.dtype)
     qf = oracle_mod.quantize_fmt(c, x.seq_lens, x.block_size, fmt)
