@@ -34,9 +34,36 @@ def _case(seed):
     return W.make_layer(w, seq_lens=lens, extra_pages=int(r.integers(0, 4))), budget, fmt
 
 
+def _long_case(seed):
+    """Long contexts (1K to 300K tokens): heads of up to 18,750 blocks, so the
+    top-K launch's 1024-thread form and the fused launch's 32-key form run."""
+    r = np.random.default_rng(9000 + seed)
+    Hkv = int(r.choice([1, 2, 3, 4, 8]))
+    G = int(r.choice([1, 2, 3, 4, 5, 6, 7, 8]))
+    D = int(r.choice([64, 128]))
+    dtype = str(r.choice(["f32", "bf16", "bf16"]))
+    B = int(r.integers(1, 4))
+    lens = r.integers(1000, 300000, B).tolist()
+    bs = tuple(int(b) for b in r.choice([16, 32, 64], Hkv))
+    budget = int(r.choice([64, 1024, 4096, 8192]))
+    fmt = FORMATS[seed % len(FORMATS)]
+    w = W.PRESETS[1].scaled(batch=B, num_q_heads=Hkv * G, num_kv_heads=Hkv, head_dim=D, dtype=dtype,
+                            context=max(lens), token_budget=budget, needles_per_head=int(r.integers(0, 17)),
+                            fixed_block_sizes=bs)
+    return W.make_layer(w, seq_lens=lens, extra_pages=int(r.integers(0, 4))), budget, fmt
+
+
 @pytest.mark.parametrize("seed", range(40))
 def test_random_layer(oracle_mod, seed):
-    x, budget, fmt = _case(seed)
+    _check_case(oracle_mod, seed, *_case(seed))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_long_layer(oracle_mod, seed):
+    _check_case(oracle_mod, seed, *_long_case(seed))
+
+
+def _check_case(oracle_mod, seed, x, budget, fmt):
     B, Hq, D = x.q.shape
     Hkv = x.k_cache.shape[1]
     print(f"[gpu random] seed={seed} B={B} Hq={Hq} Hkv={Hkv} D={D} {x.dtype} lens={x.seq_lens.tolist()} "
